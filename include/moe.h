@@ -1,0 +1,199 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer forward hot path.
+ *
+ * The layer: router top-k gating (softmax or sigmoid) fused with a stable,
+ * block-padded expert sort, then a two-stage expert GEMM -- gate-up with
+ * silu(gate)*up, then a down projection scaled by the routed weight and
+ * combined into out[token, model_dim].
+ *
+ * Sources (web pages; cited by title and section):
+ *  [P1] "[Feat] Fuse TopKGatingSoftmax and MoE Sorting kernels" (ROCm/FlyDSL #582)
+ *  [P2] "[MoE] Port moe_gemm_2stage (stage1+stage2) to the new fx.* pipeline --
+ *       fp8 (gfx942 + gfx950)" (ROCm/FlyDSL #947)
+ *  [P3] "[Common] Optimize fused router forward/backward kernels"
+ *       (NVIDIA/TransformerEngine #3012)
+ *  [P4] "[RadeonFlow] flydsl mxfp4 a4w4 MoE: bring gemm1/gemm2 to parity with
+ *       the HIP backend" (ROCm/aiter #3828)
+ *
+ * Conventions for every entry point
+ *  - Tensor arguments are DEVICE pointers to dense row-major storage that the
+ *    caller allocates and owns.  The library never allocates, frees or
+ *    synchronises: it validates arguments on the host, enqueues kernels on
+ *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and
+ *    returns.  Raw base pointers and integer sizes only ([P4] "Changes / ABI":
+ *    bare device addresses as kernel arguments).
+ *  - Return value: MOE_OK (0) or a negative moe_status.  On any error other
+ *    than MOE_ELAUNCH nothing has been enqueued.  All argument checks run
+ *    before the first HIP call.  No C++ exception crosses the ABI.  Faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - Alignment: tensors of 2-byte or wider elements and every fp8 tensor
+ *    must be 16-byte aligned; otherwise MOE_EINVAL.
+ *  - Calls on different streams may run concurrently if their output and
+ *    workspace buffers are disjoint; the library keeps no global state.
+ *
+ * Notation: T tokens, E experts, k = topk, D = model_dim, I = inter_dim,
+ * B = block_m.  Slot s = t*k + j is token t's j-th ranked expert.  The
+ * sentinel slot value is T*k.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad enum, null or misaligned pointer, topk not in [1,E], T < 0 */
+  MOE_ERANGE = -2,        /* T*E (or a derived size) does not fit a signed 32-bit int ([P3] "Hardening") */
+  MOE_ENOSPC = -3,        /* sorted_cap or ws_bytes smaller than required */
+  MOE_EUNSUPPORTED = -4,  /* E > 8160, block_m not in {16,32,64}, D or I not a positive multiple of 64 */
+  MOE_ELAUNCH = -5        /* a kernel launch failed (hipGetLastError) */
+};
+
+enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum moe_dtype { MOE_BF16 = 0, MOE_FP8_E4M3 = 1 };
+enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1 };
+
+/* Largest E accepted ([P3] "Hardening": the radix top-k path's 8160-expert bound). */
+#define MOE_MAX_EXPERTS 8160
+
+/* ---------------------------------------------------------------- host helpers
+ * Pure host functions: no device work, callable without a GPU. */
+
+/* Length of sorted_token_ids that always suffices:
+ * roundup_B(T*k + min(E, T*k)*(B-1)).  Returns a negative moe_status for
+ * invalid arguments. */
+int64_t moe_sorted_capacity(int T, int E, int topk, int block_m);
+
+/* Workspace bytes moe_topk_softmax_sort needs (0 when T is small enough for
+ * the single-workgroup path).  Negative moe_status on invalid arguments. */
+int64_t moe_route_workspace_bytes(int T, int E, int topk, int block_m);
+
+/* Workspace bytes moe_gemm1_gateup needs: 0 for bf16; for fp8 the bf16
+ * intermediate rows [T*k, I] that are requantised per row. */
+int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I);
+
+/* moe_forward's workspace: the routing outputs, the intermediate and the fp32
+ * accumulator, each at a 256-byte aligned offset.  Fields (byte offsets written
+ * to offsets[0..MOE_WS_NFIELDS-1]; a field a configuration does not use has
+ * offset -1):
+ *   0 topk_weights fp32 [T,k]      1 topk_ids int32 [T,k]
+ *   2 sorted_token_ids int32 [cap] 3 expert_ids int32 [cap/B]
+ *   4 num_valid int32 [1]          5 routing scratch
+ *   6 a: bf16 [T*k,I] or e4m3 [T*k,I]
+ *   7 a_scale fp32 [T*k] (fp8)     8 gemm1 scratch (fp8: bf16 [T*k,I])
+ *   9 y: ATOMIC fp32 [T,D] accumulator, REDUCE fp32 [T*k,D] slot rows
+ * Returns the total size in bytes, or a negative moe_status. */
+#define MOE_WS_NFIELDS 10
+int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
+                                     int block_m, int64_t* offsets);
+
+/* Static description of a status code. */
+const char* moe_strerror(int status);
+
+/* ---------------------------------------------------------------- routing
+ * [P1] "Motivation", "Relevant Files", "Additional Details": top-k gating
+ * softmax fused with the MoE sorting step; [P3] "Changes / Forward kernels"
+ * and the flowchart: score function (softmax or sigmoid), then top-k.
+ *
+ * Per token t: the k experts with the largest fp32 logits, best first, ties
+ * to the lower expert index (selection on the logits equals selection on the
+ * strictly increasing score).  -0.0 and +0.0 are equal.  NaN logits are
+ * outside the contract.
+ * Weights (fp32): softmax renormalised over the k picks
+ * (= softmax of the picked logits), or sigmoid(logit) divided by the sum over
+ * the picks; with renorm = 0 the score itself (softmax over all E, or the
+ * sigmoid) at the picks.
+ * Sort: c_e = #slots routed to e; each non-empty expert's slots, ascending,
+ * padded with the sentinel T*k up to a multiple of B, concatenated by expert
+ * index; experts with no slot get no block.  num_valid = total padded length.
+ *
+ *   logits           fp32  [T, E]               in
+ *   topk_weights     fp32  [T, k]               out
+ *   topk_ids         int32 [T, k]               out, rank order
+ *   sorted_token_ids int32 [sorted_cap]         out, slots; sentinel T*k in the padding and
+ *                                               in [num_valid, sorted_cap)
+ *   expert_ids       int32 [sorted_cap / B]     out, expert of each B-row block; -1 past num_valid
+ *   num_valid        int32 [1]                  out
+ *   workspace        moe_route_workspace_bytes(...) bytes (may be NULL when that is 0)
+ * T = 0 is valid: only num_valid (= 0) is written.
+ * Deterministic: repeated calls give bit-identical outputs. */
+int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score, int renorm,
+                          int block_m, float* topk_weights, int32_t* topk_ids,
+                          int32_t* sorted_token_ids, int64_t sorted_cap, int32_t* expert_ids,
+                          int32_t* num_valid, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- stage 1
+ * [P2] gate-up helper and stage-1 commits ("silu(gate)*up with optional fp8
+ * weight/act dequant -> bf16"; B-first MFMA with the weight as the first
+ * operand; sorted-row gather).
+ *
+ * For every B-row block b < num_valid/B with e = expert_ids[b] and every row
+ * holding a real slot s (token t = s / k):
+ *   g[n] = sum_d W1[e, n, d] * x[t, d],  u[n] = sum_d W1[e, I+n, d] * x[t, d]   (n < I)
+ *   a[s, n] = bf16_rne(silu(g[n]) * u[n]),  silu(z) = z / (1 + exp(-z))
+ * Rows [0,I) of each expert's W1 are the gate, rows [I,2I) the up projection.
+ * fp8 (e4m3fn): x[t,:] carries scale x_scale[t], W1[e,n,:] scale w1_scale[e,n];
+ * the bf16 row a[s,:] is then requantised: a_scale[s] = amax_n|a[s,n]| / 448
+ * (1.0 for an all-zero row), codes = e4m3_rne(a / a_scale[s]) clamped to +-448.
+ *
+ *   x         bf16 [T, D] | e4m3 [T, D]      x_scale  fp32 [T] (fp8 only, else NULL)
+ *   w1        bf16 [E, 2I, D] | e4m3         w1_scale fp32 [E, 2I] (fp8 only)
+ *   sorted_token_ids, expert_ids, num_valid: as written by moe_topk_softmax_sort
+ *   a         bf16 [T*k, I] | e4m3 [T*k, I]  out (every slot row is written)
+ *   a_scale   fp32 [T*k] (fp8 only)           out
+ *   workspace moe_gemm1_workspace_bytes(...) bytes (fp8), else may be NULL */
+int moe_gemm1_gateup(int dtype, const void* x, const float* x_scale, const void* w1,
+                     const float* w1_scale, const int32_t* sorted_token_ids,
+                     const int32_t* expert_ids, const int32_t* num_valid, int64_t sorted_cap,
+                     int T, int E, int topk, int D, int I, int block_m, void* a, float* a_scale,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- stage 2
+ * [P2] stage-2 commit: down projection with per-token(row) x per-channel
+ * (model_dim) fp8 dequant, the routed weight, and two epilogue modes:
+ * atomic accumulation into out[token, model_dim], or a plain store of
+ * out[token*topk + slot, model_dim] for a separate reduction.  Padding rows
+ * issue no store and no atomic.
+ *
+ * For every real slot s = t*k + j in a block of expert e:
+ *   c_s[d] = topk_weights[s] * sum_n W2[e, d, n] * a[s, n]
+ *            (fp8: * a_scale[s] * w2_scale[e, d])
+ *   ATOMIC: y[t, d] += c_s[d]   (y fp32 [T, D]; the caller zeroes it first)
+ *   REDUCE: y[s, d]  = c_s[d]   (y fp32 [T*k, D])
+ *
+ *   a, a_scale        as written by moe_gemm1_gateup
+ *   w2                bf16 [E, D, I] | e4m3 [E, D, I]   w2_scale fp32 [E, D] (fp8 only)
+ *   topk_weights      fp32 [T, k] */
+int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w2,
+                   const float* w2_scale, const float* topk_weights,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_valid, int64_t sorted_cap, int T, int E, int topk, int D,
+                   int I, int block_m, int mode, float* y, void* stream);
+
+/* ---------------------------------------------------------------- combine
+ * [P2] stage-2 commit and summary: the reduce mode's separate reduction kernel.
+ * ATOMIC: out[t, d] = bf16_rne(y[t, d]), y fp32 [T, D].
+ * REDUCE: out[t, d] = bf16_rne(sum_j y[t*k + j, d]) summed in fp32, j ascending.
+ *   out bf16 [T, D] */
+int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------- whole layer
+ * moe_topk_softmax_sort -> (ATOMIC: zero the accumulator) -> moe_gemm1_gateup
+ * -> moe_gemm2_down -> moe_finalize, all on `stream`, with every intermediate
+ * in `workspace` at the offsets moe_forward_workspace_layout reports (so they
+ * can be read back).  out bf16 [T, D]. */
+int moe_forward(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
+                const float* x_scale, const void* w1, const float* w1_scale, const void* w2,
+                const float* w2_scale, int T, int E, int topk, int D, int I, int block_m,
+                void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

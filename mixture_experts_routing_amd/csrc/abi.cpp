@@ -1,0 +1,256 @@
+// C ABI of the MoE-layer hot path: argument validation, workspace layout and
+// launch order.  Every check runs before the first HIP call; nothing here
+// allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// [P3] "Hardening": topk in [1, E], tokens*experts within a signed 32-bit int.
+int check_route_dims(int T, int E, int topk, int block_m) {
+  if (T < 0 || E < 1) return MOE_EINVAL;
+  if (topk < 1 || topk > E) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+  if (block_m != 16 && block_m != 32 && block_m != 64) return MOE_EUNSUPPORTED;
+  if ((int64_t)T * E > INT_MAX) return MOE_ERANGE;
+  if (moe::sorted_capacity(T, E, topk, block_m) > INT_MAX) return MOE_ERANGE;
+  return MOE_OK;
+}
+
+int check_layer_dims(int dtype, int T, int E, int topk, int D, int I, int block_m) {
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_EINVAL;
+  int st = check_route_dims(T, E, topk, block_m);
+  if (st) return st;
+  if (D < 64 || I < 64 || D % 64 || I % 64) return MOE_EUNSUPPORTED;
+  const int64_t eb = dtype == MOE_BF16 ? 2 : 1;
+  // row offsets inside the kernels are 32-bit per slot row; element counts are 64-bit
+  if ((int64_t)T * topk * I > INT_MAX || (int64_t)T * topk * D > INT_MAX) return MOE_ERANGE;
+  (void)eb;
+  return MOE_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+struct Layout {
+  int64_t off[MOE_WS_NFIELDS];
+  int64_t total;
+};
+
+Layout forward_layout(int dtype, int mode, int T, int E, int topk, int D, int I, int block_m) {
+  Layout L;
+  const int64_t n = (int64_t)T * topk;
+  const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
+  int64_t p = 0;
+  auto take = [&](int f, int64_t bytes) {
+    L.off[f] = p;
+    p += align256(bytes > 0 ? bytes : 1);
+  };
+  take(0, n * 4);
+  take(1, n * 4);
+  take(2, cap * 4);
+  take(3, cap / block_m * 4);
+  take(4, 4);
+  const int64_t rws = moe::route_workspace_bytes(T, E, topk);
+  if (rws > 0) take(5, rws);
+  else L.off[5] = -1;
+  take(6, n * I * (dtype == MOE_BF16 ? 2 : 1));
+  if (dtype == MOE_FP8_E4M3) {
+    take(7, n * 4);
+    take(8, n * I * 2);
+  } else {
+    L.off[7] = -1;
+    L.off[8] = -1;
+  }
+  take(9, (mode == MOE_OUT_ATOMIC ? (int64_t)T : n) * D * 4);
+  L.total = p;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument (enum, pointer, alignment, topk or T)";
+    case MOE_ERANGE: return "size out of range (tokens*experts or a derived size exceeds int32)";
+    case MOE_ENOSPC: return "sorted capacity or workspace too small";
+    case MOE_EUNSUPPORTED: return "unsupported shape (E > 8160, block_m, or D/I not multiples of 64)";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_sorted_capacity(int T, int E, int topk, int block_m) {
+  const int st = check_route_dims(T, E, topk, block_m);
+  if (st) return st;
+  return moe::sorted_capacity(T, E, topk, block_m);
+}
+
+int64_t moe_route_workspace_bytes(int T, int E, int topk, int block_m) {
+  const int st = check_route_dims(T, E, topk, block_m);
+  if (st) return st;
+  return moe::route_workspace_bytes(T, E, topk);
+}
+
+int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I) {
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_EINVAL;
+  if (T < 0 || topk < 1 || I < 64 || I % 64) return MOE_EINVAL;
+  if (dtype == MOE_BF16) return 0;
+  return (int64_t)T * topk * I * 2;
+}
+
+int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
+                                     int block_m, int64_t* offsets) {
+  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+  const int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
+  if (st) return st;
+  const Layout L = forward_layout(dtype, mode, T, E, topk, D, I, block_m);
+  if (offsets)
+    for (int f = 0; f < MOE_WS_NFIELDS; ++f) offsets[f] = L.off[f];
+  return L.total;
+}
+
+int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score, int renorm,
+                          int block_m, float* topk_weights, int32_t* topk_ids,
+                          int32_t* sorted_token_ids, int64_t sorted_cap, int32_t* expert_ids,
+                          int32_t* num_valid, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_route_dims(T, E, topk, block_m);
+  if (st) return st;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (renorm != 0 && renorm != 1) return MOE_EINVAL;
+  if (!ok_ptr(num_valid)) return MOE_EINVAL;
+  if (T > 0) {
+    if (!ok_ptr(logits) || !ok_ptr(topk_weights) || !ok_ptr(topk_ids) || !ok_ptr(sorted_token_ids) ||
+        !ok_ptr(expert_ids))
+      return MOE_EINVAL;
+  }
+  if (sorted_cap < moe::sorted_capacity(T, E, topk, block_m)) return MOE_ENOSPC;
+  const int64_t need = moe::route_workspace_bytes(T, E, topk);
+  if ((int64_t)ws_bytes < need) return MOE_ENOSPC;
+  if (need > 0 && !ok_ptr(workspace)) return MOE_EINVAL;
+  const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
+  return launch_status(moe::launch_route(logits, T, E, topk, score, renorm, block_m, topk_weights,
+                                         topk_ids, sorted_token_ids, cap, expert_ids, num_valid,
+                                         workspace, (hipStream_t)stream));
+}
+
+static int check_gemm_common(int dtype, int T, int E, int topk, int D, int I, int block_m,
+                             int64_t sorted_cap, const int32_t* sorted_token_ids,
+                             const int32_t* expert_ids, const int32_t* num_valid) {
+  const int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
+  if (st) return st;
+  if (sorted_cap < moe::sorted_capacity(T, E, topk, block_m)) return MOE_ENOSPC;
+  if (T > 0 && (!ok_ptr(sorted_token_ids) || !ok_ptr(expert_ids) || !ok_ptr(num_valid)))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int moe_gemm1_gateup(int dtype, const void* x, const float* x_scale, const void* w1,
+                     const float* w1_scale, const int32_t* sorted_token_ids,
+                     const int32_t* expert_ids, const int32_t* num_valid, int64_t sorted_cap,
+                     int T, int E, int topk, int D, int I, int block_m, void* a, float* a_scale,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_gemm_common(dtype, T, E, topk, D, I, block_m, sorted_cap, sorted_token_ids,
+                             expert_ids, num_valid);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(a)) return MOE_EINVAL;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (fp8) {
+    if (!ok_ptr(x_scale) || !ok_ptr(w1_scale) || !ok_ptr(a_scale)) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < moe_gemm1_workspace_bytes(dtype, T, topk, I)) return MOE_ENOSPC;
+    if (!ok_ptr(workspace)) return MOE_EINVAL;
+  }
+  const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
+  return launch_status(moe::launch_gemm1(fp8, x, x_scale, w1, w1_scale, sorted_token_ids,
+                                         expert_ids, num_valid, cap, T, E, topk, D, I, block_m, a,
+                                         a_scale, workspace, nullptr, 0, (hipStream_t)stream));
+}
+
+int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w2,
+                   const float* w2_scale, const float* topk_weights,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_valid, int64_t sorted_cap, int T, int E, int topk, int D,
+                   int I, int block_m, int mode, float* y, void* stream) {
+  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+  int st = check_gemm_common(dtype, T, E, topk, D, I, block_m, sorted_cap, sorted_token_ids,
+                             expert_ids, num_valid);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(a) || !ok_ptr(w2) || !ok_ptr(topk_weights) || !ok_ptr(y)) return MOE_EINVAL;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (fp8 && (!ok_ptr(a_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
+  const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
+  return launch_status(moe::launch_gemm2(fp8, a, a_scale, w2, w2_scale, topk_weights,
+                                         sorted_token_ids, expert_ids, num_valid, cap, T, E, topk,
+                                         D, I, block_m, mode, y, (hipStream_t)stream));
+}
+
+int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out, void* stream) {
+  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+  if (T < 0 || topk < 1 || D < 64 || D % 64) return T < 0 || topk < 1 ? MOE_EINVAL : MOE_EUNSUPPORTED;
+  if ((int64_t)T * topk * D > INT_MAX) return MOE_ERANGE;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(y) || !ok_ptr(out)) return MOE_EINVAL;
+  return launch_status(moe::launch_finalize(mode, y, T, topk, D, out, (hipStream_t)stream));
+}
+
+int moe_forward(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
+                const float* x_scale, const void* w1, const float* w1_scale, const void* w2,
+                const float* w2_scale, int T, int E, int topk, int D, int I, int block_m,
+                void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (renorm != 0 && renorm != 1) return MOE_EINVAL;
+  int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(w2) || !ok_ptr(out) ||
+      !ok_ptr(workspace))
+    return MOE_EINVAL;
+  if (fp8 && (!ok_ptr(x_scale) || !ok_ptr(w1_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
+  const Layout L = forward_layout(dtype, mode, T, E, topk, D, I, block_m);
+  if ((int64_t)ws_bytes < L.total) return MOE_ENOSPC;
+
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](int f) -> void* { return L.off[f] < 0 ? nullptr : ws + L.off[f]; };
+  float* topk_w = static_cast<float*>(at(0));
+  int32_t* topk_ids = static_cast<int32_t*>(at(1));
+  int32_t* sorted = static_cast<int32_t*>(at(2));
+  int32_t* eids = static_cast<int32_t*>(at(3));
+  int32_t* nvalid = static_cast<int32_t*>(at(4));
+  void* rws = at(5);
+  void* a = at(6);
+  float* a_scale = static_cast<float*>(at(7));
+  void* g1ws = at(8);
+  float* y = static_cast<float*>(at(9));
+  const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
+  hipStream_t s = (hipStream_t)stream;
+
+  // the atomic accumulator is cleared by the gate-up kernel's blocks on their way in
+  hipError_t e = moe::launch_route(logits, T, E, topk, score, renorm, block_m, topk_w, topk_ids, sorted,
+                          cap, eids, nvalid, rws, s);
+  if (e == hipSuccess)
+    e = moe::launch_gemm1(fp8, x, x_scale, w1, w1_scale, sorted, eids, nvalid, cap, T, E, topk,
+                          D, I, block_m, a, a_scale, g1ws, mode == MOE_OUT_ATOMIC ? y : nullptr,
+                          mode == MOE_OUT_ATOMIC ? (int64_t)T * D : 0, s);
+  if (e == hipSuccess)
+    e = moe::launch_gemm2(fp8, a, a_scale, w2, w2_scale, topk_w, sorted, eids, nvalid, cap, T,
+                          E, topk, D, I, block_m, mode, y, s);
+  if (e == hipSuccess) e = moe::launch_finalize(mode, y, T, topk, D, out, s);
+  return launch_status(e);
+}
+
+}  // extern "C"

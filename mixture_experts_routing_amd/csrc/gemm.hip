@@ -1,0 +1,541 @@
+// Two-stage expert GEMM on MFMA (gfx950): stage 1 gate-up + SiLU-mul, stage 2 down
+// projection + routed weight + scatter.
+//
+// [P2] "[MoE] Port moe_gemm_2stage (stage1+stage2) to the new fx.* pipeline -- fp8
+// (gfx942 + gfx950)" (ROCm/FlyDSL #947): B-first MFMA (the weight is the first
+// operand, the gathered activation rows the second), rows gathered through the
+// sorted ids with sentinel rows contributing zero, silu(gate)*up producing bf16,
+// per-token x per-channel fp8 dequant in the stage-2 epilogue, routed weight,
+// atomic or reduce epilogue, padding lanes issuing no atomics.
+//
+// Layout of the work (one 256-thread workgroup = 4 waves):
+//  * block = one BLOCK_M-row block of the sorted list (one expert) x one tile of
+//    output channels.  Blocks past num_valid exit at once.
+//  * each wave owns two 16-row groups of weight rows (stage 1: 16 gate rows and the
+//    matching 16 up rows; stage 2: 32 consecutive model_dim rows) and streams
+//    them straight from HBM into registers, 128 contiguous bytes per row per
+//    K-chunk.  The gathered activation rows are read per wave from L2.
+//  * MFMA: bf16 16x16x32 (two per 128-byte chunk) or fp8 e4m3 16x16x128 (one per
+//    chunk).  Lane (i, g) = (lane % 16, lane / 16) carries bytes [32g, 32g+32) of
+//    row i of the chunk for both operands; the MFMA sums over K, so this common
+//    permutation of K leaves the result unchanged.
+//  * accumulator lane layout: lane (j, g) holds output rows 4g..4g+3 (channels)
+//    of column j (the j-th gathered row), so a lane owns 4 consecutive channels
+//    of one slot.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+struct alignas(16) u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ i32x4_t ld16(const uint8_t* p) {
+  return *reinterpret_cast<const i32x4_t*>(p);
+}
+
+// Block -> (row block, channel tile).  Workgroups are handed to the 8 XCDs round
+// robin by id, so id L runs on XCD L % 8.  Each XCD is given one contiguous range
+// of the (tile-major, row-block-minor) order: the row blocks of one expert that
+// share a weight tile then run on the same XCD and share its L2.
+__device__ __forceinline__ bool block_tile(int mbs, int nts, int& mb, int& nt) {
+  const int n = mbs * nts;
+  const int per = (n + 7) >> 3;
+  const int L = (int)blockIdx.x;
+  const int v = (L & 7) * per + (L >> 3);
+  if (v >= n) return false;
+  nt = v / mbs;
+  mb = v - nt * mbs;
+  return true;
+}
+static inline unsigned xcd_grid(int64_t mbs, int64_t nts) {
+  return (unsigned)(((mbs * nts + 7) / 8) * 8);
+}
+
+template <bool FP8>
+__device__ __forceinline__ void mfma_chunk(f32x4_t& acc, const i32x4_t (&a)[2], const i32x4_t (&b)[2]) {
+  if constexpr (FP8) {
+    i32x8_t av = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
+    i32x8_t bv = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
+    // A/B format 0 = fp8 e4m3; block scales 127 = 2^0
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[0]),
+                                                 __builtin_bit_cast(bf16x8_t, b[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[1]),
+                                                 __builtin_bit_cast(bf16x8_t, b[1]), acc, 0, 0, 0);
+  }
+}
+
+// Streams the byte range [kb0, kb1) of K (rows are kbytes long; kb0, kb1 multiples of
+// 128) for NG weight-row groups against NT gathered activation tiles.  wrow[ng]: this
+// lane's weight row; xrow[tt]: this lane's activation row (nullptr = padding row,
+// contributes zero).  Within a 128-byte chunk, lane group g takes bytes [16g, 16g+16)
+// and [64+16g, 64+16g+16), so each load instruction covers 64 contiguous bytes per row.
+// The last chunk of an fp8 row may be half (64 bytes); its second half reads as zero.
+template <bool FP8, int NG, int NT, int U>
+__device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
+                                         const uint8_t* const (&xrow)[NT], int kb0, int kb1,
+                                         int kbytes, f32x4_t (&acc)[NG][NT]) {
+  const int g16 = (lane_id() >> 4) * 16;
+  const i32x4_t zero = {0, 0, 0, 0};
+  int kb = kb0;
+  const int kend_full = kb1 < (kbytes & ~127) ? kb1 : (kbytes & ~127);
+  for (; kb + 128 * U <= kend_full; kb += 128 * U) {
+    i32x4_t wa[U][NG][2], xb[U][NT][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int off = kb + 128 * u + g16;
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+        wa[u][ng][0] = ld16(wrow[ng] + off);
+        wa[u][ng][1] = ld16(wrow[ng] + off + 64);
+      }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        xb[u][tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
+        xb[u][tt][1] = xrow[tt] ? ld16(xrow[tt] + off + 64) : zero;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) mfma_chunk<FP8>(acc[ng][tt], wa[u][ng], xb[u][tt]);
+  }
+  for (; kb < kb1 && kb < kbytes; kb += 128) {
+    const int off = kb + g16;
+    const bool in1 = kb + 64 < kbytes;
+    i32x4_t wa[NG][2], xb[NT][2];
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng) {
+      wa[ng][0] = ld16(wrow[ng] + off);
+      wa[ng][1] = in1 ? ld16(wrow[ng] + off + 64) : zero;
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      xb[tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
+      xb[tt][1] = (in1 && xrow[tt]) ? ld16(xrow[tt] + off + 64) : zero;
+    }
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) mfma_chunk<FP8>(acc[ng][tt], wa[ng], xb[tt]);
+  }
+}
+
+// K split over KS waves of a block: wave kp takes chunks [kp*n/KS, (kp+1)*n/KS).
+__device__ __forceinline__ void k_range(int kbytes, int kp, int ks, int& kb0, int& kb1) {
+  const int nch = (kbytes + 127) >> 7;
+  kb0 = (kp * nch / ks) * 128;
+  kb1 = ((kp + 1) * nch / ks) * 128;
+}
+
+// Sums the partial accumulators of the KS waves that share a row group into the
+// wave with kp == 0 (LDS, one barrier).  Returns false on the other waves.
+template <int KS, int RG, int NG, int NT>
+__device__ __forceinline__ bool reduce_k_split(f32x4_t (&acc)[NG][NT], int rg, int kp,
+                                               f32x4_t* red) {
+  if constexpr (KS == 1) {
+    return true;
+  } else {
+    const int lane = lane_id();
+    if (kp > 0) {
+#pragma unroll
+      for (int a = 0; a < NG; ++a)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          red[((((kp - 1) * RG + rg) * NG + a) * NT + tt) * 64 + lane] = acc[a][tt];
+    }
+    __syncthreads();
+    if (kp > 0) return false;
+#pragma unroll
+    for (int q = 1; q < KS; ++q)
+#pragma unroll
+      for (int a = 0; a < NG; ++a)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[a][tt] += red[((((q - 1) * RG + rg) * NG + a) * NT + tt) * 64 + lane];
+    return true;
+  }
+}
+
+// ----------------------------------------------------------------------------- stage 1
+// Block = 4 waves = RG = 4/KS row groups x KS parts of K.  A row group is 16 gate
+// channels and the matching 16 up channels.  grid: I/(16*RG) channel tiles x cap/BM
+// row blocks (see block_tile).  Output: bf16 rows a[s, I] (for fp8 the pre-requant
+// rows).  If zero_y is set, the blocks first clear that fp32 buffer (stage 2's
+// accumulator), which saves a launch.
+template <int BM, bool FP8, int U, int KS>
+__global__ void __launch_bounds__(256) gemm1_kernel(
+    const uint8_t* __restrict__ x, const float* __restrict__ x_scale,
+    const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ expert_ids,
+    const int32_t* __restrict__ num_valid, int T, int E, int k, int D, int I, int mbs,
+    uint16_t* __restrict__ a_out, float4* __restrict__ zero_y, int64_t zero_n4) {
+  constexpr int NT = BM / 16;
+  constexpr int RG = 4 / KS;
+  constexpr int EB = FP8 ? 1 : 2;
+  __shared__ f32x4_t red[KS > 1 ? (KS - 1) * RG * 2 * NT * 64 : 1];
+  if (zero_y)
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 256)
+      zero_y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  int mb, nt;
+  if (!block_tile(mbs, I / (16 * RG), mb, nt)) return;
+  if (mb * BM >= *num_valid) return;
+  const int e = expert_ids[mb];
+  if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int rg = wave / KS, kp = wave % KS;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int n_w = nt * 16 * RG + rg * 16;  // first gate channel of this row group
+  const int n_slots = T * k;
+  const int rowb = D * EB;
+  const uint8_t* wrow[2] = {w1 + ((size_t)e * 2 * I + n_w + i16) * rowb,
+                            w1 + ((size_t)e * 2 * I + I + n_w + i16) * rowb};
+  const uint8_t* xrow[NT];
+  int slot[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int s = sorted_ids[mb * BM + tt * 16 + i16];
+    slot[tt] = s;
+    xrow[tt] = (unsigned)s < (unsigned)n_slots ? x + (size_t)(s / k) * rowb : nullptr;
+  }
+  f32x4_t acc[2][NT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[a][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int kb0, kb1;
+  k_range(rowb, kp, KS, kb0, kb1);
+  mainloop<FP8, 2, NT, U>(wrow, xrow, kb0, kb1, rowb, acc);
+  if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
+
+  const int n0 = n_w + 4 * g;  // this lane's 4 channels
+  float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (FP8) {
+    const float* ws = w1_scale + (size_t)e * 2 * I;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sg[r] = ws[n0 + r];
+      su[r] = ws[I + n0 + r];
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int s = slot[tt];
+    if ((unsigned)s >= (unsigned)n_slots) continue;
+    float xs = 1.f;
+    if constexpr (FP8) xs = x_scale[s / k];
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float gg = acc[0][tt][r] * (sg[r] * xs);
+      const float uu = acc[1][tt][r] * (su[r] * xs);
+      v[r] = silu_mul(gg, uu);
+    }
+    uint2 pk;
+    pk.x = pack_bf16x2(v[0], v[1]);
+    pk.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(a_out + (size_t)s * I + n0) = pk;
+  }
+}
+
+// fp8: per slot row, scale = amax/448 (1 for a zero row), codes = e4m3(a/scale).
+// One wave per row.
+__global__ void __launch_bounds__(256) requant_rows_kernel(const uint16_t* __restrict__ a_bf16,
+                                                           int rows, int I,
+                                                           uint8_t* __restrict__ a_codes,
+                                                           float* __restrict__ a_scale) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = lane_id();
+  const uint16_t* src = a_bf16 + (size_t)row * I;
+  float amax = 0.f;
+  for (int c = lane * 8; c < I; c += 512) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[q] >> 16))));
+  }
+  amax = wave_max_f32(amax);
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  for (int c = lane * 8; c < I; c += 512) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t lo = pack_fp8x2(bf16_bits_to_f32(w[2 * q] & 0xFFFFu) / scale,
+                                     bf16_bits_to_f32(w[2 * q] >> 16) / scale);
+      const uint32_t hi = pack_fp8x2(bf16_bits_to_f32(w[2 * q + 1] & 0xFFFFu) / scale,
+                                     bf16_bits_to_f32(w[2 * q + 1] >> 16) / scale);
+      out[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint2*>(a_codes + (size_t)row * I + c) = make_uint2(out[0], out[1]);
+  }
+  if (lane == 0) a_scale[row] = scale;
+}
+
+// ----------------------------------------------------------------------------- stage 2
+// Block = 4 waves = RG = 4/KS row groups x KS parts of K; a row group is 32
+// model_dim rows.  grid: ceil(D/(32*RG)) channel tiles x cap/BM row blocks.
+template <int BM, bool FP8, int U, bool REDUCE, int KS>
+__global__ void __launch_bounds__(256) gemm2_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
+    const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
+    int k, int D, int I, int mbs, float* __restrict__ y) {
+  constexpr int NT = BM / 16;
+  constexpr int RG = 4 / KS;
+  constexpr int EB = FP8 ? 1 : 2;
+  __shared__ f32x4_t red[KS > 1 ? (KS - 1) * RG * 2 * NT * 64 : 1];
+  int mb, nt;
+  if (!block_tile(mbs, (D + 32 * RG - 1) / (32 * RG), mb, nt)) return;
+  if (mb * BM >= *num_valid) return;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int rg = wave / KS, kp = wave % KS;
+  const int d_w = nt * 32 * RG + rg * 32;
+  // a partial last tile only happens with KS == 1 (the host keeps D % (32*RG) == 0
+  // otherwise), so leaving here never skips a barrier
+  if (KS == 1 && d_w >= D) return;
+  const int e = expert_ids[mb];
+  if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
+  const int i16 = lane & 15, g = lane >> 4;
+  const int n_slots = T * k;
+  const int rowb = I * EB;
+  const uint8_t* wrow[2] = {w2 + ((size_t)e * D + d_w + i16) * rowb,
+                            w2 + ((size_t)e * D + d_w + 16 + i16) * rowb};
+  const uint8_t* xrow[NT];
+  int slot[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int s = sorted_ids[mb * BM + tt * 16 + i16];
+    slot[tt] = s;
+    xrow[tt] = (unsigned)s < (unsigned)n_slots ? a + (size_t)s * rowb : nullptr;
+  }
+  f32x4_t acc[2][NT];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int kb0, kb1;
+  k_range(rowb, kp, KS, kb0, kb1);
+  mainloop<FP8, 2, NT, U>(wrow, xrow, kb0, kb1, rowb, acc);
+  if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
+
+  float ws[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ws[q][r] = 1.f;
+  if constexpr (FP8) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ws[q][r] = w2_scale[(size_t)e * D + d_w + 16 * q + 4 * g + r];
+  }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int s = slot[tt];
+    if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue no store and no atomic
+    float sc = topk_w[s];
+    if constexpr (FP8) sc *= a_scale[s];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int d0 = d_w + 16 * q + 4 * g;
+      float c[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[r] = acc[q][tt][r] * (FP8 ? sc * ws[q][r] : sc);
+      if constexpr (REDUCE) {
+        *reinterpret_cast<float4*>(y + (size_t)s * D + d0) = make_float4(c[0], c[1], c[2], c[3]);
+      } else {
+        float* dst = y + (size_t)(s / k) * D + d0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) atomicAdd(dst + r, c[r]);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- combine
+__global__ void __launch_bounds__(256) finalize_atomic_kernel(const float* __restrict__ y, int64_t n4,
+                                                              uint16_t* __restrict__ out) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 v = reinterpret_cast<const float4*>(y)[i];
+    reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
+}
+
+__global__ void __launch_bounds__(256) finalize_reduce_kernel(const float* __restrict__ y, int T,
+                                                              int k, int D,
+                                                              uint16_t* __restrict__ out) {
+  const int d4 = D / 4;
+  const int64_t n4 = (int64_t)T * d4;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / d4;
+    const int c = (int)(i - t * d4);
+    float4 s = reinterpret_cast<const float4*>(y + (size_t)t * k * D)[c];
+    for (int j = 1; j < k; ++j) {
+      const float4 v = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * D)[c];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+  }
+}
+
+__global__ void __launch_bounds__(256) zero_f32_kernel(float4* __restrict__ p, int64_t n4) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ----------------------------------------------------------------------------- host side
+static int grid_1d(int64_t n, int cap_blocks = 4096) {
+  int64_t b = (n + 255) / 256;
+  if (b < 1) b = 1;
+  return (int)(b < cap_blocks ? b : cap_blocks);
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;  // callers pass multiples of 4 (D % 64 == 0)
+  if (n4 == 0) return hipSuccess;
+  zero_f32_kernel<<<grid_1d(n4), 256, 0, st>>>(reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16_t* out,
+                           hipStream_t st) {
+  const int64_t n4 = (int64_t)T * D / 4;
+  if (n4 == 0) return hipSuccess;
+  if (mode == 0)
+    finalize_atomic_kernel<<<grid_1d(n4), 256, 0, st>>>(y, n4, out);
+  else
+    finalize_reduce_kernel<<<grid_1d(n4), 256, 0, st>>>(y, T, k, D, out);
+  return hipGetLastError();
+}
+
+// K-split choice: enough waves for ~12 rounds of the 256 CUs x 16 wave slots, since
+// every tile of a call does the same work and the last round runs part-empty.
+static int pick_ks(int64_t waves_ks1) {
+  const int64_t target = 256LL * 16 * 12;
+  if (waves_ks1 >= target) return 1;
+  if (waves_ks1 * 2 >= target) return 2;
+  return 4;
+}
+
+template <int BM, bool FP8, int KS>
+static void gemm1_go(const void* x, const float* x_scale, const void* w1, const float* w1_scale,
+                     const int32_t* sorted_ids, const int32_t* expert_ids,
+                     const int32_t* num_valid, int mbs, int T, int E, int k, int D, int I,
+                     uint16_t* a_bf16, float* zero_y, int64_t zero_n, hipStream_t st) {
+  constexpr int U = BM == 64 ? 2 : 4;
+  constexpr int RG = 4 / KS;
+  const dim3 grid(xcd_grid(mbs, I / (16 * RG)));
+  gemm1_kernel<BM, FP8, U, KS><<<grid, 256, 0, st>>>(
+      (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, sorted_ids, expert_ids, num_valid,
+      T, E, k, D, I, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
+}
+
+template <int BM, bool FP8>
+static void gemm1_ks(int ks, const void* x, const float* x_scale, const void* w1,
+                     const float* w1_scale, const int32_t* sorted_ids, const int32_t* expert_ids,
+                     const int32_t* num_valid, int mbs, int T, int E, int k, int D, int I,
+                     uint16_t* a_bf16, float* zero_y, int64_t zero_n, hipStream_t st) {
+  if (ks == 4)
+    gemm1_go<BM, FP8, 4>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+  else if (ks == 2)
+    gemm1_go<BM, FP8, 2>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+  else
+    gemm1_go<BM, FP8, 1>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+}
+
+hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void* w1,
+                        const float* w1_scale, const int32_t* sorted_ids,
+                        const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
+                        int E, int k, int D, int I, int B, void* a, float* a_scale, void* ws,
+                        float* zero_y, int64_t zero_n, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  uint16_t* a_bf16 = fp8 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
+  const int mbs = (int)(cap / B);
+  const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
+  const int ks = pick_ks(n_act * (I / 16));  // a block covers 16*(4/ks) channels; I % 64 == 0
+#define MOE_G1(BMV)                                                                                   \
+  if (fp8)                                                                                            \
+    gemm1_ks<BMV, true>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st); \
+  else                                                                                                \
+    gemm1_ks<BMV, false>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+  if (B == 16) {
+    MOE_G1(16)
+  } else if (B == 32) {
+    MOE_G1(32)
+  } else {
+    MOE_G1(64)
+  }
+#undef MOE_G1
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !fp8) return err;
+  const int rows = T * k;
+  requant_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>(a_bf16, rows, I, reinterpret_cast<uint8_t*>(a), a_scale);
+  return hipGetLastError();
+}
+
+template <int BM, bool FP8, bool REDUCE, int KS>
+static void gemm2_go(int mbs, const void* a, const float* a_scale, const void* w2,
+                     const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+                     const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
+                     int D, int I, float* y, hipStream_t st) {
+  constexpr int U = BM == 64 ? 2 : 4;
+  constexpr int RG = 4 / KS;
+  const dim3 grid(xcd_grid(mbs, (D + 32 * RG - 1) / (32 * RG)));
+  gemm2_kernel<BM, FP8, U, REDUCE, KS><<<grid, 256, 0, st>>>(
+      (const uint8_t*)a, a_scale, (const uint8_t*)w2, w2_scale, topk_w, sorted_ids, expert_ids,
+      num_valid, T, E, k, D, I, mbs, y);
+}
+
+template <int BM, bool FP8, bool REDUCE>
+static void gemm2_ks(int ks, int mbs, const void* a, const float* a_scale, const void* w2,
+                     const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+                     const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
+                     int D, int I, float* y, hipStream_t st) {
+  if (ks == 4)
+    gemm2_go<BM, FP8, REDUCE, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+  else if (ks == 2)
+    gemm2_go<BM, FP8, REDUCE, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+  else
+    gemm2_go<BM, FP8, REDUCE, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+}
+
+hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void* w2,
+                        const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+                        const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
+                        int E, int k, int D, int I, int B, int mode, float* y, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const int mbs = (int)(cap / B);
+  const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
+  const int ks = pick_ks(n_act * (D / 32));  // ks >= 2 needs D % 64 == 0, which always holds
+#define MOE_G2(BMV)                                                                                   \
+  if (fp8) {                                                                                          \
+    if (mode) gemm2_ks<BMV, true, true>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
+    else gemm2_ks<BMV, true, false>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
+  } else {                                                                                            \
+    if (mode) gemm2_ks<BMV, false, true>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
+    else gemm2_ks<BMV, false, false>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
+  }
+  if (B == 16) {
+    MOE_G2(16)
+  } else if (B == 32) {
+    MOE_G2(32)
+  } else {
+    MOE_G2(64)
+  }
+#undef MOE_G2
+  return hipGetLastError();
+}
+
+}  // namespace moe

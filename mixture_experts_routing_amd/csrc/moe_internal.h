@@ -1,0 +1,40 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Routing: largest T and E handled by the single-workgroup path.
+constexpr int kOneShotMaxT = 64;
+constexpr int kOneShotMaxE = 1024;
+// Multi-workgroup routing: tokens per sort chunk (16 waves x 16 tokens).
+constexpr int kChunkTokens = 256;
+
+int64_t sorted_capacity(int64_t T, int64_t E, int64_t k, int64_t B);
+bool route_is_oneshot(int T, int E);
+int64_t route_workspace_bytes(int T, int E, int k);
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int score, int renorm, int B,
+                        float* topk_w, int32_t* topk_ids, int32_t* sorted_ids, int64_t cap,
+                        int32_t* expert_ids, int32_t* num_valid, void* ws, hipStream_t st);
+
+hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void* w1,
+                        const float* w1_scale, const int32_t* sorted_ids,
+                        const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
+                        int E, int k, int D, int I, int B, void* a, float* a_scale, void* ws,
+                        float* zero_y, int64_t zero_n, hipStream_t st);
+
+hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void* w2,
+                        const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+                        const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
+                        int E, int k, int D, int I, int B, int mode, float* y, hipStream_t st);
+
+hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16_t* out,
+                           hipStream_t st);
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
+
+}  // namespace moe

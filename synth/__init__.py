@@ -81,6 +81,15 @@ def _quant_rows_e4m3(v: torch.Tensor):
     return codes.view(torch.uint8), scale
 
 
+def activations(T: int, D: int, dtype: str, seed: int = 0, x_std: float = 1.0) -> dict:
+    """Token activations on the CPU: {"x": bf16 [T,D]} or {"x": uint8 e4m3 [T,D], "x_scale": fp32 [T]}."""
+    x32 = torch.randn(T, D, generator=_gen(seed + 2, "cpu"), dtype=torch.float32) * x_std
+    if dtype == "bf16":
+        return {"x": x32.to(torch.bfloat16)}
+    xc, xs = _quant_rows_e4m3(x32)
+    return {"x": xc, "x_scale": xs}
+
+
 def layer_inputs(wl: Workload, T: int, seed: int = 0, device="cpu") -> dict:
     """All inputs of one layer call; weights are drawn per expert on `device`.
 

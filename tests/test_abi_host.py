@@ -1,0 +1,205 @@
+"""C-ABI checks that need no GPU: exports, host helpers, and every validation error path.
+
+All calls here fail validation (or are pure host helpers), so no HIP call is made.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, EINVAL, ERANGE, ENOSPC, EUNSUP, ELAUNCH = 0, -1, -2, -3, -4, -5
+
+GOOD = 0x10000  # a non-null, 16-byte aligned fake device address (never dereferenced)
+BAD_ALIGN = 0x10004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mixture_experts_routing_amd as m
+    return m.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("moe_topk_softmax_sort", "moe_gemm1_gateup", "moe_gemm2_down", "moe_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"libmoe.so does not export {n}"
+
+
+@pytest.mark.parametrize("T,E,k,B", [(1, 8, 2, 16), (4, 8, 2, 16), (16, 256, 8, 16), (16, 128, 4, 64),
+                                     (4096, 128, 4, 64), (8192, 2304, 36, 32), (16384, 385, 9, 64),
+                                     (0, 8, 2, 16), (3, 1, 1, 32), (1, 8160, 8160, 64)])
+def test_sorted_capacity_matches_oracle(lib, T, E, k, B):
+    assert lib.moe_sorted_capacity(T, E, k, B) == oracle.sorted_capacity(T, E, k, B)
+
+
+def test_workspace_layout(lib):
+    import mixture_experts_routing_amd as m
+    for dtype in ("bf16", "fp8"):
+        for mode in ("atomic", "reduce"):
+            for (T, E, k, D, I, B) in [(4, 8, 2, 128, 64, 16), (8192, 2304, 36, 64, 64, 32),
+                                       (16, 256, 8, 7168, 2048, 16)]:
+                total, offs = m.moe_forward_workspace_layout(dtype, mode, T, E, k, D, I, B)
+                n, cap = T * k, oracle.sorted_capacity(T, E, k, B)
+                sizes = {"topk_weights": 4 * n, "topk_ids": 4 * n, "sorted_token_ids": 4 * cap,
+                         "expert_ids": 4 * cap // B, "num_valid": 4,
+                         "route_scratch": m.moe_route_workspace_bytes(T, E, k, B),
+                         "a": n * I * (2 if dtype == "bf16" else 1),
+                         "a_scale": 4 * n if dtype == "fp8" else 0,
+                         "gemm1_scratch": 2 * n * I if dtype == "fp8" else 0,
+                         "y": 4 * D * (T if mode == "atomic" else n)}
+                spans = []
+                for f, o in offs.items():
+                    if sizes[f] == 0:
+                        assert o is None
+                        continue
+                    assert o is not None and o % 256 == 0
+                    spans.append((o, o + sizes[f]))
+                spans.sort()
+                for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+                    assert a1 <= b0
+                assert spans[-1][1] <= total
+
+
+def route_call(lib, T=4, E=8, k=2, score=0, renorm=1, B=16, cap=None, ptrs=None, ws=0, ws_bytes=0):
+    if cap is None:
+        cap = max(oracle.sorted_capacity(T, E, k, B), 0) if 1 <= k <= E and B in (16, 32, 64) else 1 << 20
+    p = dict(logits=GOOD, w=GOOD, ids=GOOD, sorted=GOOD, eids=GOOD, nv=GOOD)
+    p.update(ptrs or {})
+    return lib.moe_topk_softmax_sort(p["logits"], T, E, k, score, renorm, B, p["w"], p["ids"],
+                                     p["sorted"], cap, p["eids"], p["nv"], ws, ws_bytes, None)
+
+
+def test_route_validation(lib):
+    assert route_call(lib, k=0) == EINVAL
+    assert route_call(lib, k=9) == EINVAL
+    assert route_call(lib, T=-1) == EINVAL
+    assert route_call(lib, E=0, k=1) == EINVAL
+    assert route_call(lib, E=8161, k=2) == EUNSUP
+    assert route_call(lib, B=8) == EUNSUP
+    assert route_call(lib, B=128) == EUNSUP
+    assert route_call(lib, T=2**20, E=4096, k=2) == ERANGE  # T*E > INT_MAX
+    assert route_call(lib, score=2) == EINVAL
+    assert route_call(lib, renorm=2) == EINVAL
+    assert route_call(lib, cap=oracle.sorted_capacity(4, 8, 2, 16) - 1) == ENOSPC
+    for key in ("logits", "w", "ids", "sorted", "eids", "nv"):
+        assert route_call(lib, ptrs={key: None}) == EINVAL
+        assert route_call(lib, ptrs={key: BAD_ALIGN}) == EINVAL
+    # multi-workgroup path needs a workspace
+    need = lib.moe_route_workspace_bytes(1000, 256, 8, 16)
+    assert need > 0
+    assert route_call(lib, T=1000, E=256, k=8, ws=GOOD, ws_bytes=need - 1) == ENOSPC
+    assert route_call(lib, T=1000, E=256, k=8, ws=None, ws_bytes=need) == EINVAL
+    assert lib.moe_route_workspace_bytes(16, 256, 8, 16) == 0
+
+
+def gemm1_call(lib, dtype=0, T=4, E=8, k=2, D=128, I=64, B=16, cap=None, ptrs=None, ws_bytes=1 << 30):
+    if cap is None:
+        cap = oracle.sorted_capacity(T, E, k, B) if (1 <= k <= E and B in (16, 32, 64) and T >= 0) else 1 << 20
+    p = dict(x=GOOD, xs=GOOD, w1=GOOD, w1s=GOOD, sid=GOOD, eid=GOOD, nv=GOOD, a=GOOD, as_=GOOD, ws=GOOD)
+    p.update(ptrs or {})
+    return lib.moe_gemm1_gateup(dtype, p["x"], p["xs"], p["w1"], p["w1s"], p["sid"], p["eid"], p["nv"],
+                                cap, T, E, k, D, I, B, p["a"], p["as_"], p["ws"], ws_bytes, None)
+
+
+def test_gemm1_validation(lib):
+    assert gemm1_call(lib, dtype=2) == EINVAL
+    assert gemm1_call(lib, D=100) == EUNSUP
+    assert gemm1_call(lib, I=96) == EUNSUP
+    assert gemm1_call(lib, D=0) == EUNSUP
+    assert gemm1_call(lib, k=3, E=2) == EINVAL
+    assert gemm1_call(lib, B=48) == EUNSUP
+    assert gemm1_call(lib, cap=oracle.sorted_capacity(4, 8, 2, 16) - 16) == ENOSPC
+    for key in ("x", "w1", "sid", "eid", "nv", "a"):
+        assert gemm1_call(lib, ptrs={key: None}) == EINVAL
+        assert gemm1_call(lib, ptrs={key: BAD_ALIGN}) == EINVAL
+    # fp8 needs the three scales and the workspace
+    for key in ("xs", "w1s", "as_", "ws"):
+        assert gemm1_call(lib, dtype=1, ptrs={key: None}) == EINVAL
+    assert gemm1_call(lib, dtype=1, ws_bytes=4 * 2 * 64 * 2 - 1) == ENOSPC
+    assert gemm1_call(lib, T=70000, E=8, k=2, D=16384) == ERANGE  # T*k*D > INT_MAX
+
+
+def gemm2_call(lib, dtype=0, mode=0, T=4, E=8, k=2, D=128, I=64, B=16, cap=None, ptrs=None):
+    if cap is None:
+        cap = oracle.sorted_capacity(T, E, k, B)
+    p = dict(a=GOOD, as_=GOOD, w2=GOOD, w2s=GOOD, tw=GOOD, sid=GOOD, eid=GOOD, nv=GOOD, y=GOOD)
+    p.update(ptrs or {})
+    return lib.moe_gemm2_down(dtype, p["a"], p["as_"], p["w2"], p["w2s"], p["tw"], p["sid"], p["eid"],
+                              p["nv"], cap, T, E, k, D, I, B, mode, p["y"], None)
+
+
+def test_gemm2_validation(lib):
+    assert gemm2_call(lib, mode=2) == EINVAL
+    assert gemm2_call(lib, dtype=-1) == EINVAL
+    assert gemm2_call(lib, D=64 + 32) == EUNSUP
+    assert gemm2_call(lib, cap=1) == ENOSPC
+    for key in ("a", "w2", "tw", "sid", "eid", "nv", "y"):
+        assert gemm2_call(lib, ptrs={key: None}) == EINVAL
+        assert gemm2_call(lib, ptrs={key: BAD_ALIGN}) == EINVAL
+    for key in ("as_", "w2s"):
+        assert gemm2_call(lib, dtype=1, ptrs={key: None}) == EINVAL
+
+
+def test_finalize_and_forward_validation(lib):
+    assert lib.moe_finalize(3, GOOD, 4, 2, 128, GOOD, None) == EINVAL
+    assert lib.moe_finalize(0, GOOD, 4, 2, 100, GOOD, None) == EUNSUP
+    assert lib.moe_finalize(0, None, 4, 2, 128, GOOD, None) == EINVAL
+    assert lib.moe_finalize(1, GOOD, 4, 2, 128, BAD_ALIGN, None) == EINVAL
+    assert lib.moe_finalize(0, GOOD, -1, 2, 128, GOOD, None) == EINVAL
+    total = lib.moe_forward_workspace_layout(0, 0, 4, 8, 2, 128, 64, 16, None)
+    assert total > 0
+
+    def fwd(dtype=0, score=0, renorm=1, mode=0, T=4, E=8, k=2, D=128, I=64, B=16, ws_bytes=total, **ptrs):
+        p = dict(logits=GOOD, x=GOOD, xs=GOOD, w1=GOOD, w1s=GOOD, w2=GOOD, w2s=GOOD, ws=GOOD, out=GOOD)
+        p.update(ptrs)
+        return lib.moe_forward(dtype, score, renorm, mode, p["logits"], p["x"], p["xs"], p["w1"], p["w1s"],
+                               p["w2"], p["w2s"], T, E, k, D, I, B, p["ws"], ws_bytes, p["out"], None)
+
+    assert fwd(mode=5) == EINVAL
+    assert fwd(score=3) == EINVAL
+    assert fwd(ws_bytes=total - 1) == ENOSPC
+    assert fwd(k=0) == EINVAL
+    assert fwd(E=9000, k=2) == EUNSUP
+    for key in ("logits", "x", "w1", "w2", "ws", "out"):
+        assert fwd(**{key: None}) == EINVAL
+    total8 = lib.moe_forward_workspace_layout(1, 0, 4, 8, 2, 128, 64, 16, None)
+    for key in ("xs", "w1s", "w2s"):
+        assert fwd(dtype=1, ws_bytes=total8, **{key: None}) == EINVAL
+
+
+def test_strerror(lib):
+    import mixture_experts_routing_amd as m
+    texts = {m.moe_strerror(s) for s in (OK, EINVAL, ERANGE, ENOSPC, EUNSUP, ELAUNCH)}
+    assert len(texts) == 6
+    assert "unknown" in m.moe_strerror(-99)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import mixture_experts_routing_amd as m
+    saved = m._lib
+    m._lib = None
+    try:
+        with pytest.raises(ImportError):
+            m.load_library(str(tmp_path / "nope.so"))
+    finally:
+        m._lib = saved

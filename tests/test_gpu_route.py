@@ -1,0 +1,133 @@
+"""GPU parity of moe_topk_softmax_sort against the oracle: bit-exact ids and sort, weights rel <= 1e-6."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu_helpers import check_route, oracle_route
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.stderr.write(f"\n[gpu] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+
+
+def run_route(logits, k, B, score="softmax", renorm=True, cap_extra=0):
+    import mixture_experts_routing_amd as m
+    T, E = logits.shape
+    cap = m.moe_sorted_capacity(T, E, k, B)
+    dev = logits.device
+    canary = -12345
+    out = {
+        "topk_weights": torch.full((T, k), float("nan"), device=dev),
+        "topk_ids": torch.full((T, k), canary, dtype=torch.int32, device=dev),
+        "sorted_token_ids": torch.full((cap + cap_extra,), canary, dtype=torch.int32, device=dev),
+        "expert_ids": torch.full((cap // B + cap_extra,), canary, dtype=torch.int32, device=dev),
+        "num_valid": torch.full((1,), canary, dtype=torch.int32, device=dev),
+    }
+    m.moe_topk_softmax_sort(logits, k, B, score, renorm, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [
+    # (T, E, k, B): tiny, DeepSeek decode, GPT-OSS, Kimi, router stress
+    (4, 8, 2, 16),
+    (1, 256, 8, 16), (2, 256, 8, 16), (4, 256, 8, 16), (8, 256, 8, 16), (16, 256, 8, 16),
+    (16, 128, 4, 64), (4096, 128, 4, 64),
+    (64, 385, 9, 64), (4096, 385, 9, 64), (16384, 385, 9, 64),
+    (8192, 512, 4, 32), (8192, 512, 22, 32), (8192, 2304, 36, 32),
+]
+
+
+@pytest.mark.parametrize("T,E,k,B", CASES)
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_route_workloads(T, E, k, B, score):
+    if score == "sigmoid" and (T, E) not in ((4, 8), (16, 256), (8192, 512), (8192, 2304)):
+        pytest.skip("sigmoid covered on the router stress shapes and two decode shapes")
+    logits = synth.logits(T, E, seed=T + E + k)
+    got = run_route(logits.cuda(), k, B, score)
+    check_route(got, oracle_route(logits, k, B, score), T, k)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("T,E,k,B", [(5, 64, 6, 16), (300, 160, 7, 32)])
+def test_route_no_renorm(T, E, k, B, score, renorm):
+    logits = synth.logits(T, E, seed=7)
+    got = run_route(logits.cuda(), k, B, score, renorm)
+    check_route(got, oracle_route(logits, k, B, score, renorm), T, k)
+
+
+def crafted(kind, T, E, seed):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "ties3":
+        return torch.randint(-1, 2, (T, E), generator=g).float()
+    if kind == "equal":
+        return torch.full((T, E), 0.5)
+    if kind == "signed_zero":
+        l = torch.zeros(T, E)
+        l[:, ::3] = -0.0
+        l[:, 1::7] = 1.0
+        return l
+    if kind == "dup":
+        l = torch.randn(T, E, generator=g)
+        h = E // 2
+        l[:, h:2 * h] = l[:, :h]
+        return l
+    if kind == "wide":
+        return torch.randn(T, E, generator=g) * 30.0
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["ties3", "equal", "signed_zero", "dup", "wide"])
+@pytest.mark.parametrize("T,E,k,B", [(5, 8, 3, 16), (7, 63, 5, 16), (3, 65, 64, 32), (9, 300, 70, 64),
+                                     (300, 256, 8, 16), (257, 1537, 36, 32)])
+def test_route_crafted_ties(kind, T, E, k, B):
+    # heavy ties push the selection onto its exact slow path; index order must still decide
+    logits = crafted(kind, T, E, seed=T * E)
+    for score in ("softmax", "sigmoid"):
+        got = run_route(logits.cuda(), k, B, score)
+        check_route(got, oracle_route(logits, k, B, score), T, k)
+
+
+@pytest.mark.parametrize("T,E,k,B", [(1, 1, 1, 16), (3, 4, 4, 16), (2, 8160, 8, 64), (70, 8160, 3, 32),
+                                     (65, 8, 8, 64), (1, 1536, 1, 16), (64, 1536, 64, 16),
+                                     (65, 1536, 2, 16), (1000, 8, 1, 32), (64, 1024, 8, 16), (64, 1025, 8, 16)])
+def test_route_edges(T, E, k, B):
+    logits = synth.logits(T, E, seed=11)
+    got = run_route(logits.cuda(), k, B)
+    check_route(got, oracle_route(logits, k, B), T, k)
+
+
+def test_route_empty():
+    got = run_route(torch.zeros(0, 8, device="cuda"), 2, 16)
+    assert int(got["num_valid"].item()) == 0
+
+
+@pytest.mark.parametrize("T,E,k,B", [(16, 256, 8, 16), (8192, 2304, 36, 32)])
+def test_route_deterministic_and_bounded(T, E, k, B):
+    logits = synth.logits(T, E, seed=3).cuda()
+    a = run_route(logits, k, B, cap_extra=64)
+    b = run_route(logits, k, B, cap_extra=64)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+    cap = a["sorted_token_ids"].numel() - 64
+    assert torch.all(a["sorted_token_ids"][cap:] == -12345)  # nothing written past the capacity
+    assert torch.all(a["expert_ids"][cap // B:] == -12345)
+
+
+def test_route_skewed_load():
+    # a few hot experts: long per-expert lists spanning many blocks and chunks
+    T, E, k, B = 5000, 64, 6, 32
+    logits = synth.logits(T, E, seed=5)
+    logits[:, :4] += 3.0
+    got = run_route(logits.cuda(), k, B)
+    check_route(got, oracle_route(logits, k, B), T, k)
