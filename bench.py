@@ -3,13 +3,14 @@
 
 Headline: MoE-layer microseconds per call at T=16 decode on the DeepSeek-R1 shape
 (E=256, topk=8, D=7168, I=2048, bf16, BLOCK_M=16, atomic combine).  One step is one
-moe_forward call: routing (top-k softmax + sort), gate-up GEMM, down GEMM with the
-routed weight and the combine, on inputs already resident in HBM.  Eight input sets
-(logits and activations) rotate so the set of active experts changes call to call.
+moe_forward call -- routing (top-k softmax + sort), gate-up GEMM with SiLU-mul, down
+GEMM with the routed weight, combine -- on inputs already resident in HBM.  Eight
+input sets (logits and activations) rotate so the active experts change call to call.
 
-Prints one JSON line with the metric, the roofline of the dominant kernel (timed
-with HIP events on the stream it runs on) and the CPU oracle's time on a bounded
-sample of the same workload.
+The JSON line also carries the roofline of the dominant kernel (HIP events on the
+stream it runs on), the CPU oracle's time on a bounded sample, and (unless
+--headline-only) secondary lines: GPT-OSS decode/prefill and Kimi fp8 layer times
+with per-GEMM TFLOPS, and router-only GB/s at T=8192.
 """
 
 from __future__ import annotations
@@ -23,8 +24,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense
+HBM_PEAK_GBS = 8000.0                                # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense
 
 
 def parse():
@@ -36,78 +37,40 @@ def parse():
     ap.add_argument("--T", type=int, default=16)
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--headline-only", action="store_true", help="skip the secondary lines")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run a 1 GiB device copy first (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
 
 
-def algorithmic(wl, T, n_act, num_valid, dtype):
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic(wl, T, n_act, num_valid):
     """Bytes and FLOPs the method must move/compute (padding, fp32 accumulator traffic,
     weight re-reads and atomic read-modify-writes excluded)."""
     E, k, D, I, B = wl.E, wl.topk, wl.D, wl.I, wl.block_m
-    bw = 2 if dtype == "bf16" else 1
+    bw = 2 if wl.dtype == "bf16" else 1
     route = 4 * T * E + 8 * T * k + 4 * num_valid + 4 * (num_valid // B) + 4
     g1 = n_act * 2 * I * D * bw + T * D * bw + T * k * I * bw
     g2 = n_act * D * I * bw + T * k * I * bw + 4 * T * k + 2 * T * D
-    if dtype == "fp8":
+    if wl.dtype == "fp8":
         g1 += n_act * 2 * I * 4 + 4 * T + 4 * T * k
         g2 += n_act * D * 4 + 4 * T * k
-    return {"route_bytes": route, "gemm1_bytes": g1, "gemm2_bytes": g2,
+    return {"route": route, "gemm1": g1, "gemm2": g2,
             "gemm1_flops": 2 * T * k * 2 * I * D, "gemm2_flops": 2 * T * k * D * I}
 
 
-def cpu_baseline(wl, T, host_logits, host_x, host_xs, w1, w2, w1s, w2s, n_act_all):
-    """The CPU oracle, timed on a bounded sample (the first tokens of one input set),
-    scaled to a whole call by active-expert count (its cost is per expert read)."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
-    sample_tokens = list(range(min(2, T)))
-    r = oracle.route(host_logits, wl.topk, wl.block_m)
-    used = sorted(set(r.ids[sample_tokens].reshape(-1).tolist()))
-    # host copies of exactly the weights the sample reads (untimed)
-    W1 = {e: w1(e) for e in used}
-    W2 = {e: w2(e) for e in used}
-    W1s = {e: w1s(e) for e in used} if w1s else None
-    W2s = {e: w2s(e) for e in used} if w2s else None
-    t0 = time.perf_counter()
-    r = oracle.route(host_logits, wl.topk, wl.block_m)
-    oracle.moe_layer(host_x, W1, W2, r.ids, r.weights, wl.dtype, x_scale=host_xs, w1_scale=W1s,
-                     w2_scale=W2s, tokens=sample_tokens)
-    dt = time.perf_counter() - t0
-    per_call_us = dt * 1e6 * (n_act_all / len(used))
-    return {"value": round(per_call_us, 1), "unit": "us/call", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": (f"{wl.name} T={T}: routing of all {T} tokens + layer for tokens {sample_tokens} "
-                       f"({len(used)} of {n_act_all} active experts), fp64 numpy, {dt:.2f} s, "
-                       f"scaled by active experts; host has {os.cpu_count()} logical CPUs")}
-
-
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU "
-              "component in this build", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
-    import torch
-
-    import mixture_experts_routing_amd as m
-    import synth
-
-    m.load_library()
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    wl = synth.WORKLOADS[args.workload]
-    T, k, B, dtype, mode = args.T, wl.topk, wl.block_m, wl.dtype, wl.mode
+def measure_layer(env, wl, T, steps, warmup, rotate):
+    """Times moe_forward and, separately, each stage; returns a result dict."""
+    m, torch, np, synth, dev = env
+    k, B, dtype, mode = wl.topk, wl.block_m, wl.dtype, wl.mode
     E, D, I = wl.E, wl.D, wl.I
-    print(f"[bench] {wl.name} T={T} E={E} k={k} D={D} I={I} B={B} {dtype} {mode}: generating inputs",
-          file=sys.stderr, flush=True)
+    log(f"{wl.name} T={T} E={E} k={k} D={D} I={I} B={B} {dtype} {mode}: generating inputs")
     base = synth.layer_inputs(wl, 1, seed=0, device=dev)
     sets = []
-    for r in range(args.rotate):
+    for r in range(rotate):
         s = {"logits": synth.logits(T, E, seed=100 + r).to(dev)}
         s.update({kk: v.to(dev) for kk, v in synth.activations(T, D, dtype, seed=100 + r, x_std=wl.x_std).items()})
         sets.append(s)
@@ -122,41 +85,34 @@ def main():
                       x_scale=s.get("x_scale"), w1_scale=base.get("w1_scale"),
                       w2_scale=base.get("w2_scale"), workspace=ws, out=out, stream=stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    log(f"timing {steps} moe_forward calls")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     ev0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_call = ev0.elapsed_time(ev1) / steps
 
-    # per-stage durations (HIP events on the launch stream), staged calls on the same inputs
+    # per-stage durations: staged calls, every step enqueued before one synchronisation so
+    # the GPU never idles inside a bracketed interval
     views = m.workspace_views(ws, offs, dtype, mode, T, E, k, D, I, B)
-    stage_ms = {"route": [], "gemm1": [], "gemm2": [], "finalize": []}
-    bytes_acc = {"gemm1": 0, "gemm2": 0, "route": 0}
-    flops_acc = {"gemm1": 0, "gemm2": 0}
     rt = {kk: views[kk] for kk in ("topk_weights", "topk_ids", "sorted_token_ids", "expert_ids", "num_valid")}
-    a = views["a"]
-    a_scale = views["a_scale"]
-    y = views["y"]
+    a, a_scale, y = views["a"], views["a_scale"], views["y"]
     g1ws = ws[offs["gemm1_scratch"]:] if offs["gemm1_scratch"] is not None else None
     rws = ws[offs["route_scratch"]:] if offs["route_scratch"] is not None else None
-    # active experts and num_valid of each input set (read back once, untimed)
     per_set = []
-    for s in sets:
+    for s in sets:  # active experts and num_valid of each input set (untimed)
         m.moe_topk_softmax_sort(s["logits"], k, B, out=rt, workspace=rws, stream=stream)
         torch.cuda.synchronize()
         per_set.append((len(np.unique(rt["topk_ids"].cpu().numpy())), int(rt["num_valid"].item())))
-    # all steps are enqueued before one synchronisation, so the GPU never waits on the
-    # host between an event and the kernel it brackets
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    acc = {"route": 0, "gemm1": 0, "gemm2": 0, "gemm1_flops": 0, "gemm2_flops": 0}
     n_acts = []
-    for i in range(args.steps):
+    for i in range(steps):
         s = sets[i % len(sets)]
         ev = evs[i]
         if mode == "atomic":
@@ -174,67 +130,184 @@ def main():
         ev[4].record(stream)
         n_act, nv = per_set[i % len(sets)]
         n_acts.append(n_act)
-        alg = algorithmic(wl, T, n_act, nv, dtype)
-        bytes_acc["gemm1"] += alg["gemm1_bytes"]
-        bytes_acc["gemm2"] += alg["gemm2_bytes"]
-        bytes_acc["route"] += alg["route_bytes"]
-        flops_acc["gemm1"] += alg["gemm1_flops"]
-        flops_acc["gemm2"] += alg["gemm2_flops"]
+        for key, v in algorithmic(wl, T, n_act, nv).items():
+            acc[key] += v
     torch.cuda.synchronize()
-    for ev in evs:
-        for j, name in enumerate(("route", "gemm1", "gemm2", "finalize")):
-            stage_ms[name].append(ev[j].elapsed_time(ev[j + 1]))
-    mean_ms = {kk: float(np.mean(v)) for kk, v in stage_ms.items()}
-    dominant = max(("gemm1", "gemm2"), key=lambda kk: mean_ms[kk])
-    n_launch = args.steps
-    dom_bytes = bytes_acc[dominant] / n_launch
-    dom_s = mean_ms[dominant] / 1e3
-    achieved = dom_bytes / dom_s / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": f"{dominant} ({'gemm1_kernel' if dominant == 'gemm1' else 'gemm2_kernel'})",
-                "alg_bytes_per_launch": int(dom_bytes), "avg_launch_us": round(mean_ms[dominant] * 1e3, 2)}
-    layer_bytes = (bytes_acc["gemm1"] + bytes_acc["gemm2"] + bytes_acc["route"]) / n_launch
-    stages = {kk: round(v * 1e3, 2) for kk, v in mean_ms.items()}
+    stage_ms = {name: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]))
+                for j, name in enumerate(("route", "gemm1", "gemm2", "finalize"))}
+    per = {key: v / steps for key, v in acc.items()}
+    layer_bytes = per["route"] + per["gemm1"] + per["gemm2"]
+    gemm = {}
+    for g in ("gemm1", "gemm2"):
+        t_s = stage_ms[g] / 1e3
+        gbs = per[g] / t_s / 1e9
+        tflops = per[g + "_flops"] / t_s / 1e12
+        t_hbm = per[g] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = per[g + "_flops"] / (MFMA_PEAK_TFLOPS[dtype] * 1e12)
+        gemm[g] = {"us": round(stage_ms[g] * 1e3, 2), "alg_bytes": int(per[g]), "GB/s": round(gbs, 1),
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOPS": round(tflops, 1),
+                   "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[dtype], 4),
+                   "binding": "hbm" if t_hbm >= t_mfma else "mfma",
+                   "frac_of_binding_floor": round(max(t_hbm, t_mfma) / t_s, 4)}
+    res = {
+        "workload": wl.name, "T": T, "dtype": dtype, "mode": mode, "us_per_call": round(ms_per_call * 1e3, 2),
+        "layer_alg_bytes": int(layer_bytes), "layer_hbm_floor_us": round(layer_bytes / HBM_PEAK_GBS / 1e3, 1),
+        "frac_of_layer_hbm_floor": round(layer_bytes / HBM_PEAK_GBS / 1e3 / (ms_per_call * 1e3), 4),
+        "mean_active_experts": round(float(np.mean(n_acts)), 1),
+        "stage_us": {kk: round(v * 1e3, 2) for kk, v in stage_ms.items()},
+        "route_GB/s": round(per["route"] / (stage_ms["route"] / 1e3) / 1e9, 1),
+        "gemm": gemm,
+    }
+    keep = (base, sets, rt)
+    return res, keep
+
+
+def measure_router(env, E, k, score, steps, warmup):
+    """Router-only (top-k + sort) at T = 8192, BLOCK_M = 32, input sets rotated past the
+    256 MB last-level cache."""
+    m, torch, np, synth, dev = env
+    T, B = synth.ROUTER_T, synth.ROUTER_BLOCK_M
+    R = max(2, -(-512 * 2**20 // (4 * T * E)))
+    sets = [synth.logits(T, E, seed=200 + r).to(dev) for r in range(R)]
+    cap = m.moe_sorted_capacity(T, E, k, B)
+    rt = {"topk_weights": torch.empty(T, k, device=dev), "topk_ids": torch.empty(T, k, dtype=torch.int32, device=dev),
+          "sorted_token_ids": torch.empty(cap, dtype=torch.int32, device=dev),
+          "expert_ids": torch.empty(cap // B, dtype=torch.int32, device=dev),
+          "num_valid": torch.empty(1, dtype=torch.int32, device=dev)}
+    nb = m.moe_route_workspace_bytes(T, E, k, B)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        m.moe_topk_softmax_sort(sets[i % R], k, B, score, out=rt, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    nv = int(rt["num_valid"].item())
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        m.moe_topk_softmax_sort(sets[i % R], k, B, score, out=rt, workspace=ws, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) / steps * 1e3
+    alg = 4 * T * E + 8 * T * k + 4 * nv + 4 * (nv // B) + 4
+    gbs = alg / (us * 1e-6) / 1e9
+    return {"router": f"{E}/{k}", "score": score, "T": T, "block_m": B, "us_per_call": round(us, 2),
+            "alg_bytes": alg, "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "rotating_input_sets": R}
+
+
+def cpu_baseline(env, wl, T, keep):
+    """The CPU oracle, timed on a bounded sample (the first tokens of one input set),
+    scaled to a whole call by active-expert count (its cost is per expert read)."""
+    m, torch, np, synth, dev = env
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    base, sets, rt = keep
+    hb = lambda t: t.detach().cpu().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()  # noqa: E731
+    s = sets[0]
+    host_logits = s["logits"].cpu().numpy()
+    host_x = hb(s["x"])
+    host_xs = s["x_scale"].cpu().numpy() if "x_scale" in s else None
+    r = oracle.route(host_logits, wl.topk, wl.block_m)
+    n_act_all = len(np.unique(r.ids))
+    sample_tokens = list(range(min(2, T)))
+    used = sorted(set(r.ids[sample_tokens].reshape(-1).tolist()))
+    W1 = {e: hb(base["w1"][e]) for e in used}   # host copies of exactly what the sample reads
+    W2 = {e: hb(base["w2"][e]) for e in used}
+    W1s = {e: base["w1_scale"][e].cpu().numpy() for e in used} if "w1_scale" in base else None
+    W2s = {e: base["w2_scale"][e].cpu().numpy() for e in used} if "w2_scale" in base else None
+    t0 = time.perf_counter()
+    r = oracle.route(host_logits, wl.topk, wl.block_m)
+    oracle.moe_layer(host_x, W1, W2, r.ids, r.weights, wl.dtype, x_scale=host_xs, w1_scale=W1s,
+                     w2_scale=W2s, tokens=sample_tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e6 * (n_act_all / len(used)), 1), "unit": "us/call", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"{wl.name} T={T}: routing of all {T} tokens plus the layer for tokens {sample_tokens} "
+                       f"({len(used)} of {n_act_all} active experts), fp64 numpy, {dt:.2f} s, scaled by "
+                       f"active experts; BLAS threads {blas_threads}, host logical CPUs {os.cpu_count()}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU "
+              "path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_amd as m
+    import synth
+
+    m.load_library()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    env = (m, torch, np, synth, dev)
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    wl = synth.WORKLOADS[args.workload]
+    head, keep = measure_layer(env, wl, args.T, args.steps, args.warmup, args.rotate)
+    g1 = head["gemm"]["gemm1"]
+    g2 = head["gemm"]["gemm2"]
+    dom_name, dom = max((("gemm1", g1), ("gemm2", g2)), key=lambda kv: kv[1]["us"])
+    if dom["binding"] == "hbm":
+        roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": dom["hbm_frac"], "traffic": None}
+    else:
+        roofline = {"bound": "mfma", "achieved": dom["TFLOPS"], "peak": MFMA_PEAK_TFLOPS[wl.dtype],
+                    "unit": "TFLOP/s", "frac": dom["mfma_frac"], "traffic": None}
+    roofline.update(kernel=f"{dom_name}_kernel", avg_launch_us=dom["us"], alg_bytes_per_launch=dom["alg_bytes"])
 
     cpu = None
     if not args.no_cpu:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        s = sets[0]
-        hb = lambda t: t.detach().cpu().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()  # noqa: E731
-        ids0 = None
-        m.moe_topk_softmax_sort(s["logits"], k, B, out=rt, workspace=rws, stream=stream)
-        torch.cuda.synchronize()
-        ids0 = rt["topk_ids"].cpu().numpy()
-        cpu = cpu_baseline(
-            wl, T, s["logits"].cpu().numpy(), hb(s["x"]),
-            s["x_scale"].cpu().numpy() if "x_scale" in s else None,
-            lambda e: hb(base["w1"][e]), lambda e: hb(base["w2"][e]),
-            (lambda e: base["w1_scale"][e].cpu().numpy()) if "w1_scale" in base else None,
-            (lambda e: base["w2_scale"][e].cpu().numpy()) if "w2_scale" in base else None,
-            len(np.unique(ids0)))
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(env, wl, args.T, keep)
+    del keep
+    torch.cuda.empty_cache()
+
+    secondary = []
+    if not args.headline_only:
+        for name, T in (("gptoss", 16), ("gptoss", 4096), ("kimi", 64), ("kimi", 4096), ("kimi", 16384)):
+            r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2)
+            del kp
+            torch.cuda.empty_cache()
+            secondary.append(r)
+        for (E, k) in synth.ROUTER_CASES:
+            for score in ("softmax", "sigmoid"):
+                secondary.append(measure_router(env, E, k, score, args.steps, 3))
+        torch.cuda.empty_cache()
 
     res = {
-        "metric": f"moe_layer_us_per_call_T{T}_decode" if args.workload == "deepseek" else f"moe_layer_us_per_call_{wl.name}_T{T}",
-        "value": round(ms_per_step * 1e3, 2),
+        "metric": f"moe_layer_us_per_call_T{args.T}_decode" if args.workload == "deepseek"
+        else f"moe_layer_us_per_call_{wl.name}_T{args.T}",
+        "value": head["us_per_call"],
         "unit": "us/call",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(head["us_per_call"] / 1e3, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}-shaped MoE layer forward", "T": T, "E": E, "topk": k, "D": D,
-                   "I": I, "block_m": B, "mode": mode, "score": "softmax", "renorm": True,
-                   "rotating_input_sets": args.rotate},
+        "config": {"workload": f"{wl.name}-shaped MoE layer forward, T={args.T}", "T": args.T, "E": wl.E,
+                   "topk": wl.topk, "D": wl.D, "I": wl.I, "block_m": wl.block_m, "mode": wl.mode,
+                   "score": "softmax", "renorm": True, "rotating_input_sets": args.rotate},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "layer": {"alg_bytes_per_call": int(layer_bytes), "hbm_floor_us": round(layer_bytes / HBM_PEAK_GBS / 1e3, 1),
-                  "frac_of_hbm_floor": round(layer_bytes / HBM_PEAK_GBS / 1e3 / (ms_per_step * 1e3), 4),
-                  "mean_active_experts": round(float(np.mean(n_acts)), 1), "stage_us": stages},
+        "layer": head,
+        "secondary": secondary,
     }
     print(json.dumps(res))
 
