@@ -47,6 +47,44 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def graph_ms_per_call(torch, calls, n, reps=5):
+    """ms per call of `calls(i, stream)` for i in range(n), captured back to back in one HIP
+    graph and replayed (median over `reps` replays).  Host launch cost is excluded, as in the
+    graph-replay measurement of the mxfp4 page ("Measurement").  Falls back to eager launches
+    if the capture fails."""
+    stream = torch.cuda.current_stream()
+    for i in range(min(n, 3)):
+        calls(i, stream)
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            for i in range(n):
+                calls(i, cs)
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / n)
+        del g
+        return sorted(times)[len(times) // 2], "hip-graph"
+    except Exception as exc:  # pragma: no cover - capture not available
+        log(f"graph capture failed ({exc}); timing eager launches")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            calls(i, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, "eager"
+
+
 def algorithmic(wl, T, n_act, num_valid):
     """Bytes and FLOPs the method must move/compute (padding, fp32 accumulator traffic,
     weight re-reads and atomic read-modify-writes excluded)."""
@@ -79,62 +117,57 @@ def measure_layer(env, wl, T, steps, warmup, rotate):
     out = torch.empty(T, D, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def layer_call(i, st):
         s = sets[i % len(sets)]
         m.moe_forward(dtype, s["logits"], s["x"], base["w1"], base["w2"], k, B, mode,
                       x_scale=s.get("x_scale"), w1_scale=base.get("w1_scale"),
-                      w2_scale=base.get("w2_scale"), workspace=ws, out=out, stream=stream)
+                      w2_scale=base.get("w2_scale"), workspace=ws, out=out, stream=st)
 
     for i in range(warmup):
-        step(i)
+        layer_call(i, stream)
     torch.cuda.synchronize()
-    log(f"timing {steps} moe_forward calls")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_call = ev0.elapsed_time(ev1) / steps
+    log(f"timing {steps} moe_forward calls (graph replay)")
+    ms_per_call, how = graph_ms_per_call(torch, layer_call, steps)
 
-    # per-stage durations: staged calls, every step enqueued before one synchronisation so
-    # the GPU never idles inside a bracketed interval
+    # per-stage durations: each stage alone, `steps` calls per graph, on per-set routing
     views = m.workspace_views(ws, offs, dtype, mode, T, E, k, D, I, B)
-    rt = {kk: views[kk] for kk in ("topk_weights", "topk_ids", "sorted_token_ids", "expert_ids", "num_valid")}
     a, a_scale, y = views["a"], views["a_scale"], views["y"]
     g1ws = ws[offs["gemm1_scratch"]:] if offs["gemm1_scratch"] is not None else None
     rws = ws[offs["route_scratch"]:] if offs["route_scratch"] is not None else None
-    per_set = []
-    for s in sets:  # active experts and num_valid of each input set (untimed)
-        m.moe_topk_softmax_sort(s["logits"], k, B, out=rt, workspace=rws, stream=stream)
+    routes, per_set = [], []
+    for s in sets:  # routing of each input set into its own buffers; active experts (untimed)
+        r = m.moe_topk_softmax_sort(s["logits"], k, B, workspace=rws, stream=stream)
         torch.cuda.synchronize()
-        per_set.append((len(np.unique(rt["topk_ids"].cpu().numpy())), int(rt["num_valid"].item())))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        routes.append(r)
+        per_set.append((len(np.unique(r["topk_ids"].cpu().numpy())), int(r["num_valid"].item())))
+
+    def route_call(i, st):
+        j = i % len(sets)
+        m.moe_topk_softmax_sort(sets[j]["logits"], k, B, out=routes[j], workspace=rws, stream=st)
+
+    def gemm1_call(i, st):
+        j = i % len(sets)
+        m.moe_gemm1_gateup(dtype, sets[j]["x"], base["w1"], routes[j], k, B, x_scale=sets[j].get("x_scale"),
+                           w1_scale=base.get("w1_scale"), a=a, a_scale=a_scale, workspace=g1ws, stream=st)
+
+    def gemm2_call(i, st):
+        j = i % len(sets)
+        m.moe_gemm2_down(dtype, a, base["w2"], routes[j], T, k, B, mode, a_scale=a_scale,
+                         w2_scale=base.get("w2_scale"), y=y, stream=st)
+
+    def fin_call(i, st):
+        m.moe_finalize(mode, y, T, k, D, out=out, stream=st)
+
+    stage_ms = {}
+    for name, fn in (("route", route_call), ("gemm1", gemm1_call), ("gemm2", gemm2_call), ("finalize", fin_call)):
+        stage_ms[name], _ = graph_ms_per_call(torch, fn, steps)
     acc = {"route": 0, "gemm1": 0, "gemm2": 0, "gemm1_flops": 0, "gemm2_flops": 0}
     n_acts = []
     for i in range(steps):
-        s = sets[i % len(sets)]
-        ev = evs[i]
-        if mode == "atomic":
-            y.zero_()  # outside every bracketed interval
-        ev[0].record(stream)
-        m.moe_topk_softmax_sort(s["logits"], k, B, out=rt, workspace=rws, stream=stream)
-        ev[1].record(stream)
-        m.moe_gemm1_gateup(dtype, s["x"], base["w1"], rt, k, B, x_scale=s.get("x_scale"),
-                           w1_scale=base.get("w1_scale"), a=a, a_scale=a_scale, workspace=g1ws, stream=stream)
-        ev[2].record(stream)
-        m.moe_gemm2_down(dtype, a, base["w2"], rt, T, k, B, mode, a_scale=a_scale,
-                         w2_scale=base.get("w2_scale"), y=y, stream=stream)
-        ev[3].record(stream)
-        m.moe_finalize(mode, y, T, k, D, out=out, stream=stream)
-        ev[4].record(stream)
         n_act, nv = per_set[i % len(sets)]
         n_acts.append(n_act)
         for key, v in algorithmic(wl, T, n_act, nv).items():
             acc[key] += v
-    torch.cuda.synchronize()
-    stage_ms = {name: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]))
-                for j, name in enumerate(("route", "gemm1", "gemm2", "finalize"))}
     per = {key: v / steps for key, v in acc.items()}
     layer_bytes = per["route"] + per["gemm1"] + per["gemm2"]
     gemm = {}
@@ -151,6 +184,7 @@ def measure_layer(env, wl, T, steps, warmup, rotate):
                    "frac_of_binding_floor": round(max(t_hbm, t_mfma) / t_s, 4)}
     res = {
         "workload": wl.name, "T": T, "dtype": dtype, "mode": mode, "us_per_call": round(ms_per_call * 1e3, 2),
+        "timing": how,
         "layer_alg_bytes": int(layer_bytes), "layer_hbm_floor_us": round(layer_bytes / HBM_PEAK_GBS / 1e3, 1),
         "frac_of_layer_hbm_floor": round(layer_bytes / HBM_PEAK_GBS / 1e3 / (ms_per_call * 1e3), 4),
         "mean_active_experts": round(float(np.mean(n_acts)), 1),
@@ -158,7 +192,7 @@ def measure_layer(env, wl, T, steps, warmup, rotate):
         "route_GB/s": round(per["route"] / (stage_ms["route"] / 1e3) / 1e9, 1),
         "gemm": gemm,
     }
-    keep = (base, sets, rt)
+    keep = (base, sets)
     return res, keep
 
 
@@ -177,22 +211,20 @@ def measure_router(env, E, k, score, steps, warmup):
     nb = m.moe_route_workspace_bytes(T, E, k, B)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    def call(i, st):
+        m.moe_topk_softmax_sort(sets[i % R], k, B, score, out=rt, workspace=ws, stream=st)
+
     for i in range(warmup):
-        m.moe_topk_softmax_sort(sets[i % R], k, B, score, out=rt, workspace=ws, stream=stream)
+        call(i, stream)
     torch.cuda.synchronize()
     nv = int(rt["num_valid"].item())
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps):
-        m.moe_topk_softmax_sort(sets[i % R], k, B, score, out=rt, workspace=ws, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) / steps * 1e3
+    ms, how = graph_ms_per_call(torch, call, max(steps, R))
+    us = ms * 1e3
     alg = 4 * T * E + 8 * T * k + 4 * nv + 4 * (nv // B) + 4
     gbs = alg / (us * 1e-6) / 1e9
     return {"router": f"{E}/{k}", "score": score, "T": T, "block_m": B, "us_per_call": round(us, 2),
             "alg_bytes": alg, "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "rotating_input_sets": R}
+            "rotating_input_sets": R, "timing": how}
 
 
 def cpu_baseline(env, wl, T, keep):
@@ -205,7 +237,7 @@ def cpu_baseline(env, wl, T, keep):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    base, sets, rt = keep
+    base, sets = keep
     hb = lambda t: t.detach().cpu().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()  # noqa: E731
     s = sets[0]
     host_logits = s["logits"].cpu().numpy()

@@ -361,6 +361,220 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------- prefill tiles
+// Many gathered rows per expert (prefill): the same weight tile serves several 64-row
+// blocks, and the MFMA units, not HBM, set the pace.  Block = one 64-row block of the
+// sorted list x 256 weight rows; wave = 64 weight rows (4 groups of 16) x the 64
+// gathered rows (4 tiles of 16).
+//  * the gathered rows are staged in LDS, 512 K-bytes per row per stage, double
+//    buffered with one barrier per stage; 16-byte segment s of row r sits at segment
+//    s ^ (r & 15), so the 16 rows that 16 lanes of an operand read touch land in 16
+//    different bank groups;
+//  * weight rows stream from HBM/L2 straight into registers, one 128-byte chunk ahead;
+//  * stage 1 (gate-up): weight rows are the first MFMA operand, so a lane ends up with 4
+//    consecutive channels of one slot (gate and up pair in the same lane);
+//  * stage 2 (down): the operands are swapped, so a lane holds one model_dim channel of
+//    4 slots and 16 lanes cover 16 consecutive channels of one slot: each atomic (or
+//    store) instruction writes 64 contiguous bytes per row.
+enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2 };
+constexpr int kPfRows = 64;
+constexpr int kPfStage = 512;
+
+template <bool FP8, int MODE>
+__global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(
+    const uint8_t* __restrict__ act, const float* __restrict__ act_scale,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
+    int k, int N, int K, int mbs, void* __restrict__ out, float4* __restrict__ zero_y,
+    int64_t zero_n4) {
+  constexpr bool G1 = MODE == PF_G1;
+  constexpr int EB = FP8 ? 1 : 2;
+  __shared__ __align__(16) uint8_t tok[2][kPfRows * kPfStage];
+  __shared__ int s_slot[kPfRows];
+  if (zero_y)
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 256)
+      zero_y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // gemm1: N = I channels, a tile = 128 channels (256 weight rows); gemm2: N = D rows, tile = 256
+  const int tile_n = G1 ? 128 : 256;
+  int mb, nt;
+  if (!block_tile(mbs, (N + tile_n - 1) / tile_n, mb, nt)) return;
+  if (mb * kPfRows >= *num_valid) return;
+  const int e = expert_ids[mb];
+  if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int n_slots = T * k;
+  const int rowb = K * EB;
+  if (tid < kPfRows) s_slot[tid] = sorted_ids[mb * kPfRows + tid];
+
+  __syncthreads();  // s_slot
+  // staging: store instruction i moves 16-byte segment (tid & 31) of row i*8 + tid/32, so
+  // 32 lanes read 512 contiguous bytes of one row and 16 lanes write 16 different banks
+  const i32x4_t zero = {0, 0, 0, 0};
+  const int sseg = tid & 31;
+  const uint8_t* src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = s_slot[i * 8 + (tid >> 5)];
+    src[i] = (unsigned)s < (unsigned)n_slots ? act + (size_t)(G1 ? s / k : s) * rowb : nullptr;
+  }
+  i32x4_t stg[8];
+  auto load_stage = [&](int st) {
+    const int off = st * kPfStage + 16 * sseg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) stg[i] = (src[i] && off < rowb) ? ld16(src[i] + off) : zero;
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 8 + (tid >> 5);
+      *reinterpret_cast<i32x4_t*>(&tok[buf][r * kPfStage + 16 * (sseg ^ (r & 15))]) = stg[i];
+    }
+  };
+
+  // this wave's weight rows
+  int row0;       // gemm1: first gate channel of the wave; gemm2: first model_dim row
+  bool on;
+  const uint8_t* wrow[4];
+  if constexpr (G1) {
+    row0 = nt * 128 + wave * 32;
+    on = row0 < N;
+    const size_t eb = (size_t)e * 2 * N;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wrow[q] = w + (eb + (q >= 2 ? N : 0) + (on ? row0 : 0) + 16 * (q & 1) + i16) * (size_t)rowb;
+  } else {
+    row0 = nt * 256 + wave * 64;
+    on = row0 < N;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wrow[q] = w + ((size_t)e * N + (on ? row0 : 0) + 16 * q + i16) * (size_t)rowb;
+  }
+  const int nch = (rowb + 127) >> 7;
+  const int nst = (rowb + kPfStage - 1) / kPfStage;
+  i32x4_t wb[2][4][2];
+  auto load_w = [&](int gc, int slot) {
+    const int off = gc * 128 + 16 * g;
+    const bool in0 = on && gc < nch;
+    const bool in1 = in0 && off + 64 < rowb + 16 * g;  // second half exists (not a half last chunk)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wb[slot][q][0] = in0 ? ld16(wrow[q] + off) : zero;
+      wb[slot][q][1] = in1 ? ld16(wrow[q] + off + 64) : zero;
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load_stage(0);
+  store_stage(0);
+  load_w(0, 0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) load_stage(st + 1);
+    const uint8_t* tb = tok[st & 1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int gc = st * 4 + c;
+      load_w(gc + 1, (c + 1) & 1);
+      if (on && gc < nch) {
+        i32x4_t tf[4][2];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int r = tt * 16 + i16;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int sgm = (8 * c + 4 * h + g) ^ (r & 15);
+            tf[tt][h] = *reinterpret_cast<const i32x4_t*>(&tb[r * kPfStage + 16 * sgm]);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            if constexpr (G1) mfma_chunk<FP8>(acc[q][tt], wb[c & 1][q], tf[tt]);
+            else mfma_chunk<FP8>(acc[q][tt], tf[tt], wb[c & 1][q]);
+          }
+      }
+      // the next stage's rows go to the other buffer mid-stage: that buffer was last read
+      // before the previous barrier, and the staging loads (issued before this stage's
+      // weight prefetches) have landed by now
+      if (c == 1 && st + 1 < nst) store_stage((st + 1) & 1);
+    }
+    // LDS-only barrier: the weight prefetch for the next chunk stays in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  if (!on) return;
+
+  if constexpr (G1) {
+    // acc[q][tt][r]: channel row0 + 16*(q&1) + 4g + r (q<2 gate, q>=2 up), slot column i16
+    const int I = N;
+    uint16_t* a_out = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n0 = row0 + 16 * h + 4 * g;
+      float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (FP8) {
+        const float* ws = w_scale + (size_t)e * 2 * I;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sg[r] = ws[n0 + r];
+          su[r] = ws[I + n0 + r];
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int s = s_slot[tt * 16 + i16];
+        if ((unsigned)s >= (unsigned)n_slots) continue;
+        float xs = 1.f;
+        if constexpr (FP8) xs = act_scale[s / k];
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[r] = silu_mul(acc[h][tt][r] * (sg[r] * xs), acc[2 + h][tt][r] * (su[r] * xs));
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(a_out + (size_t)s * I + n0) = pk;
+      }
+    }
+  } else {
+    // acc[q][tt][r]: slot row tt*16 + 4g + r, model_dim channel row0 + 16q + i16
+    const int D = N;
+    float* y = reinterpret_cast<float*>(out);
+    float ws[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (FP8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ws[q] = w_scale[(size_t)e * D + row0 + 16 * q + i16];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = s_slot[tt * 16 + 4 * g + r];
+        if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
+        float sc = topk_w[s];
+        if constexpr (FP8) sc *= act_scale[s];
+        float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / k) * D + row0 + i16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float c = acc[q][tt][r] * (FP8 ? sc * ws[q] : sc);
+          if constexpr (MODE == PF_G2_REDUCE) dst[16 * q] = c;
+          else atomicAdd(dst + 16 * q, c);
+        }
+      }
+  }
+}
+
+// The tiled kernel pays off once the experts carry several 64-row blocks on average.
+static bool use_prefill(int B, int64_t T, int k, int E) {
+  return B == kPfRows && T * k >= 32LL * E;
+}
+
 // ----------------------------------------------------------------------------- combine
 __global__ void __launch_bounds__(256) finalize_atomic_kernel(const float* __restrict__ y, int64_t n4,
                                                               uint16_t* __restrict__ out) {
@@ -463,6 +677,22 @@ hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void
   if (T == 0) return hipSuccess;
   uint16_t* a_bf16 = fp8 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
   const int mbs = (int)(cap / B);
+  if (use_prefill(B, T, k, E)) {
+    const dim3 grid(xcd_grid(mbs, (I + 127) / 128));
+    if (fp8)
+      gemm_prefill_kernel<true, PF_G1><<<grid, 256, 0, st>>>(
+          (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, nullptr, sorted_ids, expert_ids,
+          num_valid, T, E, k, I, D, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
+    else
+      gemm_prefill_kernel<false, PF_G1><<<grid, 256, 0, st>>>(
+          (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, nullptr, sorted_ids, expert_ids,
+          num_valid, T, E, k, I, D, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !fp8) return err;
+    const int rows = T * k;
+    requant_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>(a_bf16, rows, I, reinterpret_cast<uint8_t*>(a), a_scale);
+    return hipGetLastError();
+  }
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int ks = pick_ks(n_act * (I / 16));  // a block covers 16*(4/ks) channels; I % 64 == 0
 #define MOE_G1(BMV)                                                                                   \
@@ -517,6 +747,20 @@ hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void
                         int E, int k, int D, int I, int B, int mode, float* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int mbs = (int)(cap / B);
+  if (use_prefill(B, T, k, E)) {
+    const dim3 grid(xcd_grid(mbs, (D + 255) / 256));
+#define MOE_PF2(F8, MD)                                                                              \
+  gemm_prefill_kernel<F8, MD><<<grid, 256, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,  \
+                                                   w2_scale, topk_w, sorted_ids, expert_ids,        \
+                                                   num_valid, T, E, k, D, I, mbs, y, nullptr, 0)
+    if (fp8) {
+      if (mode) MOE_PF2(true, PF_G2_REDUCE); else MOE_PF2(true, PF_G2_ATOMIC);
+    } else {
+      if (mode) MOE_PF2(false, PF_G2_REDUCE); else MOE_PF2(false, PF_G2_ATOMIC);
+    }
+#undef MOE_PF2
+    return hipGetLastError();
+  }
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int ks = pick_ks(n_act * (D / 32));  // ks >= 2 needs D % 64 == 0, which always holds
 #define MOE_G2(BMV)                                                                                   \

@@ -38,49 +38,94 @@ __device__ __forceinline__ uint64_t pick_key(uint32_t key, int expert) {
 __device__ __forceinline__ int pick_expert(uint64_t p) { return (int)(~(uint32_t)p); }
 __device__ __forceinline__ uint32_t pick_logit_key(uint64_t p) { return (uint32_t)(p >> 32); }
 
-// ----------------------------------------------------------------------------- wave shuffles
-__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m) {
-  return (uint32_t)__shfl_xor((int)v, m, kWave);
+// ----------------------------------------------------------------------------- wave exchanges
+// Value of lane (lane ^ M), in VALU instructions only (no LDS round trip): DPP quad
+// permutes for 1 and 2, DPP row rotates for 4 and 8, and gfx950's permlane16/32 swaps for
+// 16 and 32.  Lane mappings were checked on the hardware.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const int x = (int)v;
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const int lo = __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false);   // row_ror:4  (i <- i-4)
+    const int hi = __builtin_amdgcn_mov_dpp(x, 0x12C, 0xF, 0xF, false);   // row_ror:12 (i <- i+4)
+    return (uint32_t)((__lane_id() & 4) ? lo : hi);
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "xor distance must be a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() & 32) ? r[0] : r[1];
+  }
 }
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = shfl_xor_u32((uint32_t)v, m), hi = shfl_xor_u32((uint32_t)(v >> 32), m);
+// Run-time distance (folded to one case once the caller's loop is unrolled).
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int m) {
+  switch (m) {
+    case 1: return xor_lane<1>(v);
+    case 2: return xor_lane<2>(v);
+    case 4: return xor_lane<4>(v);
+    case 8: return xor_lane<8>(v);
+    case 16: return xor_lane<16>(v);
+    default: return xor_lane<32>(v);
+  }
+}
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v, int m) {
+  const uint32_t lo = xor_lane_u32((uint32_t)v, m), hi = xor_lane_u32((uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, kWave);
-  uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, kWave);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m) { return xor_lane_u32(v, m); }
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) { return xor_lane_u64(v, m); }
+// Broadcast of lane `src` (wave-uniform) through a scalar register.
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int src) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  return ((uint64_t)readlane_u32((uint32_t)(v >> 32), src) << 32) | readlane_u32((uint32_t)v, src);
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  for (int m = 32; m >= 1; m >>= 1) v += __uint_as_float(xor_lane_u32(__float_as_uint(v), m));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t b = xor_lane_u64(__double_as_longlong(v), m);
+    v += __longlong_as_double((long long)b);
+  }
   return v;
 }
 __device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  for (int m = 32; m >= 1; m >>= 1) v += (int)xor_lane_u32((uint32_t)v, m);
   return v;
 }
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __uint_as_float(xor_lane_u32(__float_as_uint(v), m)));
   return v;
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t p = shfl_xor_u64(v, m);
+    const uint64_t p = xor_lane_u64(v, m);
     v = p > v ? p : v;
   }
   return v;
 }
-// Inclusive prefix sum over the wave (Hillis-Steele with shuffles).
+// Inclusive prefix sum over the wave (Hillis-Steele with shuffles; off the per-token path).
 __device__ __forceinline__ int wave_incl_scan_i32(int v) {
-  int lane = lane_id();
+  const int lane = lane_id();
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    int p = __shfl_up(v, d, kWave);
+    const int p = __shfl_up(v, d, kWave);
     if (lane >= d) v += p;
   }
   return v;
@@ -113,11 +158,11 @@ __device__ __forceinline__ void bitonic128_desc(uint64_t& v0, uint64_t& v1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (stride == 64) {
         // positions lane and lane+64 of one register pair; size == 128 here
-        uint64_t hi = v0 > v1 ? v0 : v1, lo = v0 > v1 ? v1 : v0;
+        const uint64_t hi = v0 > v1 ? v0 : v1, lo = v0 > v1 ? v1 : v0;
         v0 = hi;
         v1 = lo;
       } else {
-        uint64_t p0 = shfl_xor_u64(v0, stride), p1 = shfl_xor_u64(v1, stride);
+        const uint64_t p0 = shfl_xor_u64(v0, stride), p1 = shfl_xor_u64(v1, stride);
         const bool lower = (lane & stride) == 0;
         const bool km0 = ((lane & size) == 0) == lower;
         const bool km1 = (((lane + 64) & size) == 0) == lower;

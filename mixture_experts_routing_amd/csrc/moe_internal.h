@@ -10,11 +10,12 @@ namespace moe {
 // Routing: largest T and E handled by the single-workgroup path.
 constexpr int kOneShotMaxT = 64;
 constexpr int kOneShotMaxE = 1024;
-// Multi-workgroup routing: tokens per sort chunk (16 waves x 16 tokens).
-constexpr int kChunkTokens = 256;
+constexpr int kOneShotMaxSlots = 4096;
+// Multi-workgroup routing: tokens per sort chunk (16 waves x 4 tokens).
+constexpr int kChunkTokens = 64;
 
 int64_t sorted_capacity(int64_t T, int64_t E, int64_t k, int64_t B);
-bool route_is_oneshot(int T, int E);
+bool route_is_oneshot(int T, int E, int k);
 int64_t route_workspace_bytes(int T, int E, int k);
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int score, int renorm, int B,

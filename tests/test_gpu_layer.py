@@ -74,6 +74,10 @@ SMALL_BF16 = [
     (61, 12, 3, 320, 128, 64),
     (5, 6, 6, 192, 256, 32),
     (200, 40, 5, 256, 64, 64),
+    # BLOCK_M = 64 with T*k >= 32*E: the LDS-tiled prefill kernels, with a partial channel
+    # tile, a partial model_dim tile and a ragged second K stage
+    (300, 8, 2, 320, 192, 64),
+    (640, 8, 4, 384, 512, 64),
 ]
 # fp8: the intermediate is requantised per row from bf16 values that the GPU (fp32 MFMA
 # sums) and the oracle (fp64) may round one bf16 ulp apart; such a pair can land on
@@ -85,6 +89,9 @@ SMALL_FP8 = [
     (37, 16, 4, 320, 576, 32),
     (61, 12, 3, 320, 512, 64),
     (200, 40, 5, 256, 640, 64),
+    # prefill kernels; D = 320 and I = 576 leave a half 128-byte chunk at the end of K
+    (300, 8, 2, 320, 576, 64),
+    (640, 8, 4, 384, 1024, 64),
 ]
 SMALL = [(*c, "bf16") for c in SMALL_BF16] + [(*c, "fp8") for c in SMALL_FP8]
 
@@ -105,8 +112,12 @@ def test_layer_small_full_compare(T, E, k, D, I, B, dtype, mode):
     else:
         compare_out(out, ref.out, rows, FP8_TOL, None)
     if mode == "reduce":
-        tol = BF16_TOL if dtype == "bf16" else FP8_TOL
-        compare_out(views["y"], ref.contrib, np.arange(T * k), tol, None)
+        # slot rows (diagnostic): in fp8 one flipped requant code is not averaged over the
+        # k slots of a token, so the per-row bound is looser than the layer-output bound
+        if dtype == "bf16":
+            compare_out(views["y"], ref.contrib, np.arange(T * k), BF16_TOL, BF16_COS)
+        else:
+            compare_out(views["y"], ref.contrib, np.arange(T * k), 0.2, BF16_COS)
     check_intermediate(views, ref, dtype, np.arange(T * k))
 
 
