@@ -413,23 +413,33 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(
   // 32 lanes read 512 contiguous bytes of one row and 16 lanes write 16 different banks
   const i32x4_t zero = {0, 0, 0, 0};
   const int sseg = tid & 31;
+  // Every load below is unconditional (addresses are clamped to valid memory), so the
+  // compiler emits straight-line code and counts outstanding loads exactly; the zero
+  // fill of padding rows and of K past the row end is applied when the rows go to LDS.
   const uint8_t* src[8];
+  uint32_t row_ok = 0;  // bit i: staging row i holds a real slot
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int s = s_slot[i * 8 + (tid >> 5)];
-    src[i] = (unsigned)s < (unsigned)n_slots ? act + (size_t)(G1 ? s / k : s) * rowb : nullptr;
+    const bool ok = (unsigned)s < (unsigned)n_slots;
+    row_ok |= (ok ? 1u : 0u) << i;
+    src[i] = act + (size_t)(ok ? (G1 ? s / k : s) : 0) * rowb;
   }
   i32x4_t stg[8];
+  int stg_off = 0;
   auto load_stage = [&](int st) {
-    const int off = st * kPfStage + 16 * sseg;
+    stg_off = st * kPfStage + 16 * sseg;
+    const int off = stg_off < rowb ? stg_off : 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) stg[i] = (src[i] && off < rowb) ? ld16(src[i] + off) : zero;
+    for (int i = 0; i < 8; ++i) stg[i] = ld16(src[i] + off);
   };
   auto store_stage = [&](int buf) {
+    const bool in_k = stg_off < rowb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = i * 8 + (tid >> 5);
-      *reinterpret_cast<i32x4_t*>(&tok[buf][r * kPfStage + 16 * (sseg ^ (r & 15))]) = stg[i];
+      const bool keep = in_k && ((row_ok >> i) & 1u);
+      *reinterpret_cast<i32x4_t*>(&tok[buf][r * kPfStage + 16 * (sseg ^ (r & 15))]) = keep ? stg[i] : zero;
     }
   };
 
@@ -454,14 +464,16 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(
   const int nch = (rowb + 127) >> 7;
   const int nst = (rowb + kPfStage - 1) / kPfStage;
   i32x4_t wb[2][4][2];
+  // chunks past the row end are loaded from chunk 0 (never used: their MFMAs are skipped);
+  // the second half of a half last chunk multiplies rows that LDS holds as zeros
   auto load_w = [&](int gc, int slot) {
-    const int off = gc * 128 + 16 * g;
-    const bool in0 = on && gc < nch;
-    const bool in1 = in0 && off + 64 < rowb + 16 * g;  // second half exists (not a half last chunk)
+    const int cc = gc < nch ? gc : 0;
+    const int off0 = cc * 128 + 16 * g;
+    const int off1 = cc * 128 + 64 < rowb ? off0 + 64 : off0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      wb[slot][q][0] = in0 ? ld16(wrow[q] + off) : zero;
-      wb[slot][q][1] = in1 ? ld16(wrow[q] + off + 64) : zero;
+      wb[slot][q][0] = ld16(wrow[q] + off0);
+      wb[slot][q][1] = ld16(wrow[q] + off1);
     }
   };
   f32x4_t acc[4][4];

@@ -78,6 +78,8 @@ SMALL_BF16 = [
     # tile, a partial model_dim tile and a ragged second K stage
     (300, 8, 2, 320, 192, 64),
     (640, 8, 4, 384, 512, 64),
+    # long rows (2 KB) through the prefill kernels
+    (256, 4, 2, 1024, 1088, 64),
 ]
 # fp8: the intermediate is requantised per row from bf16 values that the GPU (fp32 MFMA
 # sums) and the oracle (fp64) may round one bf16 ulp apart; such a pair can land on
@@ -92,6 +94,8 @@ SMALL_FP8 = [
     # prefill kernels; D = 320 and I = 576 leave a half 128-byte chunk at the end of K
     (300, 8, 2, 320, 576, 64),
     (640, 8, 4, 384, 1024, 64),
+    # long fp8 rows; 2112-byte rows end in a half 128-byte chunk
+    (200, 4, 2, 2112, 2112, 64),
 ]
 SMALL = [(*c, "bf16") for c in SMALL_BF16] + [(*c, "fp8") for c in SMALL_FP8]
 
