@@ -149,6 +149,25 @@ __device__ __forceinline__ T bitonic64_desc(T v) {
   return v;
 }
 
+// Descending bitonic sort across the wave of values replicated within aligned groups of L
+// lanes (L a power of two, wave-uniform).  Stages whose partner lane lies inside the same
+// group would compare equal values and are skipped, so G = 64/L groups cost
+// log2(G)(log2(G)+1)/2 exchanges; the j-th largest group value ends at lane j*L.
+__device__ __forceinline__ uint32_t bitonic64_desc_grouped(uint32_t v, int L) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < L) continue;
+      const uint32_t p = shfl_xor_u32(v, stride);
+      const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      v = keep_max ? (v > p ? v : p) : (v < p ? v : p);
+    }
+  }
+  return v;
+}
+
 // Bitonic sort of 128 u64 values, v0 at position lane and v1 at lane+64, descending.
 __device__ __forceinline__ void bitonic128_desc(uint64_t& v0, uint64_t& v1) {
   const int lane = lane_id();

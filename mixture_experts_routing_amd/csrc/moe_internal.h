@@ -8,14 +8,22 @@
 namespace moe {
 
 // Routing: largest T and E handled by the single-workgroup path.
-constexpr int kOneShotMaxT = 64;
+constexpr int kOneShotMaxT = 16;
 constexpr int kOneShotMaxE = 1024;
 constexpr int kOneShotMaxSlots = 4096;
 // Multi-workgroup routing: tokens per sort chunk (16 waves x 4 tokens).
 constexpr int kChunkTokens = 64;
+// Two-launch routing (select, then a one-workgroup sort): at most 8 tokens per wave; the
+// byte histograms hold per-expert ranks up to T (< 256); with two int arrays per expert
+// they take at most 61.5 KB of LDS.
+constexpr int kSort1MaxT = 128;
+constexpr int kSort1MaxE = 2560;
+// per-expert ranks inside a one-workgroup sort or a 64-token chunk live in LDS bytes
+static_assert(kOneShotMaxT <= 255 && kSort1MaxT <= 255 && kChunkTokens <= 255, "byte ranks");
 
 int64_t sorted_capacity(int64_t T, int64_t E, int64_t k, int64_t B);
 bool route_is_oneshot(int T, int E, int k);
+bool route_is_twostage(int T, int E, int k);
 int64_t route_workspace_bytes(int T, int E, int k);
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int score, int renorm, int B,

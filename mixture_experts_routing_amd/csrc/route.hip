@@ -9,21 +9,25 @@
 // Design (gfx950, wave64):
 //  * one wavefront per token.  Lane l holds the logits of experts l, l+64, ...
 //    as order-preserving u32 keys.
-//  * selection: the k-th largest of the 64 per-lane maxima is a threshold that
-//    at least k keys reach; the keys at or above it (typically a few dozen) are
-//    compacted into LDS (a ballot per register gives each lane its slot) and
-//    bitonic-sorted across the wave as (key, ~expert) pairs.  All cross-lane steps
-//    are DPP/permlane exchanges.  If more than 128 keys reach the threshold (heavy
-//    ties) or k > 64, a slower exact path extracts the maximum k times.
+//  * selection: the lanes form G groups (G the power of two >= 2k, at most 64); the
+//    k-th largest of the G group maxima is a threshold that at least k keys reach.
+//    The keys at or above it (typically a few to a few dozen) are compacted into LDS
+//    (a ballot per register gives each lane its slot), and each candidate's rank is
+//    the number of larger (key, ~expert) pairs among them.  All cross-lane steps are
+//    DPP/permlane exchanges or scalar broadcasts.  If more than 128 keys reach the
+//    threshold (heavy ties) or k > 64, a slower exact path extracts the maximum k times.
 //  * sort: experts are ranked per token in descending order, slots s = t*k + j.
 //    A token never picks an expert twice, so a slot's rank inside its expert's
 //    list is the number of earlier tokens that picked the same expert.  Waves
 //    own contiguous token ranges; each wave counts its picks into its own LDS
 //    byte histogram, a per-expert prefix over waves gives each wave's base,
 //    and each wave then places its slots walking its tokens in order.
-//  * T <= 64, E <= 1024 and T*k <= 4096: everything in one 1024-thread workgroup.
-//    Otherwise: select -> per-chunk counts -> per-expert prefix over chunks -> padded
-//    scan over experts -> per-chunk scatter (five launches, 64-token chunks).
+//  * T <= 16, E <= 1024 and T*k <= 4096: everything in one 1024-thread workgroup.
+//  * T <= 128, E <= 2560: select (one token per wave; also the sentinel fill of the sort
+//    outputs) -> one-workgroup sort (two launches).
+//  * Otherwise: select -> per-chunk counts -> per-expert prefix over chunks with a
+//    padded scan per 64 experts -> per-chunk scatter, which also combines the group
+//    offsets and writes the block experts (four launches, 64-token chunks).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -39,104 +43,56 @@ __device__ __forceinline__ double score_of(double l, double m, bool softmax) {
 }
 
 // Softmax denominator over all E logits of the token (only for softmax without
-// renormalisation): sum exp(l - max).
+// renormalisation): sum exp(l - max).  Empty slots hold NaN.
 template <int NV>
-__device__ double full_softmax_denominator(const uint32_t (&keys)[NV], int E, double m) {
-  const int lane = lane_id();
+__device__ double full_softmax_denominator(const float (&x)[NV], double m) {
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    if (lane + 64 * i < E) s += exp((double)key_logit(keys[i]) - m);
+    if (x[i] == x[i]) s += exp((double)x[i] - m);
   return wave_sum_f64(s);
 }
 
-// Selects the top-k experts of one token (row of E logits) with the calling wave.
-// Writes topk weights/ids for ranks 0..k-1 and calls on_pick(rank, expert) on the
-// lane that owns each rank (rank = p*64 + lane), in increasing rank order per lane.
+// Exact selection for heavy ties (more than 128 keys at the threshold) and k > 64: the
+// maximum (key, ~expert) pair strictly below the previous pick, k times, 64 ranks per
+// pass.  Reads the row again from memory and keeps no per-register state, so that it does
+// not raise the register budget of the common path.  The picked logit is parked in w_out
+// and turned into the weight once the denominator is known.
 template <int NV, class OnPick>
-__device__ void select_token(const float* __restrict__ row, int E, int k, int score, int renorm,
-                             uint64_t* __restrict__ cand, float* __restrict__ w_out,
-                             int32_t* __restrict__ id_out, OnPick on_pick) {
+__device__ void select_token_exact(const float* __restrict__ row, int E, int k,
+                                                bool softmax, int renorm,
+                                                float* __restrict__ w_out,
+                                                int32_t* __restrict__ id_out, OnPick on_pick) {
   const int lane = lane_id();
-  uint32_t keys[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
-    keys[i] = e < E ? logit_key(__builtin_nontemporal_load(row + e)) : 0u;
-  }
-  const bool softmax = score == 0;
-
-  // fast path: threshold from the lane maxima, compaction, one bitonic sort
-  if (k <= 64) {
-    uint32_t lm = 0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) lm = keys[i] > lm ? keys[i] : lm;
-    const uint32_t tau = readlane_u32(bitonic64_desc(lm), k - 1);
-    // compaction of the keys >= tau: a ballot per register gives each lane its slot
-    int c = 0;  // wave-uniform
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const bool p = keys[i] >= tau;
-      const uint64_t mask = __ballot(p);
-      const int pos = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-      if (p && pos < kMaxCand) cand[pos] = pick_key(keys[i], lane + 64 * i);
-      c += __popcll(mask);
-    }
-    if (c <= kMaxCand) {
-      wave_lds_sync();
-      uint64_t v0 = lane < c ? cand[lane] : 0ull;
-      uint64_t v1 = lane + 64 < c ? cand[lane + 64] : 0ull;
-      wave_lds_sync();
-      if (c <= 64) {
-        v0 = bitonic64_desc(v0);
-      } else {
-        bitonic128_desc(v0, v1);
-      }
-      // rank = lane; ranks < k <= 64 all sit in v0
-      const double m = (double)key_logit(pick_logit_key(readlane_u64(v0, 0)));
-      const bool mine = lane < k;
-      const double sc = mine ? score_of((double)key_logit(pick_logit_key(v0)), m, softmax) : 0.0;
-      double denom = 1.0;
-      if (renorm) denom = wave_sum_f64(sc);
-      else if (softmax) denom = full_softmax_denominator<NV>(keys, E, m);
-      if (mine) {
-        const int e = pick_expert(v0);
-        w_out[lane] = (float)(sc / denom);
-        id_out[lane] = e;
-        on_pick(lane, e);
-      }
-      return;
-    }
-    wave_lds_sync();  // the candidate buffer is reused by the next token
-  }
-
-  // exact slow path: extract the maximum k times, 64 ranks per pass.  The picked
-  // logit is parked in w_out and turned into the weight once the denominator is known.
-  double denom_all = 1.0;
-  double m = 0.0;
-  double part = 0.0;
-  bool have_m = false;
+  double m = 0.0, denom_all = 1.0, part = 0.0;
+  uint64_t prev = ~0ull;
   for (int p = 0; p * 64 < k; ++p) {
     uint64_t mine = 0;
     const int nr = min(64, k - p * 64);
     for (int jj = 0; jj < nr; ++jj) {
       uint64_t best = 0;
-#pragma unroll
+#pragma unroll 4
       for (int i = 0; i < NV; ++i) {
-        const uint64_t pk = keys[i] ? pick_key(keys[i], lane + 64 * i) : 0ull;
-        best = pk > best ? pk : best;
+        const int e = lane + 64 * i;
+        if (e < E) {
+          const uint64_t pk = pick_key(logit_key(row[e]), e);
+          if (pk < prev && pk > best) best = pk;
+        }
       }
       best = wave_max_u64(best);
-      const int e = pick_expert(best);
-      if (!have_m) {
+      if (p == 0 && jj == 0) {
         m = (double)key_logit(pick_logit_key(best));
-        have_m = true;
-        if (softmax && !renorm) denom_all = full_softmax_denominator<NV>(keys, E, m);
+        if (softmax && !renorm) {
+          double s = 0.0;
+#pragma unroll 4
+          for (int i = 0; i < NV; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E) s += exp((double)row[e] - m);
+          }
+          denom_all = wave_sum_f64(s);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (lane + 64 * i == e) keys[i] = 0u;
+      prev = best;
       if (lane == jj) mine = best;
     }
     if (lane < nr) {
@@ -156,43 +112,131 @@ __device__ void select_token(const float* __restrict__ row, int E, int k, int sc
     w_out[r] = (float)(score_of((double)w_out[r], m, softmax) / denom);
 }
 
-// ----------------------------------------------------------------------------- single workgroup
-// Dynamic LDS: cand [16][128] u64 | hist [16][E4] u8 | cnt [E4] i32 | off [E4] i32 |
-//              wsum [20] i32 | ids [T*k] i32
-template <int NV>
-__global__ void __launch_bounds__(1024) route_oneshot_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int score, int renorm, int B,
-    float* __restrict__ topk_w, int32_t* __restrict__ topk_ids, int32_t* __restrict__ sorted_ids,
-    int cap, int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_valid) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* s_cand = reinterpret_cast<uint64_t*>(smem);
-  uint8_t* s_hist = smem + 16 * kMaxCand * sizeof(uint64_t);
-  const int E4 = (E + 3) & ~3;
-  int32_t* s_cnt = reinterpret_cast<int32_t*>(s_hist + 16 * E4);
-  int32_t* s_off = s_cnt + E4;
-  int32_t* s_wsum = s_off + E4;
-  int32_t* s_ids = s_wsum + 20;
-
-  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
-  __syncthreads();
-
-  // waves own contiguous token ranges (at most 4 tokens each)
-  const int tw = (T + 15) / 16;
-  const int t0 = w * tw, t1 = min(T, t0 + tw);
-  uint8_t* my_hist = s_hist + w * E4;
-  for (int t = t0; t < t1; ++t) {
-    select_token<NV>(logits + (size_t)t * E, E, k, score, renorm, s_cand + w * kMaxCand,
-                     topk_w + (size_t)t * k, topk_ids + (size_t)t * k, [&](int r, int e) {
-                       s_ids[t * k + r] = e;
-                       if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
-                     });
+// Selects the top-k experts of one token (row of E logits) with the calling wave.
+// Writes topk weights/ids for ranks 0..k-1 and calls on_pick(rank, expert) once per
+// rank, on the lane that owns it.
+template <int NV, class OnPick>
+__device__ void select_token(const float* __restrict__ row, int E, int k, int score, int renorm,
+                             uint64_t* __restrict__ cand, float* __restrict__ w_out,
+                             int32_t* __restrict__ id_out, OnPick on_pick) {
+  const int lane = lane_id();
+  const bool softmax = score == 0;
+  if (k <= 64) {
+    // lane l holds experts l, l+64, ...; empty slots hold NaN, which no comparison selects
+    float x[NV];
+    const float* rl = row + lane;
+    if (E == 64 * NV) {  // every register full (wave-uniform): unpredicated loads
+#pragma unroll
+      for (int i = 0; i < NV; ++i) x[i] = __builtin_nontemporal_load(rl + 64 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        x[i] = lane + 64 * i < E ? __builtin_nontemporal_load(rl + 64 * i) : __builtin_nanf("");
+    }
+    float lm = x[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) lm = fmaxf(lm, x[i]);
+    // threshold: k-th largest of the G group maxima (as order-preserving keys, 0 = empty)
+    uint32_t lk = lm == lm ? logit_key(lm) : 0u;
+    int G = 2;
+    while (G < 2 * k && G < 64) G <<= 1;
+    const int L = 64 / G;
+#pragma unroll
+    for (int mm = 1; mm < 64; mm <<= 1)
+      if (mm < L) {
+        const uint32_t o = shfl_xor_u32(lk, mm);
+        lk = o > lk ? o : lk;
+      }
+    const uint32_t srt = bitonic64_desc_grouped(lk, L);
+    const uint32_t top = readlane_u32(srt, 0);  // the token's largest key
+    const uint32_t tk = readlane_u32(srt, (k - 1) * L);
+    const float tau = tk == 0u ? -__builtin_inff() : key_logit(tk);
+    // compaction of the logits >= tau: a ballot per register gives each lane its slot
+    int c = 0;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool p = x[i] >= tau;
+      const uint64_t mask = __ballot(p);
+      if (mask) {
+        const int pos = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (p && pos < kMaxCand) cand[pos] = pick_key(logit_key(x[i]), lane + 64 * i);
+        c += __popcll(mask);
+      }
+    }
+    if (c <= kMaxCand) {
+      wave_lds_sync();
+      const uint64_t v0 = lane < c ? cand[lane] : 0ull;
+      const uint64_t v1 = lane + 64 < c ? cand[lane + 64] : 0ull;
+      // rank = number of larger candidates (broadcast reads); pick keys are distinct
+      int r0 = 0, r1 = 0;
+      if (c <= 64) {
+        for (int i = 0; i < c; ++i) r0 += cand[i] > v0;
+      } else {
+        for (int i = 0; i < c; ++i) {
+          const uint64_t o = cand[i];
+          r0 += o > v0;
+          r1 += o > v1;
+        }
+      }
+      wave_lds_sync();  // the candidate buffer is reused by the next token
+      const bool in0 = lane < c && r0 < k, in1 = lane + 64 < c && r1 < k;
+      const double m = (double)key_logit(top);
+      const double sc0 = in0 ? score_of((double)key_logit(pick_logit_key(v0)), m, softmax) : 0.0;
+      const double sc1 = in1 ? score_of((double)key_logit(pick_logit_key(v1)), m, softmax) : 0.0;
+      double denom = 1.0;
+      if (renorm) denom = wave_sum_f64(sc0 + sc1);
+      else if (softmax) denom = full_softmax_denominator<NV>(x, m);
+      if (in0) {
+        const int e = pick_expert(v0);
+        w_out[r0] = (float)(sc0 / denom);
+        id_out[r0] = e;
+        on_pick(r0, e);
+      }
+      if (in1) {
+        const int e = pick_expert(v1);
+        w_out[r1] = (float)(sc1 / denom);
+        id_out[r1] = e;
+        on_pick(r1, e);
+      }
+      return;
+    }
     wave_lds_sync();
   }
-  __syncthreads();
+  select_token_exact<NV>(row, E, k, softmax, renorm, w_out, id_out, on_pick);
+}
 
-  // per-expert: exclusive prefix over waves (in place), count, padded count
-  const int per = (E + 1023) / 1024;  // <= 1 expert per thread for E <= 1024
+// Sentinel fill of sorted_ids [cap) and -1 fill of expert_ids [cap/B): share `part` of
+// `nparts`, written with nthreads threads (int4 stores; cap is a multiple of B >= 16).
+// Real slots and block experts are written over it later.
+__device__ __forceinline__ void prefill_share(int32_t* __restrict__ sorted_ids, int cap,
+                                              int32_t* __restrict__ expert_ids, int B, int sentinel,
+                                              int part, int nparts, int tid, int nthreads) {
+  const int n4 = cap / 4, per = (n4 + nparts - 1) / nparts;
+  const int a = part * per, b = min(n4, a + per);
+  const int4 s4 = make_int4(sentinel, sentinel, sentinel, sentinel);
+  for (int i = a + tid; i < b; i += nthreads) reinterpret_cast<int4*>(sorted_ids)[i] = s4;
+  const int nb = cap / B, pe = (nb + nparts - 1) / nparts;
+  const int ea = part * pe, eb = min(nb, ea + pe);
+  for (int i = ea + tid; i < eb; i += nthreads) expert_ids[i] = -1;
+}
+
+// Block experts of expert e: o = its padded offset, c = its count (> 0).
+__device__ __forceinline__ void write_block_experts(int e, int o, int c, int B,
+                                                    int32_t* __restrict__ expert_ids) {
+  const int p = (c + B - 1) / B * B;
+  for (int b = o / B; b < (o + p) / B; ++b) expert_ids[b] = e;
+}
+
+// Shared by the single-workgroup sorts (16 waves), once wave w has counted its tokens'
+// picks into hist[w][e] (bytes): in place, hist[w][e] becomes the exclusive prefix over
+// waves; cnt[e] = the expert's count; off[e] = its padded exclusive offset.  Returns the
+// padded total (num_valid); ends with a barrier.
+__device__ int block_prefix_scan(uint8_t* s_hist, int32_t* s_cnt, int32_t* s_off,
+                                 int32_t* s_wsum, int E, int B) {
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const int E4 = (E + 3) & ~3;
+  const int per = (E + 1023) / 1024;
   const int e0 = tid * per;
   int local = 0;
   for (int q = 0; q < per; ++q) {
@@ -208,7 +252,6 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
       local += (c + B - 1) / B * B;
     }
   }
-  // block exclusive scan of the padded counts
   const int incl = wave_incl_scan_i32(local);
   if (lane == 63) s_wsum[w] = incl;
   __syncthreads();
@@ -229,9 +272,50 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
     }
   }
   __syncthreads();
+  return nv;
+}
+
+// ----------------------------------------------------------------------------- single workgroup
+// Dynamic LDS: cand [16][128] u64 | hist [16][E4] u8 | cnt [E4] i32 | off [E4] i32 |
+//              wsum [20] i32 | ids [T*k] i32
+template <int NV>
+__global__ void __launch_bounds__(1024) route_oneshot_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int score, int renorm, int B,
+    float* __restrict__ topk_w, int32_t* __restrict__ topk_ids, int32_t* __restrict__ sorted_ids,
+    int cap, int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_valid) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* s_cand = reinterpret_cast<uint64_t*>(smem);
+  uint8_t* s_hist = smem + 16 * kMaxCand * sizeof(uint64_t);
+  const int E4 = (E + 3) & ~3;
+  int32_t* s_cnt = reinterpret_cast<int32_t*>(s_hist + 16 * E4);
+  int32_t* s_off = s_cnt + E4;
+  int32_t* s_wsum = s_off + E4;
+  int32_t* s_ids = s_wsum + 20;
+
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const int sentinel = T * k;
+  prefill_share(sorted_ids, cap, expert_ids, B, sentinel, 0, 1, tid, 1024);
+  for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
+  __syncthreads();
+
+  // waves own contiguous token ranges (at most 4 tokens each)
+  const int tw = (T + 15) / 16;
+  const int t0 = w * tw, t1 = min(T, t0 + tw);
+  uint8_t* my_hist = s_hist + w * E4;
+  for (int t = t0; t < t1; ++t) {
+    select_token<NV>(logits + (size_t)t * E, E, k, score, renorm, s_cand + w * kMaxCand,
+                     topk_w + (size_t)t * k, topk_ids + (size_t)t * k, [&](int r, int e) {
+                       s_ids[t * k + r] = e;
+                       if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
+                     });
+    wave_lds_sync();
+  }
+  __threadfence();  // the fill stores complete before any slot is written over them
+  __syncthreads();
+
+  const int nv = block_prefix_scan(s_hist, s_cnt, s_off, s_wsum, E, B);
 
   // scatter: each wave walks its tokens in order (a token's k experts are distinct)
-  const int sentinel = T * k;
   for (int t = t0; t < t1; ++t) {
     for (int j = lane; j < k; j += 64) {
       const int e = s_ids[t * k + j];
@@ -242,36 +326,93 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
     }
     wave_lds_sync();
   }
-  // padding rows, block experts, tail
-  for (int e = tid; e < E; e += 1024) {
-    const int c = s_cnt[e];
-    if (c == 0) continue;
-    const int o = s_off[e], p = (c + B - 1) / B * B;
-    for (int q = c; q < p; ++q) sorted_ids[o + q] = sentinel;
-    for (int b = o / B; b < (o + p) / B; ++b) expert_ids[b] = e;
-  }
-  for (int i = nv + tid; i < cap; i += 1024) sorted_ids[i] = sentinel;
-  for (int b = nv / B + tid; b < cap / B; b += 1024) expert_ids[b] = -1;
+  for (int e = tid; e < E; e += 1024)
+    if (s_cnt[e] > 0) write_block_experts(e, s_off[e], s_cnt[e], B, expert_ids);
   if (tid == 0) *num_valid = nv;
 }
 
 // ----------------------------------------------------------------------------- multi workgroup
+// One token per wave; each workgroup also writes one share of the sentinel / -1 fill of
+// sorted_ids and expert_ids.
 template <int NV>
 __global__ void __launch_bounds__(256) route_select_kernel(const float* __restrict__ logits,
                                                            int T, int E, int k, int score,
-                                                           int renorm, float* __restrict__ topk_w,
-                                                           int32_t* __restrict__ topk_ids) {
+                                                           int renorm, int B, int cap,
+                                                           float* __restrict__ topk_w,
+                                                           int32_t* __restrict__ topk_ids,
+                                                           int32_t* __restrict__ sorted_ids,
+                                                           int32_t* __restrict__ expert_ids) {
   __shared__ uint64_t s_cand[4][kMaxCand];
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
+  prefill_share(sorted_ids, cap, expert_ids, B, T * k, blockIdx.x, gridDim.x, threadIdx.x, 256);
   if (t >= T) return;
   select_token<NV>(logits + (size_t)t * E, E, k, score, renorm, s_cand[w],
                    topk_w + (size_t)t * k, topk_ids + (size_t)t * k, [](int, int) {});
 }
 
-// cnt[chunk][e] = picks of expert e among the chunk's tokens
+// Single-workgroup sort after the select kernel (T <= kSort1MaxT, E <= kSort1MaxE): 16
+// waves own contiguous token ranges of at most 8 tokens, whose ids are loaded once into
+// registers (one per token and lane for k <= 64); byte histograms per wave, the shared
+// prefix and padded scan, then ordered placement and block experts.  Padding and tail hold
+// the select kernel's fill.
+// Dynamic LDS: hist [16][E4] u8 | cnt [E4] i32 | off [E4] i32 | wsum [20] i32
+__global__ void __launch_bounds__(1024) route_sort1_kernel(const int32_t* __restrict__ topk_ids,
+                                                           int T, int E, int k, int B,
+                                                           int32_t* __restrict__ sorted_ids,
+                                                           int32_t* __restrict__ expert_ids,
+                                                           int32_t* __restrict__ num_valid) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int E4 = (E + 3) & ~3;
+  uint8_t* s_hist = smem;
+  int32_t* s_cnt = reinterpret_cast<int32_t*>(s_hist + 16 * E4);
+  int32_t* s_off = s_cnt + E4;
+  int32_t* s_wsum = s_off + E4;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
+  constexpr int TW = kSort1MaxT / 16;
+  const int tw = (T + 15) / 16;
+  const int t0 = w * tw, t1 = min(T, t0 + tw);
+  int ids[TW];
+#pragma unroll
+  for (int q = 0; q < TW; ++q)
+    ids[q] = (t0 + q < t1 && lane < k) ? topk_ids[(size_t)(t0 + q) * k + lane] : -1;
+  __syncthreads();
+  uint8_t* my_hist = s_hist + w * E4;
+#pragma unroll
+  for (int q = 0; q < TW; ++q) {
+    const int t = t0 + q;
+    if (t >= t1) break;
+    for (int j = lane; j < k; j += 64) {
+      const int e = j < 64 ? ids[q] : topk_ids[(size_t)t * k + j];
+      if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
+    }
+    wave_lds_sync();
+  }
+  __syncthreads();
+  const int nv = block_prefix_scan(s_hist, s_cnt, s_off, s_wsum, E, B);
+#pragma unroll
+  for (int q = 0; q < TW; ++q) {
+    const int t = t0 + q;
+    if (t >= t1) break;
+    for (int j = lane; j < k; j += 64) {
+      const int e = j < 64 ? ids[q] : topk_ids[(size_t)t * k + j];
+      if ((unsigned)e >= (unsigned)E) continue;
+      const int r = my_hist[e];
+      my_hist[e] = (uint8_t)(r + 1);
+      sorted_ids[s_off[e] + r] = t * k + j;
+    }
+    wave_lds_sync();
+  }
+  for (int e = tid; e < E; e += 1024)
+    if (s_cnt[e] > 0) write_block_experts(e, s_off[e], s_cnt[e], B, expert_ids);
+  if (tid == 0) *num_valid = nv;
+}
+
+// Multi-workgroup sort.  cnt is expert-major: cnt[e * nch + chunk] = picks of expert e
+// among the chunk's tokens.
 __global__ void __launch_bounds__(1024) route_count_kernel(const int32_t* __restrict__ topk_ids,
-                                                           int T, int E, int k,
+                                                           int T, int E, int k, int nch,
                                                            int32_t* __restrict__ cnt) {
   extern __shared__ __align__(16) unsigned char smem[];
   int32_t* h = reinterpret_cast<int32_t*>(smem);
@@ -285,84 +426,82 @@ __global__ void __launch_bounds__(1024) route_count_kernel(const int32_t* __rest
     if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) cnt[(size_t)chunk * E + e] = h[e];
+  for (int e = tid; e < E; e += 1024) cnt[(size_t)e * nch + chunk] = h[e];
 }
 
-// exclusive prefix over chunks per expert (in place), and the total per expert
-__global__ void __launch_bounds__(256) route_colscan_kernel(int32_t* __restrict__ cnt,
-                                                            int nchunks, int E,
-                                                            int32_t* __restrict__ tot) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
-  int c = 0;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int v = cnt[(size_t)ch * E + e];
-    cnt[(size_t)ch * E + e] = c;
-    c += v;
-  }
-  tot[e] = c;
-}
-
-// padded exclusive scan over experts; expert_ids, padding, tail, num_valid
-__global__ void __launch_bounds__(1024) route_scan_kernel(const int32_t* __restrict__ tot, int E,
-                                                          int B, int sentinel, int cap,
-                                                          int32_t* __restrict__ off,
-                                                          int32_t* __restrict__ sorted_ids,
-                                                          int32_t* __restrict__ expert_ids,
-                                                          int32_t* __restrict__ num_valid) {
-  __shared__ int s_wsum[17];
-  __shared__ int s_nv;
+// 64 experts per workgroup, 4 per wave: each expert's exclusive prefix over the chunks (in
+// place; 64 chunks per coalesced load and wave scan), its total, and the padded exclusive
+// scan over the workgroup's 64 experts; gsum[group] = the group's padded total.
+__global__ void __launch_bounds__(1024) route_colscan_kernel(int32_t* __restrict__ cnt, int nch,
+                                                             int E, int B,
+                                                             int32_t* __restrict__ tot,
+                                                             int32_t* __restrict__ loff,
+                                                             int32_t* __restrict__ gsum) {
+  __shared__ int s_c[64];
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  const int per = (E + 1023) / 1024;
-  const int e0 = tid * per;
-  int local = 0;
-  for (int q = 0; q < per; ++q)
-    if (e0 + q < E) local += (tot[e0 + q] + B - 1) / B * B;
-  const int incl = wave_incl_scan_i32(local);
-  if (lane == 63) s_wsum[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    const int x = lane < 16 ? s_wsum[lane] : 0;
-    const int xi = wave_incl_scan_i32(x);
-    if (lane < 16) s_wsum[lane] = xi - x;
-    if (lane == 15) s_nv = xi;
-  }
-  __syncthreads();
-  int run = s_wsum[w] + incl - local;
-  for (int q = 0; q < per; ++q) {
-    const int e = e0 + q;
-    if (e < E) {
-      const int c = tot[e], p = (c + B - 1) / B * B;
-      off[e] = run;
-      for (int r = c; r < p; ++r) sorted_ids[run + r] = sentinel;
-      for (int b = run / B; b < (run + p) / B; ++b) expert_ids[b] = e;
-      run += p;
+  const int eb = blockIdx.x * 64 + w * 4;
+  int c[4] = {0, 0, 0, 0};
+  for (int ch = 0; ch < nch; ch += 64) {
+    const int i = ch + lane;
+    int v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (eb + q < E && i < nch) ? cnt[(size_t)(eb + q) * nch + i] : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int incl = wave_incl_scan_i32(v[q]);
+      if (eb + q < E && i < nch) cnt[(size_t)(eb + q) * nch + i] = c[q] + incl - v[q];
+      c[q] += (int)readlane_u32((uint32_t)incl, 63);
     }
   }
-  const int nv = s_nv;
-  for (int i = nv + tid; i < cap; i += 1024) sorted_ids[i] = sentinel;
-  for (int b = nv / B + tid; b < cap / B; b += 1024) expert_ids[b] = -1;
-  if (tid == 0) *num_valid = nv;
+  if (lane < 4) s_c[w * 4 + lane] = lane == 0 ? c[0] : lane == 1 ? c[1] : lane == 2 ? c[2] : c[3];
+  __syncthreads();
+  if (w == 0) {
+    const int e = blockIdx.x * 64 + lane;
+    const int cc = s_c[lane];
+    const int p = (cc + B - 1) / B * B;
+    const int incl = wave_incl_scan_i32(p);
+    if (e < E) {
+      tot[e] = cc;
+      loff[e] = incl - p;
+    }
+    if (lane == 63) gsum[blockIdx.x] = incl;
+  }
 }
 
-// per chunk: 16 waves x 4 tokens; byte histograms per wave, then ordered placement.  The
-// ids of a wave's tokens are loaded once (k <= 64: one register per token and lane).
-__global__ void __launch_bounds__(1024) route_scatter_kernel(const int32_t* __restrict__ topk_ids,
-                                                             int T, int E, int k,
-                                                             const int32_t* __restrict__ cnt,
-                                                             const int32_t* __restrict__ off,
-                                                             int32_t* __restrict__ sorted_ids) {
+// Per chunk: 16 waves x 4 tokens; byte histograms per wave, then ordered placement.  The
+// ids of a wave's tokens and their experts' bases are loaded once, before the histogram
+// (k <= 64: one register per token and lane).  The workgroups also write the block experts
+// of experts chunk, chunk + nch, ...; padding and tail hold the select kernel's fill.
+__global__ void __launch_bounds__(1024) route_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int E, int k, int B, int nch,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ tot,
+    const int32_t* __restrict__ loff, const int32_t* __restrict__ gsum,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ num_valid) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_goff[129];  // E <= 8160: at most 128 groups of 64 experts, then the total
   const int E4 = (E + 3) & ~3;
   uint8_t* s_hist = smem;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, chunk = blockIdx.x;
+  const int ngroups = (E + 63) / 64;
   for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
+  if (w == 0) {
+    const int g0 = 2 * lane, g1 = 2 * lane + 1;
+    const int x0 = g0 < ngroups ? gsum[g0] : 0, x1 = g1 < ngroups ? gsum[g1] : 0;
+    const int xi = wave_incl_scan_i32(x0 + x1);
+    if (g0 < ngroups) s_goff[g0] = xi - x0 - x1;
+    if (g1 < ngroups) s_goff[g1] = xi - x1;
+    if (lane == 63) s_goff[128] = xi;
+  }
   constexpr int TPW = kChunkTokens / 16;
   const int t0 = chunk * kChunkTokens + w * TPW, t1 = min(T, t0 + TPW);
-  int ids[TPW];
+  int ids[TPW], base[TPW];
 #pragma unroll
   for (int q = 0; q < TPW; ++q)
     ids[q] = (t0 + q < t1 && lane < k) ? topk_ids[(size_t)(t0 + q) * k + lane] : -1;
+#pragma unroll
+  for (int q = 0; q < TPW; ++q)
+    base[q] = (unsigned)ids[q] < (unsigned)E ? loff[ids[q]] + cnt[(size_t)ids[q] * nch + chunk] : 0;
   __syncthreads();
   uint8_t* my_hist = s_hist + w * E4;
 #pragma unroll
@@ -385,7 +524,6 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(const int32_t* __re
     }
   }
   __syncthreads();
-  const int32_t* base = cnt + (size_t)chunk * E;
 #pragma unroll
   for (int q = 0; q < TPW; ++q) {
     const int t = t0 + q;
@@ -393,12 +531,19 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(const int32_t* __re
     for (int j = lane; j < k; j += 64) {
       const int e = j < 64 ? ids[q] : topk_ids[(size_t)t * k + j];
       if ((unsigned)e >= (unsigned)E) continue;
+      const int bj = j < 64 ? base[q] : loff[e] + cnt[(size_t)e * nch + chunk];
       const int r = my_hist[e];
       my_hist[e] = (uint8_t)(r + 1);
-      sorted_ids[off[e] + base[e] + r] = t * k + j;
+      sorted_ids[s_goff[e >> 6] + bj + r] = t * k + j;
     }
     wave_lds_sync();
   }
+  for (int e = chunk + nch * tid; e < E; e += nch * 1024) {
+    const int c = tot[e];
+    if (c > 0) write_block_experts(e, s_goff[e >> 6] + loff[e], c, B, expert_ids);
+  }
+  const int nv = s_goff[128];
+  if (chunk == 0 && tid == 0) *num_valid = nv;
 }
 
 __global__ void write_zero_i32(int32_t* p) { *p = 0; }
@@ -414,13 +559,16 @@ bool route_is_oneshot(int T, int E, int k) {
   return T <= kOneShotMaxT && E <= kOneShotMaxE && T * k <= kOneShotMaxSlots;
 }
 
+bool route_is_twostage(int T, int E, int k) {
+  return !route_is_oneshot(T, E, k) && T <= kSort1MaxT && E <= kSort1MaxE;
+}
+
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t route_workspace_bytes(int T, int E, int k) {
-  (void)k;
-  if (T == 0 || route_is_oneshot(T, E, k)) return 0;
+  if (T == 0 || route_is_oneshot(T, E, k) || route_is_twostage(T, E, k)) return 0;
   const int64_t nchunks = (T + kChunkTokens - 1) / kChunkTokens;
-  return align256(nchunks * E * 4) + align256((int64_t)E * 4) * 2;
+  return align256(nchunks * E * 4) + align256((int64_t)E * 4) * 2 + align256(128 * 4);
 }
 
 template <int NV>
@@ -440,14 +588,23 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
       return hipGetLastError();
     }
   }
-  const int nchunks = (T + kChunkTokens - 1) / kChunkTokens;
-  int32_t* cnt = reinterpret_cast<int32_t*>(ws);
-  int32_t* tot = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + align256((int64_t)nchunks * E * 4));
-  int32_t* off = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tot) + align256((int64_t)E * 4));
-  route_select_kernel<NV><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, score, renorm, topk_w, topk_ids);
-  route_count_kernel<<<nchunks, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, cnt);
-  route_colscan_kernel<<<(E + 255) / 256, 256, 0, st>>>(cnt, nchunks, E, tot);
-  route_scan_kernel<<<1, 1024, 0, st>>>(tot, E, B, T * k, (int)cap, off, sorted_ids, expert_ids, num_valid);
+  if (route_is_twostage(T, E, k)) {
+    route_select_kernel<NV><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, score, renorm, B, (int)cap,
+                                                          topk_w, topk_ids, sorted_ids, expert_ids);
+    const size_t lds = 24 * (size_t)E4 + 20 * 4;  // <= 61.5 KB for E <= 2560
+    route_sort1_kernel<<<1, 1024, lds, st>>>(topk_ids, T, E, k, B, sorted_ids, expert_ids, num_valid);
+    return hipGetLastError();
+  }
+  const int nch = (T + kChunkTokens - 1) / kChunkTokens;
+  char* wsb = reinterpret_cast<char*>(ws);
+  int32_t* cnt = reinterpret_cast<int32_t*>(wsb);
+  int32_t* tot = reinterpret_cast<int32_t*>(wsb + align256((int64_t)nch * E * 4));
+  int32_t* loff = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tot) + align256((int64_t)E * 4));
+  int32_t* gsum = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(loff) + align256((int64_t)E * 4));
+  route_select_kernel<NV><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, score, renorm, B, (int)cap, topk_w,
+                                                      topk_ids, sorted_ids, expert_ids);
+  route_count_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt);
+  route_colscan_kernel<<<(E + 63) / 64, 1024, 0, st>>>(cnt, nch, E, B, tot, loff, gsum);
   const size_t lds = 16 * (size_t)E4;
   if (lds > 64 * 1024) {
     // byte histograms of 16 waves for E > 4096 need more than the default 64 KB of LDS
@@ -455,7 +612,8 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
-  route_scatter_kernel<<<nchunks, 1024, lds, st>>>(topk_ids, T, E, k, cnt, off, sorted_ids);
+  route_scatter_kernel<<<nch, 1024, lds, st>>>(topk_ids, T, E, k, B, nch, cnt, tot, loff,
+                                               gsum, sorted_ids, expert_ids, num_valid);
   return hipGetLastError();
 }
 

@@ -89,7 +89,7 @@ def crafted(kind, T, E, seed):
 
 @pytest.mark.parametrize("kind", ["ties3", "equal", "signed_zero", "dup", "wide"])
 @pytest.mark.parametrize("T,E,k,B", [(5, 8, 3, 16), (7, 63, 5, 16), (3, 65, 64, 32), (9, 300, 70, 64),
-                                     (300, 256, 8, 16), (257, 1537, 36, 32)])
+                                     (128, 256, 8, 16), (300, 256, 8, 16), (257, 1537, 36, 32)])
 def test_route_crafted_ties(kind, T, E, k, B):
     # heavy ties push the selection onto its exact slow path; index order must still decide
     logits = crafted(kind, T, E, seed=T * E)
@@ -100,7 +100,10 @@ def test_route_crafted_ties(kind, T, E, k, B):
 
 @pytest.mark.parametrize("T,E,k,B", [(1, 1, 1, 16), (3, 4, 4, 16), (2, 8160, 8, 64), (70, 8160, 3, 32),
                                      (65, 8, 8, 64), (1, 1536, 1, 16), (64, 1536, 64, 16),
-                                     (65, 1536, 2, 16), (1000, 8, 1, 32), (64, 1024, 8, 16), (64, 1025, 8, 16)])
+                                     (65, 1536, 2, 16), (1000, 8, 1, 32), (64, 1024, 8, 16), (64, 1025, 8, 16),
+                                     (16, 1024, 8, 16), (17, 1024, 8, 16), (16, 1025, 8, 16),
+                                     (16, 256, 64, 16), (17, 8160, 1, 64), (128, 2560, 8, 16),
+                                     (129, 2560, 8, 16), (128, 2561, 4, 16), (100, 64, 64, 64)])
 def test_route_edges(T, E, k, B):
     logits = synth.logits(T, E, seed=11)
     got = run_route(logits.cuda(), k, B)
