@@ -49,8 +49,37 @@ __device__ __forceinline__ bool block_tile(int mbs, int nts, int& mb, int& nt) {
   mb = v - nt * mbs;
   return true;
 }
+// The same with the (row-block-major, tile-minor) order: all weight tiles of a row block, and
+// the row blocks of one expert, run next to each other on one XCD, which then fetches the
+// gathered rows once for all weight tiles and each weight tile once for the expert's blocks.
+__device__ __forceinline__ bool block_tile_rows(int mbs, int nts, int& mb, int& nt) {
+  const int n = mbs * nts;
+  const int per = (n + 7) >> 3;
+  const int L = (int)blockIdx.x;
+  const int v = (L & 7) * per + (L >> 3);
+  if (v >= n) return false;
+  mb = v / nts;
+  nt = v - mb * nts;
+  return true;
+}
 static inline unsigned xcd_grid(int64_t mbs, int64_t nts) {
   return (unsigned)(((mbs * nts + 7) / 8) * 8);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane (lds is the
+// wave-uniform LDS byte address, in M0).  Written as assembly so that the compiler, which
+// does not see these loads, keeps its own waits on the register loads around them (loads
+// it does not count only make its counts conservative) and inserts no blanket wait before
+// LDS reads; the code that uses the staged bytes waits for them explicitly.
+// The same with a wave-uniform 64-bit base and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16_to_lds_s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma16_to_lds(const void* g, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory");
 }
 
 template <bool FP8>
@@ -377,161 +406,150 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
 //    4 slots and 16 lanes cover 16 consecutive channels of one slot: each atomic (or
 //    store) instruction writes 64 contiguous bytes per row.
 enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2 };
-constexpr int kPfRows = 64;
-constexpr int kPfStage = 512;
+constexpr int kPfRows = 64;                          // rows of one sorted block
+constexpr int kPfMaxBlocks = 4;                      // sorted blocks per tile
+constexpr int kPfMaxRows = kPfRows * kPfMaxBlocks;   // 256
 
-template <bool FP8, int MODE>
-__global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(
-    const uint8_t* __restrict__ act, const float* __restrict__ act_scale,
-    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
-    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
-    int k, int N, int K, int mbs, void* __restrict__ out, float4* __restrict__ zero_y,
-    int64_t zero_n4) {
+struct PfArgs {
+  const uint8_t* act;
+  const float* act_scale;
+  const uint8_t* w;
+  const float* w_scale;
+  const float* topk_w;
+  int T, k, N, K, e, nt;
+  void* out;
+};
+
+// One tile of NB sorted blocks (64 NB slot rows) x the block's 256 weight rows, 8 waves.
+// Wave w computes weight rows 64 (w % 4) .. + 63 against the slot-row groups tt with
+// tt % 2 == w / 4.  Both operands are staged by direct-to-LDS loads, one 128-byte K chunk
+// at a time, double buffered.  A load instruction fills 1 KB = 8 rows x 128 B; lane l takes
+// row l/8 and physical segment l%8, which holds logical segment (l%8) ^ ((row/2) % 8): every
+// 8 consecutive lanes read one full 128-byte line, and the 16 rows that an MFMA operand
+// reads (one 16-byte segment each) land in 16 different bank groups.  The per-lane parts of
+// the load addresses are fixed; each chunk only advances the wave-uniform bases.
+template <bool FP8, int MODE, int NB>
+__device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restrict__ s_slot,
+                                             uint8_t (*tok)[kPfMaxRows * 128],
+                                             uint8_t (*wgt)[256 * 128]) {
   constexpr bool G1 = MODE == PF_G1;
   constexpr int EB = FP8 ? 1 : 2;
-  __shared__ __align__(16) uint8_t tok[2][kPfRows * kPfStage];
-  __shared__ int s_slot[kPfRows];
-  if (zero_y)
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 256)
-      zero_y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  // gemm1: N = I channels, a tile = 128 channels (256 weight rows); gemm2: N = D rows, tile = 256
-  const int tile_n = G1 ? 128 : 256;
-  int mb, nt;
-  if (!block_tile(mbs, (N + tile_n - 1) / tile_n, mb, nt)) return;
-  if (mb * kPfRows >= *num_valid) return;
-  const int e = expert_ids[mb];
-  if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  constexpr int MH = 2 * NB;  // slot-row groups per wave
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wr = wave & 3, th = wave >> 2;
   const int i16 = lane & 15, g = lane >> 4;
-  const int n_slots = T * k;
-  const int rowb = K * EB;
-  if (tid < kPfRows) s_slot[tid] = sorted_ids[mb * kPfRows + tid];
+  const int n_slots = p.T * p.k;
+  const int rowb = p.K * EB;
+  const int N = p.N;
+  const int pseg = lane & 7, rsub = lane >> 3;
+  // ((8 j + rsub) / 2) % 8 = (4 (j % 2) + rsub / 2) % 8; every instruction of this wave has
+  // j % 2 == wave % 2
+  const int ls = pseg ^ ((4 * (wave & 1) + (rsub >> 1)) & 7);
 
-  __syncthreads();  // s_slot
-  // staging: store instruction i moves 16-byte segment (tid & 31) of row i*8 + tid/32, so
-  // 32 lanes read 512 contiguous bytes of one row and 16 lanes write 16 different banks
-  const i32x4_t zero = {0, 0, 0, 0};
-  const int sseg = tid & 31;
-  // Every load below is unconditional (addresses are clamped to valid memory), so the
-  // compiler emits straight-line code and counts outstanding loads exactly; the zero
-  // fill of padding rows and of K past the row end is applied when the rows go to LDS.
-  const uint8_t* src[8];
-  uint32_t row_ok = 0;  // bit i: staging row i holds a real slot
+  // slot rows: instruction jj = wave + 8 v covers tile rows 8 jj .. 8 jj + 7
+  uint32_t toff[NB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int s = s_slot[i * 8 + (tid >> 5)];
-    const bool ok = (unsigned)s < (unsigned)n_slots;
-    row_ok |= (ok ? 1u : 0u) << i;
-    src[i] = act + (size_t)(ok ? (G1 ? s / k : s) : 0) * rowb;
+  for (int v = 0; v < NB; ++v) {
+    const int s = s_slot[8 * (wave + 8 * v) + rsub];
+    const bool ok = (unsigned)s < (unsigned)n_slots;  // padding slots read row 0 (dropped)
+    toff[v] = (uint32_t)((ok ? (G1 ? s / p.k : s) : 0) * rowb);
   }
-  i32x4_t stg[8];
-  int stg_off = 0;
-  auto load_stage = [&](int st) {
-    stg_off = st * kPfStage + 16 * sseg;
-    const int off = stg_off < rowb ? stg_off : 0;
+  // weight rows: instruction jw = wave + 8 u covers block rows 8 jw .. 8 jw + 7, i.e. group
+  // q = (br / 16) % 4 of wave group br / 64.  Rows past N read row 0 (results not stored).
+  const uint8_t* wexp = G1 ? p.w + (size_t)p.e * 2 * N * rowb : p.w + (size_t)p.e * N * rowb;
+  uint32_t woff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) stg[i] = ld16(src[i] + off);
-  };
-  auto store_stage = [&](int buf) {
-    const bool in_k = stg_off < rowb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = i * 8 + (tid >> 5);
-      const bool keep = in_k && ((row_ok >> i) & 1u);
-      *reinterpret_cast<i32x4_t*>(&tok[buf][r * kPfStage + 16 * (sseg ^ (r & 15))]) = keep ? stg[i] : zero;
+  for (int u = 0; u < 4; ++u) {
+    const int br = 8 * (wave + 8 * u) + rsub, wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
+    int row, ch;
+    if constexpr (G1) {
+      ch = p.nt * 128 + 32 * wg + 16 * (q & 1) + i;
+      row = (q >= 2 ? N : 0) + ch;
+    } else {
+      ch = p.nt * 256 + br;
+      row = ch;
     }
-  };
-
-  // this wave's weight rows
-  int row0;       // gemm1: first gate channel of the wave; gemm2: first model_dim row
-  bool on;
-  const uint8_t* wrow[4];
-  if constexpr (G1) {
-    row0 = nt * 128 + wave * 32;
-    on = row0 < N;
-    const size_t eb = (size_t)e * 2 * N;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      wrow[q] = w + (eb + (q >= 2 ? N : 0) + (on ? row0 : 0) + 16 * (q & 1) + i16) * (size_t)rowb;
-  } else {
-    row0 = nt * 256 + wave * 64;
-    on = row0 < N;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      wrow[q] = w + ((size_t)e * N + (on ? row0 : 0) + 16 * q + i16) * (size_t)rowb;
+    woff[u] = (uint32_t)((ch < N ? row : 0) * rowb);
   }
+  const int row0 = G1 ? p.nt * 128 + wr * 32 : p.nt * 256 + wr * 64;
+  const bool on = row0 < N;
   const int nch = (rowb + 127) >> 7;
-  const int nst = (rowb + kPfStage - 1) / kPfStage;
-  i32x4_t wb[2][4][2];
-  // chunks past the row end are loaded from chunk 0 (never used: their MFMAs are skipped);
-  // the second half of a half last chunk multiplies rows that LDS holds as zeros
-  auto load_w = [&](int gc, int slot) {
-    const int cc = gc < nch ? gc : 0;
-    const int off0 = cc * 128 + 16 * g;
-    const int off1 = cc * 128 + 64 < rowb ? off0 + 64 : off0;
+  const uint32_t tok_lds = (uint32_t)(uintptr_t)&tok[0][0], wgt_lds = (uint32_t)(uintptr_t)&wgt[0][0];
+  // chunk c's loads into buffer c % 2.  In a half last chunk (fp8, K % 128 == 64) the lanes
+  // of the missing half read the present half again; their weight operand bytes are zeroed.
+  auto issue = [&](int c) {
+    const int b = c & 1;
+    const uint32_t lo = (c * 128 + 64 >= rowb && ls >= 4) ? 16u * (ls & 3) : 16u * ls;
+    const uint8_t* tb = p.act + (size_t)c * 128;
+    const uint8_t* wb = wexp + (size_t)c * 128;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      wb[slot][q][0] = ld16(wrow[q] + off0);
-      wb[slot][q][1] = ld16(wrow[q] + off1);
-    }
+    for (int v = 0; v < NB; ++v)
+      dma16_to_lds_s(tb, toff[v] + lo, tok_lds + b * (kPfMaxRows * 128) + (wave + 8 * v) * 1024);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dma16_to_lds_s(wb, woff[u] + lo, wgt_lds + b * (256 * 128) + (wave + 8 * u) * 1024);
   };
-  f32x4_t acc[4][4];
+
+  f32x4_t acc[4][MH];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MH; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0);
-  store_stage(0);
-  load_w(0, 0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) load_stage(st + 1);
-    const uint8_t* tb = tok[st & 1];
+  const int fsw = (i16 >> 1) & 7;  // read-side swizzle of row i16 of any 16-row group
+  issue(0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) issue(c + 1);
+    const uint8_t* tb = tok[c & 1];
+    const uint8_t* wbuf = wgt[c & 1] + (64 * wr) * 128;
+    i32x4_t wf[4][2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int gc = st * 4 + c;
-      load_w(gc + 1, (c + 1) & 1);
-      if (on && gc < nch) {
-        i32x4_t tf[4][2];
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int r = tt * 16 + i16;
+      for (int h = 0; h < 2; ++h)
+        wf[q][h] = *reinterpret_cast<const i32x4_t*>(&wbuf[(16 * q + i16) * 128 + 16 * ((4 * h + g) ^ fsw)]);
+    if (c * 128 + 64 >= rowb) {  // half last chunk
+      const i32x4_t zero = {0, 0, 0, 0};
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int sgm = (8 * c + 4 * h + g) ^ (r & 15);
-            tf[tt][h] = *reinterpret_cast<const i32x4_t*>(&tb[r * kPfStage + 16 * sgm]);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            if constexpr (G1) mfma_chunk<FP8>(acc[q][tt], wb[c & 1][q], tf[tt]);
-            else mfma_chunk<FP8>(acc[q][tt], tf[tt], wb[c & 1][q]);
-          }
-      }
-      // the next stage's rows go to the other buffer mid-stage: that buffer was last read
-      // before the previous barrier, and the staging loads (issued before this stage's
-      // weight prefetches) have landed by now
-      if (c == 1 && st + 1 < nst) store_stage((st + 1) & 1);
+      for (int q = 0; q < 4; ++q) wf[q][1] = zero;
     }
-    // LDS-only barrier: the weight prefetch for the next chunk stays in flight
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // slot-row fragments: a ring of 4, read 3 groups ahead of the MFMAs that use them
+    i32x4_t tf[4][2];
+    auto rd = [&](int m) {
+      const int tt = 2 * m + th;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        tf[m & 3][h] = *reinterpret_cast<const i32x4_t*>(&tb[(tt * 16 + i16) * 128 + 16 * ((4 * h + g) ^ fsw)]);
+    };
+#pragma unroll
+    for (int m = 0; m < 3 && m < MH; ++m) rd(m);
+#pragma unroll
+    for (int m = 0; m < MH; ++m) {
+      if (m + 3 < MH) rd(m + 3);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (G1) mfma_chunk<FP8>(acc[q][m], wf[q], tf[m & 3]);
+        else mfma_chunk<FP8>(acc[q][m], tf[m & 3], wf[q]);
+      }
+    }
+    // chunk c + 1 has landed and every wave is done with buffer c % 2
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (!on) return;
 
   if constexpr (G1) {
-    // acc[q][tt][r]: channel row0 + 16*(q&1) + 4g + r (q<2 gate, q>=2 up), slot column i16
+    // acc[q][m][r]: channel row0 + 16*(q&1) + 4g + r (q<2 gate, q>=2 up), slot column i16
+    // of group tt = 2 m + th
     const int I = N;
-    uint16_t* a_out = reinterpret_cast<uint16_t*>(out);
+    uint16_t* a_out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n0 = row0 + 16 * h + 4 * g;
       float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
       if constexpr (FP8) {
-        const float* ws = w_scale + (size_t)e * 2 * I;
+        const float* ws = p.w_scale + (size_t)p.e * 2 * I;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           sg[r] = ws[n0 + r];
@@ -539,15 +557,15 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(
         }
       }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int s = s_slot[tt * 16 + i16];
+      for (int m = 0; m < MH; ++m) {
+        const int s = s_slot[(2 * m + th) * 16 + i16];
         if ((unsigned)s >= (unsigned)n_slots) continue;
         float xs = 1.f;
-        if constexpr (FP8) xs = act_scale[s / k];
+        if constexpr (FP8) xs = p.act_scale[s / p.k];
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          v[r] = silu_mul(acc[h][tt][r] * (sg[r] * xs), acc[2 + h][tt][r] * (su[r] * xs));
+          v[r] = silu_mul(acc[h][m][r] * (sg[r] * xs), acc[2 + h][m][r] * (su[r] * xs));
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
@@ -555,30 +573,71 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(
       }
     }
   } else {
-    // acc[q][tt][r]: slot row tt*16 + 4g + r, model_dim channel row0 + 16q + i16
+    // acc[q][m][r]: slot row (2 m + th)*16 + 4g + r, model_dim channel row0 + 16q + i16
     const int D = N;
-    float* y = reinterpret_cast<float*>(out);
+    float* y = reinterpret_cast<float*>(p.out);
     float ws[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (FP8) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ws[q] = w_scale[(size_t)e * D + row0 + 16 * q + i16];
+      for (int q = 0; q < 4; ++q) ws[q] = p.w_scale[(size_t)p.e * D + row0 + 16 * q + i16];
     }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int m = 0; m < MH; ++m) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = s_slot[tt * 16 + 4 * g + r];
+        const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
         if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
-        float sc = topk_w[s];
-        if constexpr (FP8) sc *= act_scale[s];
-        float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / k) * D + row0 + i16;
+        float sc = p.topk_w[s];
+        if constexpr (FP8) sc *= p.act_scale[s];
+        float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / p.k) * D + row0 + i16;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float c = acc[q][tt][r] * (FP8 ? sc * ws[q] : sc);
-          if constexpr (MODE == PF_G2_REDUCE) dst[16 * q] = c;
-          else atomicAdd(dst + 16 * q, c);
+          const float cv = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
+          if constexpr (MODE == PF_G2_REDUCE) dst[16 * q] = cv;
+          else atomicAdd(dst + 16 * q, cv);
         }
       }
+    }
+  }
+}
+
+// Block = 8 waves; tile = a run of one expert's sorted blocks inside an aligned window of
+// kPfMaxBlocks blocks (the workgroups of the run's other blocks exit at once) x one tile of
+// 256 weight rows (gemm1: 128 gate and the matching 128 up channels; gemm2: 256 model_dim
+// rows).
+template <bool FP8, int MODE>
+__global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
+    const uint8_t* __restrict__ act, const float* __restrict__ act_scale,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
+    int k, int N, int K, int mbs, void* __restrict__ out, float4* __restrict__ zero_y,
+    int64_t zero_n4) {
+  constexpr bool G1 = MODE == PF_G1;
+  __shared__ __align__(16) uint8_t tok[2][kPfMaxRows * 128];
+  __shared__ __align__(16) uint8_t wgt[2][256 * 128];
+  __shared__ int s_slot[kPfMaxRows];
+  if (zero_y)
+    for (int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 512)
+      zero_y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int tile_n = G1 ? 128 : 256;
+  int mb, nt;
+  if (!block_tile_rows(mbs, (N + tile_n - 1) / tile_n, mb, nt)) return;
+  const int nvb = *num_valid / kPfRows;  // sorted blocks holding slots
+  if (mb >= nvb) return;
+  const int e = expert_ids[mb];
+  if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
+  if ((mb % kPfMaxBlocks) != 0 && expert_ids[mb - 1] == e) return;
+  int nb = 1;
+  while (nb < kPfMaxBlocks - (mb % kPfMaxBlocks) && mb + nb < nvb && expert_ids[mb + nb] == e) ++nb;
+  for (int i = threadIdx.x; i < kPfRows * nb; i += 512) s_slot[i] = sorted_ids[mb * kPfRows + i];
+  __syncthreads();  // s_slot
+  const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out};
+  switch (nb) {
+    case 1: prefill_tile<FP8, MODE, 1>(p, s_slot, tok, wgt); break;
+    case 2: prefill_tile<FP8, MODE, 2>(p, s_slot, tok, wgt); break;
+    case 3: prefill_tile<FP8, MODE, 3>(p, s_slot, tok, wgt); break;
+    default: prefill_tile<FP8, MODE, 4>(p, s_slot, tok, wgt); break;
   }
 }
 
@@ -692,11 +751,11 @@ hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void
   if (use_prefill(B, T, k, E)) {
     const dim3 grid(xcd_grid(mbs, (I + 127) / 128));
     if (fp8)
-      gemm_prefill_kernel<true, PF_G1><<<grid, 256, 0, st>>>(
+      gemm_prefill_kernel<true, PF_G1><<<grid, 512, 0, st>>>(
           (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, nullptr, sorted_ids, expert_ids,
           num_valid, T, E, k, I, D, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
     else
-      gemm_prefill_kernel<false, PF_G1><<<grid, 256, 0, st>>>(
+      gemm_prefill_kernel<false, PF_G1><<<grid, 512, 0, st>>>(
           (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, nullptr, sorted_ids, expert_ids,
           num_valid, T, E, k, I, D, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
     hipError_t err = hipGetLastError();
@@ -762,7 +821,7 @@ hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void
   if (use_prefill(B, T, k, E)) {
     const dim3 grid(xcd_grid(mbs, (D + 255) / 256));
 #define MOE_PF2(F8, MD)                                                                              \
-  gemm_prefill_kernel<F8, MD><<<grid, 256, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,  \
+  gemm_prefill_kernel<F8, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,  \
                                                    w2_scale, topk_w, sorted_ids, expert_ids,        \
                                                    num_valid, T, E, k, D, I, mbs, y, nullptr, 0)
     if (fp8) {
