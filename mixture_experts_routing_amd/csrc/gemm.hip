@@ -409,6 +409,7 @@ enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2 };
 constexpr int kPfRows = 64;                          // rows of one sorted block
 constexpr int kPfMaxBlocks = 4;                      // sorted blocks per tile
 constexpr int kPfMaxRows = kPfRows * kPfMaxBlocks;   // 256
+constexpr int kPfRingBytes = 160 * 1024 - kPfMaxRows * 4;  // LDS of one CU, less the slot ids
 
 struct PfArgs {
   const uint8_t* act;
@@ -430,11 +431,15 @@ struct PfArgs {
 // the load addresses are fixed; each chunk only advances the wave-uniform bases.
 template <bool FP8, int MODE, int NB>
 __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restrict__ s_slot,
-                                             uint8_t (*tok)[kPfMaxRows * 128],
-                                             uint8_t (*wgt)[256 * 128]) {
+                                             uint8_t* __restrict__ ring) {
   constexpr bool G1 = MODE == PF_G1;
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int MH = 2 * NB;  // slot-row groups per wave
+  // LDS ring: NBUF buffers of (slot rows | weight rows) for one 128-byte chunk each; short
+  // tiles fit three buffers and load two chunks ahead
+  constexpr int TOKB = kPfRows * NB * 128, BUF = TOKB + 256 * 128;
+  constexpr int NBUF = 3 * BUF <= kPfRingBytes ? 3 : 2;
+  constexpr int NDMA = NB + 4;  // load instructions per wave and chunk
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wr = wave & 3, th = wave >> 2;
@@ -475,20 +480,19 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
   const int row0 = G1 ? p.nt * 128 + wr * 32 : p.nt * 256 + wr * 64;
   const bool on = row0 < N;
   const int nch = (rowb + 127) >> 7;
-  const uint32_t tok_lds = (uint32_t)(uintptr_t)&tok[0][0], wgt_lds = (uint32_t)(uintptr_t)&wgt[0][0];
-  // chunk c's loads into buffer c % 2.  In a half last chunk (fp8, K % 128 == 64) the lanes
-  // of the missing half read the present half again; their weight operand bytes are zeroed.
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  // chunk c's loads into buffer c % NBUF.  In a half last chunk (fp8, K % 128 == 64) the
+  // lanes of the missing half read the present half again; their weight operand bytes are
+  // zeroed.
   auto issue = [&](int c) {
-    const int b = c & 1;
+    const uint32_t bo = ring_lds + (uint32_t)((c % NBUF) * BUF);
     const uint32_t lo = (c * 128 + 64 >= rowb && ls >= 4) ? 16u * (ls & 3) : 16u * ls;
     const uint8_t* tb = p.act + (size_t)c * 128;
     const uint8_t* wb = wexp + (size_t)c * 128;
 #pragma unroll
-    for (int v = 0; v < NB; ++v)
-      dma16_to_lds_s(tb, toff[v] + lo, tok_lds + b * (kPfMaxRows * 128) + (wave + 8 * v) * 1024);
+    for (int v = 0; v < NB; ++v) dma16_to_lds_s(tb, toff[v] + lo, bo + (wave + 8 * v) * 1024);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      dma16_to_lds_s(wb, woff[u] + lo, wgt_lds + b * (256 * 128) + (wave + 8 * u) * 1024);
+    for (int u = 0; u < 4; ++u) dma16_to_lds_s(wb, woff[u] + lo, bo + TOKB + (wave + 8 * u) * 1024);
   };
 
   f32x4_t acc[4][MH];
@@ -499,11 +503,15 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
 
   const int fsw = (i16 >> 1) & 7;  // read-side swizzle of row i16 of any 16-row group
   issue(0);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (NBUF == 3 && nch > 1) issue(1);
+  if (NBUF == 3 && nch > 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) issue(c + 1);
-    const uint8_t* tb = tok[c & 1];
-    const uint8_t* wbuf = wgt[c & 1] + (64 * wr) * 128;
+    // buffer (c + NBUF - 1) % NBUF was last read in chunk c - 1, before the last barrier
+    const bool more = c + NBUF - 1 < nch;
+    if (more) issue(c + NBUF - 1);
+    const uint8_t* tb = ring + (c % NBUF) * BUF;
+    const uint8_t* wbuf = tb + TOKB + (64 * wr) * 128;
     i32x4_t wf[4][2];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -534,8 +542,10 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
         else mfma_chunk<FP8>(acc[q][m], tf[m & 3], wf[q]);
       }
     }
-    // chunk c + 1 has landed and every wave is done with buffer c % 2
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // chunk c + 1 has landed (only the loads issued in this chunk may still be in flight)
+    // and every wave is done with buffer c % NBUF
+    if (NBUF == 3 && more) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (!on) return;
 
@@ -614,8 +624,7 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
     int k, int N, int K, int mbs, void* __restrict__ out, float4* __restrict__ zero_y,
     int64_t zero_n4) {
   constexpr bool G1 = MODE == PF_G1;
-  __shared__ __align__(16) uint8_t tok[2][kPfMaxRows * 128];
-  __shared__ __align__(16) uint8_t wgt[2][256 * 128];
+  __shared__ __align__(16) uint8_t ring[kPfRingBytes];
   __shared__ int s_slot[kPfMaxRows];
   if (zero_y)
     for (int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 512)
@@ -634,10 +643,10 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
   __syncthreads();  // s_slot
   const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out};
   switch (nb) {
-    case 1: prefill_tile<FP8, MODE, 1>(p, s_slot, tok, wgt); break;
-    case 2: prefill_tile<FP8, MODE, 2>(p, s_slot, tok, wgt); break;
-    case 3: prefill_tile<FP8, MODE, 3>(p, s_slot, tok, wgt); break;
-    default: prefill_tile<FP8, MODE, 4>(p, s_slot, tok, wgt); break;
+    case 1: prefill_tile<FP8, MODE, 1>(p, s_slot, ring); break;
+    case 2: prefill_tile<FP8, MODE, 2>(p, s_slot, ring); break;
+    case 3: prefill_tile<FP8, MODE, 3>(p, s_slot, ring); break;
+    default: prefill_tile<FP8, MODE, 4>(p, s_slot, ring); break;
   }
 }
 
