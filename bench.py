@@ -230,6 +230,48 @@ def measure_router(env, E, k, score, steps, warmup):
 KERNEL_SOURCES = ("mixture_experts_routing_amd/csrc/gemm.hip", "mixture_experts_routing_amd/csrc/moe_device.h")
 
 
+def achievable_peaks(torch, dev):
+    """What PyTorch's own kernels reach on this machine, reported beside the spec-sheet peaks as
+    context (not as a ceiling: the layer's gemm1 streams faster than torch's sum reads): a
+    streaming read (sum over 4 GiB), a device copy (1 GiB each way, both directions counted),
+    and dense 8192^3 matmuls (bf16, and fp8 e4m3 with unit scales when torch supports it)."""
+    res = {}
+    def timed(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / 1e3
+    a = torch.empty(1 << 30, dtype=torch.float32, device=dev)
+    a.fill_(1.0)
+    res["hbm_read_GBps"] = round(4 * 2**30 / timed(lambda: a.sum()) / 1e9, 1)
+    del a
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    res["hbm_copy_GBps"] = round(2 * 2**30 / timed(lambda: dst.copy_(src)) / 1e9, 1)
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    y = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    res["bf16_matmul_TFLOPS"] = round(2 * n**3 / timed(lambda: x @ y) / 1e12, 1)
+    try:
+        xf = x.to(torch.float8_e4m3fn)
+        yf = y.t().contiguous().to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device=dev)
+        res["fp8_matmul_TFLOPS"] = round(
+            2 * n**3 / timed(lambda: torch._scaled_mm(xf, yf, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)) / 1e12, 1)
+    except Exception as exc:  # pragma: no cover - depends on the torch build
+        res["fp8_matmul_TFLOPS"] = None
+        res["fp8_matmul_note"] = f"torch._scaled_mm unavailable: {type(exc).__name__}"
+    del x, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def kernel_source_sha256():
     import hashlib
     h = hashlib.sha256()
@@ -338,6 +380,9 @@ def main():
     del keep
     torch.cuda.empty_cache()
 
+    log("measuring achievable peaks (torch streaming read, copy, dense matmuls)")
+    peaks = achievable_peaks(torch, dev)
+
     secondary = []
     if not args.headline_only:
         for name, T in (("gptoss", 16), ("gptoss", 4096), ("kimi", 64), ("kimi", 4096), ("kimi", 16384)):
@@ -370,6 +415,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "layer": head,
+        "achievable_peaks": peaks,
         "secondary": secondary,
     }
     print(json.dumps(res))
