@@ -25,6 +25,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                                # MI355X HBM3E
+# fp32 atomic adds to HBM-resident memory, measured on MI355X with a plain atomic-add stream
+# (0.32-0.34 G adds/ms whatever the lane pattern or occupancy): the floor of atomic mode
+ATOMIC_ADDS_PER_S = 3.3e11
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense
 
 
@@ -182,6 +185,11 @@ def measure_layer(env, wl, T, steps, warmup, rotate):
                    "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[dtype], 4),
                    "binding": "hbm" if t_hbm >= t_mfma else "mfma",
                    "frac_of_binding_floor": round(max(t_hbm, t_mfma) / t_s, 4)}
+    if mode == "atomic":
+        adds = T * k * D  # one fp32 atomic add per slot and model_dim channel
+        gemm["gemm2"]["atomic_adds"] = adds
+        gemm["gemm2"]["atomic_floor_us"] = round(adds / ATOMIC_ADDS_PER_S * 1e6, 1)
+        gemm["gemm2"]["frac_of_atomic_floor"] = round(adds / ATOMIC_ADDS_PER_S / (stage_ms["gemm2"] / 1e3), 4)
     res = {
         "workload": wl.name, "T": T, "dtype": dtype, "mode": mode, "us_per_call": round(ms_per_call * 1e3, 2),
         "timing": how,

@@ -8,20 +8,21 @@
 // per-token x per-channel fp8 dequant in the stage-2 epilogue, routed weight,
 // atomic or reduce epilogue, padding lanes issuing no atomics.
 //
-// Layout of the work (one 256-thread workgroup = 4 waves):
+// Decode kernels (gemm1_kernel, gemm2_kernel; one 256-thread workgroup = 4 waves):
 //  * block = one BLOCK_M-row block of the sorted list (one expert) x one tile of
 //    output channels.  Blocks past num_valid exit at once.
 //  * each wave owns two 16-row groups of weight rows (stage 1: 16 gate rows and the
 //    matching 16 up rows; stage 2: 32 consecutive model_dim rows) and streams
-//    them straight from HBM into registers, 128 contiguous bytes per row per
-//    K-chunk.  The gathered activation rows are read per wave from L2.
+//    them straight from HBM into registers; K may be split over the block's waves.
+//    The gathered activation rows are read per wave from L2.
 //  * MFMA: bf16 16x16x32 (two per 128-byte chunk) or fp8 e4m3 16x16x128 (one per
-//    chunk).  Lane (i, g) = (lane % 16, lane / 16) carries bytes [32g, 32g+32) of
-//    row i of the chunk for both operands; the MFMA sums over K, so this common
-//    permutation of K leaves the result unchanged.
+//    chunk).  Lane (i, g) = (lane % 16, lane / 16) carries bytes [16g, 16g+16) and
+//    [64+16g, 64+16g+16) of row i of the chunk for both operands; the MFMA sums over K,
+//    so this common permutation of K leaves the result unchanged.
 //  * accumulator lane layout: lane (j, g) holds output rows 4g..4g+3 (channels)
 //    of column j (the j-th gathered row), so a lane owns 4 consecutive channels
 //    of one slot.
+// The prefill kernel (gemm_prefill_kernel, further down) tiles many rows per expert.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -391,15 +392,13 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
 }
 
 // ----------------------------------------------------------------------------- prefill tiles
-// Many gathered rows per expert (prefill): the same weight tile serves several 64-row
-// blocks, and the MFMA units, not HBM, set the pace.  Block = one 64-row block of the
-// sorted list x 256 weight rows; wave = 64 weight rows (4 groups of 16) x the 64
-// gathered rows (4 tiles of 16).
-//  * the gathered rows are staged in LDS, 512 K-bytes per row per stage, double
-//    buffered with one barrier per stage; 16-byte segment s of row r sits at segment
-//    s ^ (r & 15), so the 16 rows that 16 lanes of an operand read touch land in 16
-//    different bank groups;
-//  * weight rows stream from HBM/L2 straight into registers, one 128-byte chunk ahead;
+// Many gathered rows per expert (prefill): a weight tile serves up to four 64-row blocks of
+// one expert, and both operands go through LDS.
+//  * loads: a 16-byte load whose 64 lanes cover 16 rows x 64 B (the MFMA operand layout)
+//    streams about a third as fast from L2 as one covering 8 rows x 128 B with 8
+//    consecutive lanes per row.  Both operands are therefore brought in full 128-byte rows
+//    by direct-to-LDS loads and read back in MFMA layout; logical segment s of row r sits at
+//    segment s ^ ((r / 2) % 8), which keeps both the loads and the reads conflict-free;
 //  * stage 1 (gate-up): weight rows are the first MFMA operand, so a lane ends up with 4
 //    consecutive channels of one slot (gate and up pair in the same lane);
 //  * stage 2 (down): the operands are swapped, so a lane holds one model_dim channel of
