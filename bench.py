@@ -281,11 +281,17 @@ def achievable_peaks(torch, dev):
 
 
 def kernel_source_sha256():
+    """sha256 of the GEMM sources with comments and blank space removed, so that only code
+    changes (which can change the kernels' traffic) invalidate stored counter readings."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()
 
 
