@@ -610,10 +610,10 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
   }
 }
 
-// Block = 8 waves; tile = a run of one expert's sorted blocks inside an aligned window of
-// kPfMaxBlocks blocks (the workgroups of the run's other blocks exit at once) x one tile of
-// 256 weight rows (gemm1: 128 gate and the matching 128 up channels; gemm2: 256 model_dim
-// rows).
+// Block = 8 waves; tile = up to kPfMaxBlocks consecutive sorted blocks of one expert, counted
+// from the expert's first block (the workgroups of the tile's other blocks exit at once) x one
+// tile of 256 weight rows (gemm1: 128 gate and the matching 128 up channels; gemm2: 256
+// model_dim rows).
 template <bool FP8, int MODE>
 __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
     const uint8_t* __restrict__ act, const float* __restrict__ act_scale,
@@ -635,9 +635,20 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
   if (mb >= nvb) return;
   const int e = expert_ids[mb];
   if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
-  if ((mb % kPfMaxBlocks) != 0 && expert_ids[mb - 1] == e) return;
+  // blocks of expert e right before mb (expert_ids is non-decreasing), 64 per step, every
+  // wave on its own
+  int before = 0;
+  for (int base = mb - 1;; base -= 64) {
+    const int idx = base - lane_id();
+    const bool same = idx >= 0 && expert_ids[idx] == e;
+    const uint64_t run = ~__ballot(same);
+    const int n = run == 0 ? 64 : __builtin_ctzll(run);
+    before += n;
+    if (n < 64) break;
+  }
+  if (before % kPfMaxBlocks != 0) return;
   int nb = 1;
-  while (nb < kPfMaxBlocks - (mb % kPfMaxBlocks) && mb + nb < nvb && expert_ids[mb + nb] == e) ++nb;
+  while (nb < kPfMaxBlocks && mb + nb < nvb && expert_ids[mb + nb] == e) ++nb;
   for (int i = threadIdx.x; i < kPfRows * nb; i += 512) s_slot[i] = sorted_ids[mb * kPfRows + i];
   __syncthreads();  // s_slot
   const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out};
