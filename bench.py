@@ -10,7 +10,8 @@ input sets (logits and activations) rotate so the active experts change call to 
 The JSON line also carries the roofline of the dominant kernel (HIP events on the
 stream it runs on), the CPU oracle's time on a bounded sample, and (unless
 --headline-only) secondary lines: GPT-OSS decode/prefill and Kimi fp8 layer times
-with per-GEMM TFLOPS, and router-only GB/s at T=8192.
+with per-GEMM TFLOPS, the DeepSeek and Kimi layers again with packed bf16 atomics into
+the output, and router-only GB/s at T=8192.
 """
 
 from __future__ import annotations
@@ -103,10 +104,12 @@ def algorithmic(wl, T, n_act, num_valid):
             "gemm1_flops": 2 * T * k * 2 * I * D, "gemm2_flops": 2 * T * k * D * I}
 
 
-def measure_layer(env, wl, T, steps, warmup, rotate):
-    """Times moe_forward and, separately, each stage; returns a result dict."""
+def measure_layer(env, wl, T, steps, warmup, rotate, mode=None):
+    """Times moe_forward and, separately, each stage; returns a result dict.  mode overrides
+    the workload's output mode (atomic_bf16: packed bf16 atomics straight into out)."""
     m, torch, np, synth, dev = env
-    k, B, dtype, mode = wl.topk, wl.block_m, wl.dtype, wl.mode
+    k, B, dtype = wl.topk, wl.block_m, wl.dtype
+    mode = mode or wl.mode
     E, D, I = wl.E, wl.D, wl.I
     log(f"{wl.name} T={T} E={E} k={k} D={D} I={I} B={B} {dtype} {mode}: generating inputs")
     base = synth.layer_inputs(wl, 1, seed=0, device=dev)
@@ -135,6 +138,8 @@ def measure_layer(env, wl, T, steps, warmup, rotate):
     # per-stage durations: each stage alone, `steps` calls per graph, on per-set routing
     views = m.workspace_views(ws, offs, dtype, mode, T, E, k, D, I, B)
     a, a_scale, y = views["a"], views["a_scale"], views["y"]
+    if mode == "atomic_bf16":
+        y = out  # stage 2 adds into the bf16 output (the timing leaves its values meaningless)
     g1ws = ws[offs["gemm1_scratch"]:] if offs["gemm1_scratch"] is not None else None
     rws = ws[offs["route_scratch"]:] if offs["route_scratch"] is not None else None
     routes, per_set = [], []
@@ -185,8 +190,11 @@ def measure_layer(env, wl, T, steps, warmup, rotate):
                    "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[dtype], 4),
                    "binding": "hbm" if t_hbm >= t_mfma else "mfma",
                    "frac_of_binding_floor": round(max(t_hbm, t_mfma) / t_s, 4)}
-    if mode == "atomic":
-        adds = T * k * D  # one fp32 atomic add per slot and model_dim channel
+    if mode in ("atomic", "atomic_bf16"):
+        # one fp32 atomic add per slot and model_dim channel, or one packed bf16 add per
+        # channel pair; the floor takes the measured fp32 rate for both (the packed rate is
+        # assumed equal, per 32-bit operation)
+        adds = T * k * D if mode == "atomic" else T * k * D // 2
         gemm["gemm2"]["atomic_adds"] = adds
         gemm["gemm2"]["atomic_floor_us"] = round(adds / ATOMIC_ADDS_PER_S * 1e6, 1)
         gemm["gemm2"]["frac_of_atomic_floor"] = round(adds / ATOMIC_ADDS_PER_S / (stage_ms["gemm2"] / 1e3), 4)
@@ -399,8 +407,10 @@ def main():
 
     secondary = []
     if not args.headline_only:
-        for name, T in (("gptoss", 16), ("gptoss", 4096), ("kimi", 64), ("kimi", 4096), ("kimi", 16384)):
-            r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2)
+        for name, T, mode in (("gptoss", 16, None), ("gptoss", 4096, None), ("kimi", 64, None),
+                              ("kimi", 4096, None), ("kimi", 16384, None), ("deepseek", 16, "atomic_bf16"),
+                              ("kimi", 4096, "atomic_bf16"), ("kimi", 16384, "atomic_bf16")):
+            r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2, mode)
             del kp
             torch.cuda.empty_cache()
             secondary.append(r)

@@ -56,7 +56,7 @@ enum moe_status {
 
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_dtype { MOE_BF16 = 0, MOE_FP8_E4M3 = 1 };
-enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1 };
+enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1, MOE_OUT_ATOMIC_BF16 = 2 };
 
 /* Largest E accepted ([P3] "Hardening": the radix top-k path's 8160-expert bound). */
 #define MOE_MAX_EXPERTS 8160
@@ -87,6 +87,7 @@ int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I);
  *   6 a: bf16 [T*k,I] or e4m3 [T*k,I]
  *   7 a_scale fp32 [T*k] (fp8)     8 gemm1 scratch (fp8: bf16 [T*k,I])
  *   9 y: ATOMIC fp32 [T,D] accumulator, REDUCE fp32 [T*k,D] slot rows
+ *        (ATOMIC_BF16: unused, -1; the stage-2 atomics add into out itself)
  * Returns the total size in bytes, or a negative moe_status. */
 #define MOE_WS_NFIELDS 10
 int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
@@ -163,8 +164,14 @@ int moe_gemm1_gateup(int dtype, const void* x, const float* x_scale, const void*
  * For every real slot s = t*k + j in a block of expert e:
  *   c_s[d] = topk_weights[s] * sum_n W2[e, d, n] * a[s, n]
  *            (fp8: * a_scale[s] * w2_scale[e, d])
- *   ATOMIC: y[t, d] += c_s[d]   (y fp32 [T, D]; the caller zeroes it first)
- *   REDUCE: y[s, d]  = c_s[d]   (y fp32 [T*k, D])
+ *   ATOMIC:      y[t, d] += c_s[d]   (y fp32 [T, D]; the caller zeroes it first)
+ *   REDUCE:      y[s, d]  = c_s[d]   (y fp32 [T*k, D])
+ *   ATOMIC_BF16: y[t, d] += c_s[d]   (y bf16 [T, D], zeroed by the caller; [P2] "atomic
+ *                scatter into out": each c_s[d] is rounded to bf16 and added to the
+ *                pair (d, d+1) with one packed bf16 atomic add, which rounds the running
+ *                sum to bf16 again.  Half the atomic operations of ATOMIC; the result
+ *                depends on the order of the k adds, and beyond ATOMIC's rounding it may
+ *                differ from the exact sum by up to (k+1) * 2^-9 * sum_j |c_{t*k+j}[d]|.)
  *
  *   a, a_scale        as written by moe_gemm1_gateup
  *   w2                bf16 [E, D, I] | e4m3 [E, D, I]   w2_scale fp32 [E, D] (fp8 only)
@@ -173,20 +180,21 @@ int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w
                    const float* w2_scale, const float* topk_weights,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
                    const int32_t* num_valid, int64_t sorted_cap, int T, int E, int topk, int D,
-                   int I, int block_m, int mode, float* y, void* stream);
+                   int I, int block_m, int mode, void* y, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * [P2] stage-2 commit and summary: the reduce mode's separate reduction kernel.
  * ATOMIC: out[t, d] = bf16_rne(y[t, d]), y fp32 [T, D].
  * REDUCE: out[t, d] = bf16_rne(sum_j y[t*k + j, d]) summed in fp32, j ascending.
+ * ATOMIC_BF16: nothing to do (stage 2 wrote the bf16 result); y and out are not used.
  *   out bf16 [T, D] */
 int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------- whole layer
- * moe_topk_softmax_sort -> (ATOMIC: zero the accumulator) -> moe_gemm1_gateup
- * -> moe_gemm2_down -> moe_finalize, all on `stream`, with every intermediate
- * in `workspace` at the offsets moe_forward_workspace_layout reports (so they
- * can be read back).  out bf16 [T, D]. */
+ * moe_topk_softmax_sort -> (ATOMIC: zero the accumulator; ATOMIC_BF16: zero out)
+ * -> moe_gemm1_gateup -> moe_gemm2_down -> moe_finalize, all on `stream`, with every
+ * intermediate in `workspace` at the offsets moe_forward_workspace_layout reports (so
+ * they can be read back).  out bf16 [T, D]. */
 int moe_forward(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
                 const float* x_scale, const void* w1, const float* w1_scale, const void* w2,
                 const float* w2_scale, int T, int E, int topk, int D, int I, int block_m,

@@ -37,7 +37,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 SCORE = {"softmax": 0, "sigmoid": 1}
 DTYPE = {"bf16": 0, "fp8": 1}
-MODE = {"atomic": 0, "reduce": 1}
+MODE = {"atomic": 0, "reduce": 1, "atomic_bf16": 2}
 WS_FIELDS = ("topk_weights", "topk_ids", "sorted_token_ids", "expert_ids", "num_valid",
              "route_scratch", "a", "a_scale", "gemm1_scratch", "y")
 
@@ -178,12 +178,16 @@ def moe_gemm1_gateup(dtype: str, x, w1, route: dict, topk: int, block_m: int, x_
 
 def moe_gemm2_down(dtype: str, a, w2, route: dict, T: int, topk: int, block_m: int, mode: str,
                    a_scale=None, w2_scale=None, y=None, stream=None):
-    """Stage 2: returns y (ATOMIC: fp32 [T, D] accumulated into; REDUCE: fp32 [T*k, D])."""
+    """Stage 2: returns y (ATOMIC: fp32 [T, D] accumulated into; REDUCE: fp32 [T*k, D];
+    ATOMIC_BF16: bf16 [T, D] accumulated into)."""
     E, D, I = w2.shape
     dev = a.device
     if y is None:
-        rows = T if mode == "atomic" else T * topk
-        y = torch.zeros(rows, D, dtype=torch.float32, device=dev)
+        if mode == "atomic_bf16":
+            y = torch.zeros(T, D, dtype=torch.bfloat16, device=dev)
+        else:
+            rows = T if mode == "atomic" else T * topk
+            y = torch.zeros(rows, D, dtype=torch.float32, device=dev)
     sid = route["sorted_token_ids"]
     _check(load_library().moe_gemm2_down(
         DTYPE[dtype], _ptr(a), _ptr(a_scale), _ptr(w2), _ptr(w2_scale), _ptr(route["topk_weights"]),
@@ -193,7 +197,7 @@ def moe_gemm2_down(dtype: str, a, w2, route: dict, T: int, topk: int, block_m: i
 
 
 def moe_finalize(mode: str, y, T: int, topk: int, D: int, out=None, stream=None):
-    """Combine: bf16 out [T, D] from the fp32 accumulator or slot rows."""
+    """Combine: bf16 out [T, D] from the fp32 accumulator or slot rows (ATOMIC_BF16: no-op)."""
     if out is None:
         out = torch.empty(T, D, dtype=torch.bfloat16, device=y.device)
     _check(load_library().moe_finalize(MODE[mode], _ptr(y), T, topk, D, _ptr(out), _stream(stream)),

@@ -40,6 +40,10 @@ int check_layer_dims(int dtype, int T, int E, int topk, int D, int I, int block_
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 
+bool ok_mode(int mode) {
+  return mode == MOE_OUT_ATOMIC || mode == MOE_OUT_REDUCE || mode == MOE_OUT_ATOMIC_BF16;
+}
+
 struct Layout {
   int64_t off[MOE_WS_NFIELDS];
   int64_t total;
@@ -70,7 +74,8 @@ Layout forward_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
     L.off[7] = -1;
     L.off[8] = -1;
   }
-  take(9, (mode == MOE_OUT_ATOMIC ? (int64_t)T : n) * D * 4);
+  if (mode == MOE_OUT_ATOMIC_BF16) L.off[9] = -1;
+  else take(9, (mode == MOE_OUT_ATOMIC ? (int64_t)T : n) * D * 4);
   L.total = p;
   return L;
 }
@@ -112,7 +117,7 @@ int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I) {
 
 int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
                                      int block_m, int64_t* offsets) {
-  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+  if (!ok_mode(mode)) return MOE_EINVAL;
   const int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
   if (st) return st;
   const Layout L = forward_layout(dtype, mode, T, E, topk, D, I, block_m);
@@ -182,8 +187,8 @@ int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w
                    const float* w2_scale, const float* topk_weights,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
                    const int32_t* num_valid, int64_t sorted_cap, int T, int E, int topk, int D,
-                   int I, int block_m, int mode, float* y, void* stream) {
-  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+                   int I, int block_m, int mode, void* y, void* stream) {
+  if (!ok_mode(mode)) return MOE_EINVAL;
   int st = check_gemm_common(dtype, T, E, topk, D, I, block_m, sorted_cap, sorted_token_ids,
                              expert_ids, num_valid);
   if (st) return st;
@@ -198,10 +203,10 @@ int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w
 }
 
 int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out, void* stream) {
-  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+  if (!ok_mode(mode)) return MOE_EINVAL;
   if (T < 0 || topk < 1 || D < 64 || D % 64) return T < 0 || topk < 1 ? MOE_EINVAL : MOE_EUNSUPPORTED;
   if ((int64_t)T * topk * D > INT_MAX) return MOE_ERANGE;
-  if (T == 0) return MOE_OK;
+  if (T == 0 || mode == MOE_OUT_ATOMIC_BF16) return MOE_OK;  // bf16 atomics: stage 2 wrote out
   if (!ok_ptr(y) || !ok_ptr(out)) return MOE_EINVAL;
   return launch_status(moe::launch_finalize(mode, y, T, topk, D, out, (hipStream_t)stream));
 }
@@ -210,7 +215,7 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
                 const float* x_scale, const void* w1, const float* w1_scale, const void* w2,
                 const float* w2_scale, int T, int E, int topk, int D, int I, int block_m,
                 void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
-  if (mode != MOE_OUT_ATOMIC && mode != MOE_OUT_REDUCE) return MOE_EINVAL;
+  if (!ok_mode(mode)) return MOE_EINVAL;
   if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
   if (renorm != 0 && renorm != 1) return MOE_EINVAL;
   int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
@@ -236,6 +241,10 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   float* a_scale = static_cast<float*>(at(7));
   void* g1ws = at(8);
   float* y = static_cast<float*>(at(9));
+  // ATOMIC clears the fp32 accumulator, ATOMIC_BF16 the bf16 output (T*D/2 floats' worth)
+  float* zero = mode == MOE_OUT_ATOMIC ? y : mode == MOE_OUT_ATOMIC_BF16 ? reinterpret_cast<float*>(out) : nullptr;
+  const int64_t zero_n = mode == MOE_OUT_ATOMIC ? (int64_t)T * D : mode == MOE_OUT_ATOMIC_BF16 ? (int64_t)T * D / 2 : 0;
+  void* y2 = mode == MOE_OUT_ATOMIC_BF16 ? static_cast<void*>(out) : static_cast<void*>(y);
   const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
   hipStream_t s = (hipStream_t)stream;
 
@@ -244,11 +253,10 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
                           cap, eids, nvalid, rws, s);
   if (e == hipSuccess)
     e = moe::launch_gemm1(fp8, x, x_scale, w1, w1_scale, sorted, eids, nvalid, cap, T, E, topk,
-                          D, I, block_m, a, a_scale, g1ws, mode == MOE_OUT_ATOMIC ? y : nullptr,
-                          mode == MOE_OUT_ATOMIC ? (int64_t)T * D : 0, s);
+                          D, I, block_m, a, a_scale, g1ws, zero, zero_n, s);
   if (e == hipSuccess)
     e = moe::launch_gemm2(fp8, a, a_scale, w2, w2_scale, topk_w, sorted, eids, nvalid, cap, T,
-                          E, topk, D, I, block_m, mode, y, s);
+                          E, topk, D, I, block_m, mode, y2, s);
   if (e == hipSuccess) e = moe::launch_finalize(mode, y, T, topk, D, out, s);
   return launch_status(e);
 }

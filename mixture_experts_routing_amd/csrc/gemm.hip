@@ -36,6 +36,18 @@ __device__ __forceinline__ i32x4_t ld16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4_t*>(p);
 }
 
+// Output modes of stage 2 (moe_mode): fp32 atomic accumulation, fp32 slot rows, or packed
+// bf16 atomic accumulation straight into the bf16 output.
+enum { OM_ATOMIC = 0, OM_REDUCE = 1, OM_ATOMIC_BF16 = 2 };
+
+// out[0..1] += (lo, hi): both values rounded to bf16 (nearest even), then one packed bf16
+// atomic add (the sum is rounded to bf16 again); out must be 4-byte aligned.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void atomic_add_bf16x2(uint16_t* out, float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  __builtin_amdgcn_global_atomic_fadd_v2bf16((__attribute__((address_space(1))) bf16x2_t*)out, v);
+}
+
 // Block -> (row block, channel tile).  Workgroups are handed to the 8 XCDs round
 // robin by id, so id L runs on XCD L % 8.  Each XCD is given one contiguous range
 // of the (tile-major, row-block-minor) order: the row blocks of one expert that
@@ -312,13 +324,13 @@ __global__ void __launch_bounds__(256) requant_rows_kernel(const uint16_t* __res
 // ----------------------------------------------------------------------------- stage 2
 // Block = 4 waves = RG = 4/KS row groups x KS parts of K; a row group is 32
 // model_dim rows.  grid: ceil(D/(32*RG)) channel tiles x cap/BM row blocks.
-template <int BM, bool FP8, int U, bool REDUCE, int KS>
+template <int BM, bool FP8, int U, int OM, int KS>
 __global__ void __launch_bounds__(256) gemm2_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
-    int k, int D, int I, int mbs, float* __restrict__ y) {
+    int k, int D, int I, int mbs, void* __restrict__ y) {
   constexpr int NT = BM / 16;
   constexpr int RG = 4 / KS;
   constexpr int EB = FP8 ? 1 : 2;
@@ -380,12 +392,16 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
       float c[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) c[r] = acc[q][tt][r] * (FP8 ? sc * ws[q][r] : sc);
-      if constexpr (REDUCE) {
-        *reinterpret_cast<float4*>(y + (size_t)s * D + d0) = make_float4(c[0], c[1], c[2], c[3]);
-      } else {
-        float* dst = y + (size_t)(s / k) * D + d0;
+      if constexpr (OM == OM_REDUCE) {
+        *reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)s * D + d0) = make_float4(c[0], c[1], c[2], c[3]);
+      } else if constexpr (OM == OM_ATOMIC) {
+        float* dst = static_cast<float*>(y) + (size_t)(s / k) * D + d0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) atomicAdd(dst + r, c[r]);
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(y) + (size_t)(s / k) * D + d0;
+        atomic_add_bf16x2(dst, c[0], c[1]);
+        atomic_add_bf16x2(dst + 2, c[2], c[3]);
       }
     }
   }
@@ -404,7 +420,7 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
 //  * stage 2 (down): the operands are swapped, so a lane holds one model_dim channel of
 //    4 slots and 16 lanes cover 16 consecutive channels of one slot: each atomic (or
 //    store) instruction writes 64 contiguous bytes per row.
-enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2 };
+enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2, PF_G2_ATOMIC_BF16 = 3 };
 constexpr int kPfRows = 64;                          // rows of one sorted block
 constexpr int kPfMaxBlocks = 4;                      // sorted blocks per tile
 constexpr int kPfMaxRows = kPfRows * kPfMaxBlocks;   // 256
@@ -584,26 +600,62 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
   } else {
     // acc[q][m][r]: slot row (2 m + th)*16 + 4g + r, model_dim channel row0 + 16q + i16
     const int D = N;
-    float* y = reinterpret_cast<float*>(p.out);
     float ws[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (FP8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) ws[q] = p.w_scale[(size_t)p.e * D + row0 + 16 * q + i16];
     }
+    if constexpr (MODE == PF_G2_ATOMIC_BF16) {
+      // channel pairs (2c, 2c+1) sit in lanes i16 = 2c and 2c+1: the even lane adds the pairs
+      // of slot rows r = 0, 1, the odd lane those of r = 2, 3, after one exchange of two
+      // values between the two lanes
+      uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+      const bool odd = (i16 & 1) != 0;
 #pragma unroll
-    for (int m = 0; m < MH; ++m) {
+      for (int m = 0; m < MH; ++m) {
+        int sr[4];
+        float sc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
-        if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
-        float sc = p.topk_w[s];
-        if constexpr (FP8) sc *= p.act_scale[s];
-        float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / p.k) * D + row0 + i16;
+        for (int r = 0; r < 4; ++r) {
+          sr[r] = s_slot[(2 * m + th) * 16 + 4 * g + r];
+          sc[r] = 0.f;
+          if ((unsigned)sr[r] < (unsigned)n_slots) {
+            sc[r] = p.topk_w[sr[r]];
+            if constexpr (FP8) sc[r] *= p.act_scale[sr[r]];
+          }
+        }
+        const int s_a = odd ? sr[2] : sr[0], s_b = odd ? sr[3] : sr[1];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float cv = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
-          if constexpr (MODE == PF_G2_REDUCE) dst[16 * q] = cv;
-          else atomicAdd(dst + 16 * q, cv);
+          float cv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cv[r] = acc[q][m][r] * (FP8 ? sc[r] * ws[q] : sc[r]);
+          const float ra = __uint_as_float(xor_lane<1>(__float_as_uint(odd ? cv[0] : cv[2])));
+          const float rb = __uint_as_float(xor_lane<1>(__float_as_uint(odd ? cv[1] : cv[3])));
+          const int dch = row0 + 16 * q + (i16 & ~1);
+          if ((unsigned)s_a < (unsigned)n_slots)  // padding rows issue nothing
+            atomic_add_bf16x2(out + (size_t)(s_a / p.k) * D + dch, odd ? ra : cv[0], odd ? cv[2] : ra);
+          if ((unsigned)s_b < (unsigned)n_slots)
+            atomic_add_bf16x2(out + (size_t)(s_b / p.k) * D + dch, odd ? rb : cv[1], odd ? cv[3] : rb);
+        }
+      }
+    } else {
+      float* y = reinterpret_cast<float*>(p.out);
+#pragma unroll
+      for (int m = 0; m < MH; ++m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
+          if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
+          float sc = p.topk_w[s];
+          if constexpr (FP8) sc *= p.act_scale[s];
+          float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / p.k) * D + row0 + i16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float cv = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
+            if constexpr (MODE == PF_G2_REDUCE) dst[16 * q] = cv;
+            else atomicAdd(dst + 16 * q, cv);
+          }
         }
       }
     }
@@ -660,9 +712,14 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
   }
 }
 
-// The tiled kernel pays off once the experts carry several 64-row blocks on average.
-static bool use_prefill(int B, int64_t T, int k, int E) {
-  return B == kPfRows && T * k >= 32LL * E;
+// The tiled kernel pays off once the experts carry several 64-row blocks on average.  Its
+// direct-to-LDS loads take 32-bit byte offsets: the activation rows and one expert's
+// weights must each span less than 2 GB (larger shapes run the decode kernels, which
+// address in 64 bits).
+static bool use_prefill(int B, int64_t T, int k, int E, int64_t D, int64_t I) {
+  const int64_t kMax = (int64_t)1 << 31;
+  return B == kPfRows && T * k >= 32LL * E && T * k * (D > I ? D : I) * 2 < kMax &&
+         2 * I * D * 2 < kMax;
 }
 
 // ----------------------------------------------------------------------------- combine
@@ -716,7 +773,7 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st) {
 hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16_t* out,
                            hipStream_t st) {
   const int64_t n4 = (int64_t)T * D / 4;
-  if (n4 == 0) return hipSuccess;
+  if (n4 == 0 || mode == OM_ATOMIC_BF16) return hipSuccess;  // bf16 atomics wrote out itself
   if (mode == 0)
     finalize_atomic_kernel<<<grid_1d(n4), 256, 0, st>>>(y, n4, out);
   else
@@ -767,7 +824,7 @@ hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void
   if (T == 0) return hipSuccess;
   uint16_t* a_bf16 = fp8 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
   const int mbs = (int)(cap / B);
-  if (use_prefill(B, T, k, E)) {
+  if (use_prefill(B, T, k, E, D, I)) {
     const dim3 grid(xcd_grid(mbs, (I + 127) / 128));
     if (fp8)
       gemm_prefill_kernel<true, PF_G1><<<grid, 512, 0, st>>>(
@@ -805,61 +862,70 @@ hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void
   return hipGetLastError();
 }
 
-template <int BM, bool FP8, bool REDUCE, int KS>
+template <int BM, bool FP8, int OM, int KS>
 static void gemm2_go(int mbs, const void* a, const float* a_scale, const void* w2,
                      const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
-                     int D, int I, float* y, hipStream_t st) {
+                     int D, int I, void* y, hipStream_t st) {
   constexpr int U = BM == 64 ? 2 : 4;
   constexpr int RG = 4 / KS;
   const dim3 grid(xcd_grid(mbs, (D + 32 * RG - 1) / (32 * RG)));
-  gemm2_kernel<BM, FP8, U, REDUCE, KS><<<grid, 256, 0, st>>>(
+  gemm2_kernel<BM, FP8, U, OM, KS><<<grid, 256, 0, st>>>(
       (const uint8_t*)a, a_scale, (const uint8_t*)w2, w2_scale, topk_w, sorted_ids, expert_ids,
       num_valid, T, E, k, D, I, mbs, y);
 }
 
-template <int BM, bool FP8, bool REDUCE>
+template <int BM, bool FP8, int OM>
 static void gemm2_ks(int ks, int mbs, const void* a, const float* a_scale, const void* w2,
                      const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
-                     int D, int I, float* y, hipStream_t st) {
+                     int D, int I, void* y, hipStream_t st) {
   if (ks == 4)
-    gemm2_go<BM, FP8, REDUCE, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, FP8, OM, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
   else if (ks == 2)
-    gemm2_go<BM, FP8, REDUCE, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, FP8, OM, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
   else
-    gemm2_go<BM, FP8, REDUCE, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, FP8, OM, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
 }
 
 hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void* w2,
                         const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
-                        int E, int k, int D, int I, int B, int mode, float* y, hipStream_t st) {
+                        int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int mbs = (int)(cap / B);
-  if (use_prefill(B, T, k, E)) {
+  if (use_prefill(B, T, k, E, D, I)) {
     const dim3 grid(xcd_grid(mbs, (D + 255) / 256));
 #define MOE_PF2(F8, MD)                                                                              \
   gemm_prefill_kernel<F8, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,  \
                                                    w2_scale, topk_w, sorted_ids, expert_ids,        \
                                                    num_valid, T, E, k, D, I, mbs, y, nullptr, 0)
+#define MOE_PF2_MODES(F8)                                   \
+  if (mode == OM_REDUCE) MOE_PF2(F8, PF_G2_REDUCE);         \
+  else if (mode == OM_ATOMIC) MOE_PF2(F8, PF_G2_ATOMIC);    \
+  else MOE_PF2(F8, PF_G2_ATOMIC_BF16);
     if (fp8) {
-      if (mode) MOE_PF2(true, PF_G2_REDUCE); else MOE_PF2(true, PF_G2_ATOMIC);
+      MOE_PF2_MODES(true)
     } else {
-      if (mode) MOE_PF2(false, PF_G2_REDUCE); else MOE_PF2(false, PF_G2_ATOMIC);
+      MOE_PF2_MODES(false)
     }
+#undef MOE_PF2_MODES
 #undef MOE_PF2
     return hipGetLastError();
   }
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int ks = pick_ks(n_act * (D / 32));  // ks >= 2 needs D % 64 == 0, which always holds
-#define MOE_G2(BMV)                                                                                   \
-  if (fp8) {                                                                                          \
-    if (mode) gemm2_ks<BMV, true, true>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
-    else gemm2_ks<BMV, true, false>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
-  } else {                                                                                            \
-    if (mode) gemm2_ks<BMV, false, true>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
-    else gemm2_ks<BMV, false, false>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st); \
+#define MOE_G2_OM(BMV, F8, OMV) \
+  gemm2_ks<BMV, F8, OMV>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st)
+#define MOE_G2_F8(BMV, F8)                                 \
+  if (mode == OM_REDUCE) MOE_G2_OM(BMV, F8, OM_REDUCE);     \
+  else if (mode == OM_ATOMIC) MOE_G2_OM(BMV, F8, OM_ATOMIC); \
+  else MOE_G2_OM(BMV, F8, OM_ATOMIC_BF16);
+#define MOE_G2(BMV)          \
+  if (fp8) {                 \
+    MOE_G2_F8(BMV, true)     \
+  } else {                   \
+    MOE_G2_F8(BMV, false)    \
   }
   if (B == 16) {
     MOE_G2(16)
@@ -869,6 +935,8 @@ hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void
     MOE_G2(64)
   }
 #undef MOE_G2
+#undef MOE_G2_F8
+#undef MOE_G2_OM
   return hipGetLastError();
 }
 

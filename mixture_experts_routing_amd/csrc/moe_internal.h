@@ -39,7 +39,7 @@ hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void
 hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void* w2,
                         const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
-                        int E, int k, int D, int I, int B, int mode, float* y, hipStream_t st);
+                        int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st);
 
 hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16_t* out,
                            hipStream_t st);

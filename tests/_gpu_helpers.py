@@ -72,6 +72,28 @@ def compare_out(out_gpu: torch.Tensor, ref_out: np.ndarray, rows, tol: float, co
     return err / rms, cos
 
 
+def compare_out_bf16_atomic(out_gpu: torch.Tensor, ref_out: np.ndarray, ref_contrib: np.ndarray, rows,
+                            k: int, tol: float):
+    """Packed bf16 atomic accumulation: each of a token's k contributions is rounded to bf16
+    and each of the k atomic adds rounds the running sum to bf16, so on top of the fp32
+    modes' bound tol * rms(ref) an element may move by (k + 1) * 2^-9 * sum_j |c_j| (half a
+    bf16 step per rounding, of a value at most sum_j |c_j|).  Returns the largest fraction
+    of that allowance used."""
+    got = out_gpu.detach().float().cpu().double().numpy()[rows]
+    ref = ref_out[rows]
+    assert np.isfinite(got).all()
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    D = ref.shape[1]
+    s_abs = np.abs(ref_contrib.reshape(-1, k, D)[rows]).sum(axis=1)
+    allow = tol * rms + (k + 1) * 2.0 ** -9 * s_abs
+    err = np.abs(got - ref)
+    used = float((err / allow).max())
+    i = np.unravel_index(np.argmax(err / allow), err.shape)
+    assert used <= 1.0, (f"err {err[i]:.4g} > allowance {allow[i]:.4g} at {i} (ref {ref[i]:.5g}, "
+                         f"sum|c| {s_abs[i]:.4g}, rms {rms:.4g})")
+    return used
+
+
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
     """Spacing of bf16 numbers at |v| (normal range)."""
     _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -126))

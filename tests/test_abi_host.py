@@ -55,7 +55,7 @@ def test_sorted_capacity_matches_oracle(lib, T, E, k, B):
 def test_workspace_layout(lib):
     import mixture_experts_routing_amd as m
     for dtype in ("bf16", "fp8"):
-        for mode in ("atomic", "reduce"):
+        for mode in ("atomic", "reduce", "atomic_bf16"):
             for (T, E, k, D, I, B) in [(4, 8, 2, 128, 64, 16), (8192, 2304, 36, 64, 64, 32),
                                        (16, 256, 8, 7168, 2048, 16)]:
                 total, offs = m.moe_forward_workspace_layout(dtype, mode, T, E, k, D, I, B)
@@ -66,7 +66,7 @@ def test_workspace_layout(lib):
                          "a": n * I * (2 if dtype == "bf16" else 1),
                          "a_scale": 4 * n if dtype == "fp8" else 0,
                          "gemm1_scratch": 2 * n * I if dtype == "fp8" else 0,
-                         "y": 4 * D * (T if mode == "atomic" else n)}
+                         "y": 0 if mode == "atomic_bf16" else 4 * D * (T if mode == "atomic" else n)}
                 spans = []
                 for f, o in offs.items():
                     if sizes[f] == 0:
@@ -149,7 +149,8 @@ def gemm2_call(lib, dtype=0, mode=0, T=4, E=8, k=2, D=128, I=64, B=16, cap=None,
 
 
 def test_gemm2_validation(lib):
-    assert gemm2_call(lib, mode=2) == EINVAL
+    assert gemm2_call(lib, mode=3) == EINVAL
+    assert gemm2_call(lib, mode=-1) == EINVAL
     assert gemm2_call(lib, dtype=-1) == EINVAL
     assert gemm2_call(lib, D=64 + 32) == EUNSUP
     assert gemm2_call(lib, cap=1) == ENOSPC
@@ -162,6 +163,9 @@ def test_gemm2_validation(lib):
 
 def test_finalize_and_forward_validation(lib):
     assert lib.moe_finalize(3, GOOD, 4, 2, 128, GOOD, None) == EINVAL
+    # packed bf16 atomics write out in stage 2: nothing to combine, no pointer is used
+    assert lib.moe_finalize(2, None, 4, 2, 128, None, None) == OK
+    assert lib.moe_finalize(2, None, 4, 2, 100, None, None) == EUNSUP
     assert lib.moe_finalize(0, GOOD, 4, 2, 100, GOOD, None) == EUNSUP
     assert lib.moe_finalize(0, None, 4, 2, 128, GOOD, None) == EINVAL
     assert lib.moe_finalize(1, GOOD, 4, 2, 128, BAD_ALIGN, None) == EINVAL

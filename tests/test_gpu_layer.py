@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from _gpu_helpers import (BF16_COS, BF16_TOL, FP8_TOL, PerExpert, check_a_bf16, check_a_fp8, check_route,
-                          compare_out, host_bits, oracle_route)
+                          compare_out, compare_out_bf16_atomic, host_bits, oracle_route)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,6 +125,20 @@ def test_layer_small_full_compare(T, E, k, D, I, B, dtype, mode):
     check_intermediate(views, ref, dtype, np.arange(T * k))
 
 
+@pytest.mark.parametrize("T,E,k,D,I,B,dtype", SMALL)
+def test_layer_small_atomic_bf16(T, E, k, D, I, B, dtype):
+    """Packed bf16 atomic accumulation into out: within the fp32 modes' bound plus the
+    allowance of the k + 1 bf16 roundings (decode kernels, the tiled prefill kernel's paired
+    epilogue, half chunks)."""
+    inp = synth.small_layer_inputs(T, E, k, D, I, dtype, seed=T + D, w_std=0.05)
+    ref_route = oracle_route(inp["logits"], k, B)
+    ref = oracle_layer(inp, ref_route, dtype)
+    out, views = run_forward(to_cuda(inp), k, B, dtype, "atomic_bf16")
+    assert views["y"] is None
+    compare_out_bf16_atomic(out, ref.out, ref.contrib, np.arange(T), k, BF16_TOL if dtype == "bf16" else FP8_TOL)
+    check_intermediate(views, ref, dtype, np.arange(T * k))
+
+
 @pytest.mark.parametrize("mode", ["atomic", "reduce"])
 @pytest.mark.parametrize("dtype,I", [("bf16", 64), ("fp8", 512)])
 def test_layer_long_expert_run(dtype, I, mode):
@@ -230,3 +244,8 @@ def test_layer_full_size_sampled(name, T, tokens, weights_cache):
         compare_out(out, ref.out, rows, FP8_TOL, None)
     slots = np.concatenate([np.arange(t * wl.topk, (t + 1) * wl.topk) for t in tokens])
     check_intermediate(views, ref, wl.dtype, slots)
+    if name in ("deepseek", "kimi") and T in (16, 16384):
+        # the same inputs with packed bf16 atomics into out
+        out2, _ = run_forward(inp, wl.topk, wl.block_m, wl.dtype, "atomic_bf16")
+        compare_out_bf16_atomic(out2, ref.out, ref.contrib, rows, wl.topk,
+                                BF16_TOL if wl.dtype == "bf16" else FP8_TOL)
