@@ -18,7 +18,7 @@ follows:
 * "[Common] Optimize fused router forward/backward kernels"
   (NVIDIA/TransformerEngine #3012) -- score functions and the host checks.
 * "[RadeonFlow] flydsl mxfp4 a4w4 MoE: bring gemm1/gemm2 to parity with the
-  HIP backend" (ROCm/aiter #3828) -- the Kimi-K2.5 shape.
+  HIP backend" (ROCm/aiter #3828) -- the Kimi-K2.5 shape and the mxfp4 (a4w4) GEMMs.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (brute force, closed forms, invariants, library
@@ -29,9 +29,19 @@ layer, so absolute layer outputs are pinned only through those checks.
 from .codecs import (
     bf16_decode,
     bf16_encode_rne,
+    e2m1_decode,
+    e2m1_encode_rne_sat,
     e4m3_decode,
     e4m3_encode_rne_sat,
+    e8m0_decode,
+    fp4_pack,
+    fp4_unpack,
+    mx_dequantize,
+    mx_quantize,
+    E2M1_MAX,
+    E2M1_TABLE,
     E4M3_MAX,
+    MX_BLOCK,
 )
 from .routing import (
     RouteResult,
@@ -46,9 +56,19 @@ from .layer import LayerResult, moe_layer
 __all__ = [
     "bf16_decode",
     "bf16_encode_rne",
+    "e2m1_decode",
+    "e2m1_encode_rne_sat",
     "e4m3_decode",
     "e4m3_encode_rne_sat",
+    "e8m0_decode",
+    "fp4_pack",
+    "fp4_unpack",
+    "mx_dequantize",
+    "mx_quantize",
+    "E2M1_MAX",
+    "E2M1_TABLE",
     "E4M3_MAX",
+    "MX_BLOCK",
     "RouteResult",
     "route",
     "routing_weights",

@@ -23,6 +23,11 @@ Readings (listed with the design notes):
   row: scale = fp32(amax / 448) (1.0 if the row is all zero), code =
   e4m3_rne_sat(fp32(a / scale)).  This decision is taken in fp32, the
   precision of the kernel that makes it;
+* mxfp4 ("[RadeonFlow] flydsl mxfp4 a4w4 MoE", ROCm/aiter #3828: 4-bit activations
+  and weights in both GEMMs): x, W1 and W2 are MX blocks (E2M1 codes, one E8M0 scale
+  per 32 consecutive elements along K; formats in codecs.py); the bf16 intermediate is
+  requantised to MX blocks of 32 along I before the down GEMM.  The block exponent and
+  codes are exact functions of the bf16 values, so no precision choice enters;
 * the routed weight multiplies the down-projection output before the
   combine; the combined output is kept in float64, unrounded.
 """
@@ -33,7 +38,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .codecs import bf16_decode, bf16_encode_rne, e4m3_decode, e4m3_encode_rne_sat, E4M3_MAX
+from .codecs import (bf16_decode, bf16_encode_rne, e4m3_decode, e4m3_encode_rne_sat, E4M3_MAX,
+                     fp4_unpack, mx_dequantize, mx_quantize)
 
 
 def _silu(z: np.ndarray) -> np.ndarray:
@@ -51,13 +57,20 @@ def requant_rows_fp8(a_bits: np.ndarray):
     return codes, scale, deq
 
 
+def requant_rows_mx(a_bits: np.ndarray):
+    """MX requantisation of bf16 rows in blocks of 32; returns (codes uint8 [n, I], scale
+    codes uint8 [n, I/32], dequantised fp64)."""
+    codes, sc = mx_quantize(bf16_decode(a_bits))
+    return codes, sc, mx_dequantize(codes, sc)
+
+
 @dataclass
 class LayerResult:
     out: np.ndarray       # float64 [T, D]; rows not requested are NaN
     contrib: np.ndarray   # float64 [T*k, D]: routed-weighted down output of each slot
     a_bits: np.ndarray    # uint16 [T*k, I]: bf16 intermediate silu(g)*u (pre-requant)
-    a_codes: np.ndarray | None   # uint8 [T*k, I]: fp8 requantised intermediate
-    a_scale: np.ndarray | None   # float32 [T*k]
+    a_codes: np.ndarray | None   # uint8 [T*k, I]: fp8 codes, or mxfp4 codes (one per byte)
+    a_scale: np.ndarray | None   # float32 [T*k] (fp8), or uint8 E8M0 [T*k, I/32] (mxfp4)
     computed: np.ndarray  # bool [T*k]: slots that were evaluated
 
 
@@ -65,19 +78,21 @@ def moe_layer(x, w1, w2, ids, weights, dtype: str = "bf16", x_scale=None,
               w1_scale=None, w2_scale=None, tokens=None) -> LayerResult:
     """Reference forward of one MoE layer.
 
-    x: bf16 bits uint16 [T, D] (fp8: e4m3 codes uint8 [T, D] with x_scale fp32 [T]).
+    x: bf16 bits uint16 [T, D] (fp8: e4m3 codes uint8 [T, D] with x_scale fp32 [T];
+       mxfp4: packed uint8 [T, D/2] with x_scale uint8 E8M0 [T, D/32]).
     w1: per-expert indexable, w1[e] is [2I, D] (bf16 bits or e4m3 codes with
-        w1_scale[e] fp32 [2I]); w2[e] is [D, I] (with w2_scale[e] fp32 [D]).
+        w1_scale[e] fp32 [2I]; mxfp4: packed [2I, D/2] with scales [2I, D/32]);
+        w2[e] is [D, I] (with w2_scale[e] fp32 [D]; mxfp4: [D, I/2], [D, I/32]).
     ids int32 [T, k], weights fp32 [T, k] from routing.
     tokens: optional iterable of token indices to evaluate (others are NaN);
         only the experts those tokens use are read.
     """
-    if dtype not in ("bf16", "fp8"):
-        raise ValueError("dtype must be 'bf16' or 'fp8'")
+    if dtype not in ("bf16", "fp8", "mxfp4"):
+        raise ValueError("dtype must be 'bf16', 'fp8' or 'mxfp4'")
     ids = np.asarray(ids, dtype=np.int64)
     weights = np.asarray(weights, dtype=np.float32)
     T, k = ids.shape
-    D = np.asarray(x).shape[1]
+    D = np.asarray(x).shape[1] * (2 if dtype == "mxfp4" else 1)
     tok_mask = np.zeros(T, dtype=bool)
     if tokens is None:
         tok_mask[:] = True
@@ -87,11 +102,15 @@ def moe_layer(x, w1, w2, ids, weights, dtype: str = "bf16", x_scale=None,
     def dec_x(rows):
         if dtype == "bf16":
             return bf16_decode(np.asarray(x)[rows])
+        if dtype == "mxfp4":
+            return mx_dequantize(fp4_unpack(np.asarray(x)[rows]), np.asarray(x_scale)[rows])
         return e4m3_decode(np.asarray(x)[rows]) * np.asarray(x_scale, dtype=np.float32)[rows, None].astype(np.float64)
 
     def dec_w(w, scale, e):
         if dtype == "bf16":
             return bf16_decode(np.asarray(w[e]))
+        if dtype == "mxfp4":
+            return mx_dequantize(fp4_unpack(np.asarray(w[e])), np.asarray(scale[e]))
         return e4m3_decode(np.asarray(w[e])) * np.asarray(scale[e], dtype=np.float32)[:, None].astype(np.float64)
 
     flat = ids.reshape(-1)
@@ -116,12 +135,19 @@ def moe_layer(x, w1, w2, ids, weights, dtype: str = "bf16", x_scale=None,
             if dtype == "fp8":
                 a_codes_all = np.zeros((T * k, I), dtype=np.uint8)
                 a_scale_all = np.zeros(T * k, dtype=np.float32)
+            elif dtype == "mxfp4":
+                a_codes_all = np.zeros((T * k, I), dtype=np.uint8)
+                a_scale_all = np.zeros((T * k, I // 32), dtype=np.uint8)
         gu = xh @ W1.T                        # [n, 2I]: gate then up
         g, u = gu[:, :I], gu[:, I:]
         a_bits = bf16_encode_rne(_silu(g) * u)
         a_bits_all[slots] = a_bits
         if dtype == "fp8":
             codes, sc, a_hat = requant_rows_fp8(a_bits)
+            a_codes_all[slots] = codes
+            a_scale_all[slots] = sc
+        elif dtype == "mxfp4":
+            codes, sc, a_hat = requant_rows_mx(a_bits)
             a_codes_all[slots] = codes
             a_scale_all[slots] = sc
         else:

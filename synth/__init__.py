@@ -15,11 +15,16 @@ share on the aiter mxfp4 page):
 * gptoss:   E=128, topk=4, D=I=2880, T=16 (decode) / 4096 (prefill), BLOCK_M=64, bf16, reduce
 * router:   T=8192, E/topk in {512/4, 512/22, 2304/36}, softmax|sigmoid, BLOCK_M=32
 * kimi:     E=385, topk=9, D=7168, I=512, T in {64, 4096, 16384}, BLOCK_M=64, fp8, atomic
+* kimi_mxfp4: the kimi shape with mxfp4 (a4w4) activations and weights
 
 Distributions: router logits fp32 N(0,1); activations N(0,1) (gptoss:
 N(0,0.02)); weights N(0,0.02).  fp8 inputs: activations get one scale per
 token and weights one scale per output channel, scale = amax / 448, values
-cast with torch's e4m3fn conversion of value/scale.
+cast with torch's e4m3fn conversion of value/scale.  mxfp4 inputs are drawn
+directly in their storage format, so no quantisation happens here: every byte
+of the packed E2M1 codes is uniform (two uniform codes), and each block of 32
+elements along K gets an E8M0 exponent uniform in 125..127 for activations
+(rms about 0.7) and 119..121 for weights (rms about 0.02).
 """
 
 from __future__ import annotations
@@ -39,7 +44,7 @@ class Workload:
     D: int
     I: int
     block_m: int
-    dtype: str          # "bf16" | "fp8"
+    dtype: str          # "bf16" | "fp8" | "mxfp4"
     mode: str           # "atomic" | "reduce"
     x_std: float
     w_std: float
@@ -54,7 +59,13 @@ WORKLOADS = {
                        (16, 4096)),
     "kimi": Workload("kimi", 385, 9, 7168, 512, 64, "fp8", "atomic", 1.0, 0.02,
                      (64, 4096, 16384)),
+    "kimi_mxfp4": Workload("kimi_mxfp4", 385, 9, 7168, 512, 64, "mxfp4", "atomic", 1.0, 0.02,
+                           (64, 4096, 16384)),
 }
+
+# E8M0 exponent ranges of the random mxfp4 blocks
+MX_X_EXP = (125, 127)
+MX_W_EXP = (119, 121)
 
 # router-only stress cases: (E, topk); T = 8192, BLOCK_M = 32
 ROUTER_T = 8192
@@ -81,8 +92,20 @@ def _quant_rows_e4m3(v: torch.Tensor):
     return codes.view(torch.uint8), scale
 
 
+def _mx_random(rows: tuple, n: int, exps: tuple, gen: torch.Generator, device):
+    """Random mxfp4 storage: packed codes uint8 [*rows, n/2] and E8M0 exponents uint8
+    [*rows, n/32] uniform in exps (inclusive)."""
+    packed = torch.randint(0, 256, (*rows, n // 2), generator=gen, dtype=torch.uint8, device=device)
+    scale = torch.randint(exps[0], exps[1] + 1, (*rows, n // 32), generator=gen, dtype=torch.uint8, device=device)
+    return packed, scale
+
+
 def activations(T: int, D: int, dtype: str, seed: int = 0, x_std: float = 1.0) -> dict:
-    """Token activations on the CPU: {"x": bf16 [T,D]} or {"x": uint8 e4m3 [T,D], "x_scale": fp32 [T]}."""
+    """Token activations on the CPU: {"x": bf16 [T,D]}, {"x": uint8 e4m3 [T,D], "x_scale": fp32 [T]}
+    or mxfp4 {"x": packed uint8 [T, D/2], "x_scale": uint8 E8M0 [T, D/32]}."""
+    if dtype == "mxfp4":
+        xp, xs = _mx_random((T,), D, MX_X_EXP, _gen(seed + 2, "cpu"), "cpu")
+        return {"x": xp, "x_scale": xs}
     x32 = torch.randn(T, D, generator=_gen(seed + 2, "cpu"), dtype=torch.float32) * x_std
     if dtype == "bf16":
         return {"x": x32.to(torch.bfloat16)}
@@ -95,10 +118,26 @@ def layer_inputs(wl: Workload, T: int, seed: int = 0, device="cpu") -> dict:
 
     Returns a dict with logits fp32 [T,E] (on `device`), x ([T,D] bf16, or
     uint8 e4m3 codes + x_scale fp32 [T]), w1 [E,2I,D], w2 [E,D,I] (bf16, or
-    uint8 codes + w1_scale [E,2I] / w2_scale [E,D]).
+    uint8 codes + w1_scale [E,2I] / w2_scale [E,D]).  mxfp4: x packed [T, D/2] +
+    x_scale [T, D/32], w1 [E, 2I, D/2] + w1_scale [E, 2I, D/32], w2 [E, D, I/2] +
+    w2_scale [E, D, I/32] (uint8 throughout).
     """
     E, D, I = wl.E, wl.D, wl.I
     lg = logits(T, E, seed)
+    if wl.dtype == "mxfp4":
+        out = {"logits": lg.to(device)}
+        xp, xs = _mx_random((T,), D, MX_X_EXP, _gen(seed + 2, "cpu"), "cpu")
+        out["x"], out["x_scale"] = xp.to(device), xs.to(device)
+        gw = _gen(seed + 1, device)
+        w1 = torch.empty(E, 2 * I, D // 2, dtype=torch.uint8, device=device)
+        w2 = torch.empty(E, D, I // 2, dtype=torch.uint8, device=device)
+        w1s = torch.empty(E, 2 * I, D // 32, dtype=torch.uint8, device=device)
+        w2s = torch.empty(E, D, I // 32, dtype=torch.uint8, device=device)
+        for e in range(E):
+            w1[e], w1s[e] = _mx_random((2 * I,), D, MX_W_EXP, gw, device)
+            w2[e], w2s[e] = _mx_random((D,), I, MX_W_EXP, gw, device)
+        out.update(w1=w1, w2=w2, w1_scale=w1s, w2_scale=w2s)
+        return out
     gx = _gen(seed + 2, "cpu")
     x32 = torch.randn(T, D, generator=gx, dtype=torch.float32) * wl.x_std
     gw = _gen(seed + 1, device)

@@ -25,18 +25,46 @@ def bf16_round_torch(v: float) -> float:
     return float(torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).float())
 
 
+FP4_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # E2M1 magnitudes (MX format)
+
+
+def fp4_value(byte_row, i):
+    """Element i of a packed row (element 2j in the low nibble)."""
+    code = (byte_row[i // 2] >> (4 * (i % 2))) & 0xF
+    return -FP4_VALUES[code & 7] if code & 8 else FP4_VALUES[code & 7]
+
+
+def mx_round_block(vals):
+    """One MX block of 32 values: scale 2**(floor(log2 amax) - 2), elements to the nearest
+    E2M1 magnitude (ties to the even code), clamped at 6; returns the dequantised values."""
+    amax = max(abs(v) for v in vals)
+    if amax == 0:
+        return [0.0] * len(vals)
+    scale = 2.0 ** (math.frexp(amax)[1] - 1 - 2)
+    out = []
+    for v in vals:
+        y = min(abs(v) / scale, 6.0)
+        best = min(range(8), key=lambda c: (abs(y - FP4_VALUES[c]), c % 2))
+        out.append(math.copysign(FP4_VALUES[best], v) * scale)
+    return out
+
+
 def brute_layer(x, w1, w2, ids, wts, dtype="bf16", xs=None, w1s=None, w2s=None):
     """Pure-Python loops over tokens, slots, channels; rounding by torch's casts."""
     T, k = ids.shape
-    D = len(x[0])
+    D = len(x[0]) * (2 if dtype == "mxfp4" else 1)
     I = len(w1[0]) // 2
 
     def xv(t, d):
+        if dtype == "mxfp4":
+            return fp4_value(x[t], d) * 2.0 ** (int(xs[t][d // 32]) - 127)
         if dtype == "bf16":
             return float(torch.tensor(int(x[t][d]), dtype=torch.int32).to(torch.int16).view(torch.bfloat16))
         return float(torch.tensor(int(x[t][d]), dtype=torch.uint8).view(torch.float8_e4m3fn)) * float(xs[t])
 
     def wv(w, s, e, r, c):
+        if dtype == "mxfp4":
+            return fp4_value(w[e][r], c) * 2.0 ** (int(s[e][r][c // 32]) - 127)
         if dtype == "bf16":
             return float(torch.tensor(int(w[e][r][c]), dtype=torch.int32).to(torch.int16).view(torch.bfloat16))
         return float(torch.tensor(int(w[e][r][c]), dtype=torch.uint8).view(torch.float8_e4m3fn)) * float(s[e][r])
@@ -56,16 +84,19 @@ def brute_layer(x, w1, w2, ids, wts, dtype="bf16", xs=None, w1s=None, w2s=None):
                 q = torch.tensor([v / sc for v in a], dtype=torch.float32)
                 q = (q.float() / 1.0).to(torch.float8_e4m3fn).float().tolist()
                 a = [v * sc for v in q]
+            if dtype == "mxfp4":
+                a = [v for b in range(0, I, 32) for v in mx_round_block(a[b:b + 32])]
             for d in range(D):
                 y = sum(wv(w2, w2s, e, d, n) * a[n] for n in range(I))
                 out[t][d] += float(wts[t][j]) * y
     return np.array(out)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("seed", [0, 1])
 def test_brute_force_tiny(dtype, seed):
-    T, E, k, D, I = 3, 4, 2, 8, 4
+    # MX blocks need multiples of 32 along K
+    T, E, k, D, I = (3, 4, 2, 8, 4) if dtype != "mxfp4" else (3, 4, 2, 64, 32)
     inp = np_inputs(synth.small_layer_inputs(T, E, k, D, I, dtype, seed=seed, w_std=0.3))
     r = route(inp["logits"], k, 16)
     ref = moe_layer(inp["x"], inp["w1"], inp["w2"], r.ids, r.weights, dtype,
