@@ -11,7 +11,7 @@ The JSON line also carries the roofline of the dominant kernel (HIP events on th
 stream it runs on), the CPU oracle's time on a bounded sample, and (unless
 --headline-only) secondary lines: GPT-OSS decode/prefill and Kimi fp8 layer times
 with per-GEMM TFLOPS, the DeepSeek and Kimi layers again with packed bf16 atomics into
-the output, and router-only GB/s at T=8192.
+the output, the Kimi shape in mxfp4 (a4w4), and router-only GB/s at T=8192.
 """
 
 from __future__ import annotations
@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0                                # MI355X HBM3E
 # fp32 atomic adds to HBM-resident memory, measured on MI355X with a plain atomic-add stream
 # (0.32-0.34 G adds/ms whatever the lane pattern or occupancy): the floor of atomic mode
 ATOMIC_ADDS_PER_S = 3.3e11
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}   # dense
 
 
 def parse():
@@ -93,10 +93,12 @@ def algorithmic(wl, T, n_act, num_valid):
     """Bytes and FLOPs the method must move/compute (padding, fp32 accumulator traffic,
     weight re-reads and atomic read-modify-writes excluded)."""
     E, k, D, I, B = wl.E, wl.topk, wl.D, wl.I, wl.block_m
-    bw = 2 if wl.dtype == "bf16" else 1
+
+    def nbytes(elems):  # storage of `elems` values; mxfp4: half a byte + one scale byte per 32
+        return elems * 2 if wl.dtype == "bf16" else elems if wl.dtype == "fp8" else elems * 17 // 32
     route = 4 * T * E + 8 * T * k + 4 * num_valid + 4 * (num_valid // B) + 4
-    g1 = n_act * 2 * I * D * bw + T * D * bw + T * k * I * bw
-    g2 = n_act * D * I * bw + T * k * I * bw + 4 * T * k + 2 * T * D
+    g1 = nbytes(n_act * 2 * I * D) + nbytes(T * D) + nbytes(T * k * I)
+    g2 = nbytes(n_act * D * I) + nbytes(T * k * I) + 4 * T * k + 2 * T * D
     if wl.dtype == "fp8":
         g1 += n_act * 2 * I * 4 + 4 * T + 4 * T * k
         g2 += n_act * D * 4 + 4 * T * k
@@ -409,7 +411,9 @@ def main():
     if not args.headline_only:
         for name, T, mode in (("gptoss", 16, None), ("gptoss", 4096, None), ("kimi", 64, None),
                               ("kimi", 4096, None), ("kimi", 16384, None), ("deepseek", 16, "atomic_bf16"),
-                              ("kimi", 4096, "atomic_bf16"), ("kimi", 16384, "atomic_bf16")):
+                              ("kimi", 4096, "atomic_bf16"), ("kimi", 16384, "atomic_bf16"),
+                              ("kimi_mxfp4", 64, None), ("kimi_mxfp4", 4096, None),
+                              ("kimi_mxfp4", 16384, None)):
             r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2, mode)
             del kp
             torch.cuda.empty_cache()

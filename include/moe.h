@@ -50,12 +50,13 @@ enum moe_status {
   MOE_EINVAL = -1,        /* bad enum, null or misaligned pointer, topk not in [1,E], T < 0 */
   MOE_ERANGE = -2,        /* T*E (or a derived size) does not fit a signed 32-bit int ([P3] "Hardening") */
   MOE_ENOSPC = -3,        /* sorted_cap or ws_bytes smaller than required */
-  MOE_EUNSUPPORTED = -4,  /* E > 8160, block_m not in {16,32,64}, D or I not a positive multiple of 64 */
+  MOE_EUNSUPPORTED = -4,  /* E > 8160, block_m not in {16,32,64}, D or I not a positive multiple of 64
+                             (of 128 for MOE_MXFP4) */
   MOE_ELAUNCH = -5        /* a kernel launch failed (hipGetLastError) */
 };
 
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
-enum moe_dtype { MOE_BF16 = 0, MOE_FP8_E4M3 = 1 };
+enum moe_dtype { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_MXFP4 = 2 };
 enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1, MOE_OUT_ATOMIC_BF16 = 2 };
 
 /* Largest E accepted ([P3] "Hardening": the radix top-k path's 8160-expert bound). */
@@ -73,8 +74,8 @@ int64_t moe_sorted_capacity(int T, int E, int topk, int block_m);
  * the single-workgroup path).  Negative moe_status on invalid arguments. */
 int64_t moe_route_workspace_bytes(int T, int E, int topk, int block_m);
 
-/* Workspace bytes moe_gemm1_gateup needs: 0 for bf16; for fp8 the bf16
- * intermediate rows [T*k, I] that are requantised per row. */
+/* Workspace bytes moe_gemm1_gateup needs: 0 for bf16; for fp8 and mxfp4 the bf16
+ * intermediate rows [T*k, I] that are requantised. */
 int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I);
 
 /* moe_forward's workspace: the routing outputs, the intermediate and the fp32
@@ -84,8 +85,9 @@ int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I);
  *   0 topk_weights fp32 [T,k]      1 topk_ids int32 [T,k]
  *   2 sorted_token_ids int32 [cap] 3 expert_ids int32 [cap/B]
  *   4 num_valid int32 [1]          5 routing scratch
- *   6 a: bf16 [T*k,I] or e4m3 [T*k,I]
- *   7 a_scale fp32 [T*k] (fp8)     8 gemm1 scratch (fp8: bf16 [T*k,I])
+ *   6 a: bf16 [T*k,I], e4m3 [T*k,I] or packed mxfp4 [T*k,I/2]
+ *   7 a_scale: fp32 [T*k] (fp8), E8M0 uint8 [T*k,I/32] (mxfp4)
+ *   8 gemm1 scratch (fp8, mxfp4: bf16 [T*k,I])
  *   9 y: ATOMIC fp32 [T,D] accumulator, REDUCE fp32 [T*k,D] slot rows
  *        (ATOMIC_BF16: unused, -1; the stage-2 atomics add into out itself)
  * Returns the total size in bytes, or a negative moe_status. */
@@ -142,16 +144,24 @@ int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score
  * the bf16 row a[s,:] is then requantised: a_scale[s] = amax_n|a[s,n]| / 448
  * (1.0 for an all-zero row), codes = e4m3_rne(a / a_scale[s]) clamped to +-448.
  *
- *   x         bf16 [T, D] | e4m3 [T, D]      x_scale  fp32 [T] (fp8 only, else NULL)
- *   w1        bf16 [E, 2I, D] | e4m3         w1_scale fp32 [E, 2I] (fp8 only)
+ * mxfp4 ([P4] "Summary": 4-bit activations and weights, "a4w4"; the format is the OCP
+ * Microscaling one): x, W1 (and W2, a) hold E2M1 codes two per byte, element 2j in the
+ * low nibble, with one E8M0 scale 2^(s-127) per block of 32 consecutive elements along K;
+ * the bf16 row a[s,:] is requantised block by block: scale 2^(floor(log2 amax) - 2) (2^0
+ * for an all-zero block), codes = E2M1 round-to-nearest-even of a/scale, saturating at 6.
+ *
+ *   x         bf16 [T, D] | e4m3 [T, D] | mxfp4 uint8 [T, D/2]
+ *   x_scale   fp32 [T] (fp8) | E8M0 uint8 [T, D/32] (mxfp4) | NULL (bf16)
+ *   w1        bf16 [E, 2I, D] | e4m3 | mxfp4 uint8 [E, 2I, D/2]
+ *   w1_scale  fp32 [E, 2I] (fp8) | E8M0 uint8 [E, 2I, D/32] (mxfp4)
  *   sorted_token_ids, expert_ids, num_valid: as written by moe_topk_softmax_sort
- *   a         bf16 [T*k, I] | e4m3 [T*k, I]  out (every slot row is written)
- *   a_scale   fp32 [T*k] (fp8 only)           out
- *   workspace moe_gemm1_workspace_bytes(...) bytes (fp8), else may be NULL */
-int moe_gemm1_gateup(int dtype, const void* x, const float* x_scale, const void* w1,
-                     const float* w1_scale, const int32_t* sorted_token_ids,
+ *   a         bf16 [T*k, I] | e4m3 [T*k, I] | mxfp4 uint8 [T*k, I/2]   out (every slot row)
+ *   a_scale   fp32 [T*k] (fp8) | E8M0 uint8 [T*k, I/32] (mxfp4)         out
+ *   workspace moe_gemm1_workspace_bytes(...) bytes (fp8, mxfp4), else may be NULL */
+int moe_gemm1_gateup(int dtype, const void* x, const void* x_scale, const void* w1,
+                     const void* w1_scale, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int64_t sorted_cap,
-                     int T, int E, int topk, int D, int I, int block_m, void* a, float* a_scale,
+                     int T, int E, int topk, int D, int I, int block_m, void* a, void* a_scale,
                      void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- stage 2
@@ -173,11 +183,14 @@ int moe_gemm1_gateup(int dtype, const void* x, const float* x_scale, const void*
  *                depends on the order of the k adds, and beyond ATOMIC's rounding it may
  *                differ from the exact sum by up to (k+1) * 2^-9 * sum_j |c_{t*k+j}[d]|.)
  *
+ *   mxfp4: the block scales of a and W2 enter the products; no per-row factors.
+ *
  *   a, a_scale        as written by moe_gemm1_gateup
- *   w2                bf16 [E, D, I] | e4m3 [E, D, I]   w2_scale fp32 [E, D] (fp8 only)
+ *   w2                bf16 [E, D, I] | e4m3 [E, D, I] | mxfp4 uint8 [E, D, I/2]
+ *   w2_scale          fp32 [E, D] (fp8) | E8M0 uint8 [E, D, I/32] (mxfp4)
  *   topk_weights      fp32 [T, k] */
-int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w2,
-                   const float* w2_scale, const float* topk_weights,
+int moe_gemm2_down(int dtype, const void* a, const void* a_scale, const void* w2,
+                   const void* w2_scale, const float* topk_weights,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
                    const int32_t* num_valid, int64_t sorted_cap, int T, int E, int topk, int D,
                    int I, int block_m, int mode, void* y, void* stream);
@@ -196,8 +209,8 @@ int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out
  * intermediate in `workspace` at the offsets moe_forward_workspace_layout reports (so
  * they can be read back).  out bf16 [T, D]. */
 int moe_forward(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
-                const float* x_scale, const void* w1, const float* w1_scale, const void* w2,
-                const float* w2_scale, int T, int E, int topk, int D, int I, int block_m,
+                const void* x_scale, const void* w1, const void* w1_scale, const void* w2,
+                const void* w2_scale, int T, int E, int topk, int D, int I, int block_m,
                 void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
 
 #ifdef __cplusplus

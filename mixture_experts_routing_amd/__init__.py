@@ -36,7 +36,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 SCORE = {"softmax": 0, "sigmoid": 1}
-DTYPE = {"bf16": 0, "fp8": 1}
+DTYPE = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 MODE = {"atomic": 0, "reduce": 1, "atomic_bf16": 2}
 WS_FIELDS = ("topk_weights", "topk_ids", "sorted_token_ids", "expert_ids", "num_valid",
              "route_scratch", "a", "a_scale", "gemm1_scratch", "y")
@@ -156,16 +156,22 @@ def moe_topk_softmax_sort(logits: torch.Tensor, topk: int, block_m: int, score: 
 
 def moe_gemm1_gateup(dtype: str, x, w1, route: dict, topk: int, block_m: int, x_scale=None,
                      w1_scale=None, a=None, a_scale=None, workspace=None, stream=None):
-    """Stage 1: returns (a, a_scale); a is bf16 [T*k, I] (fp8: uint8 e4m3 codes + fp32 scales)."""
+    """Stage 1: returns (a, a_scale); a is bf16 [T*k, I] (fp8: uint8 e4m3 codes + fp32 scales;
+    mxfp4: packed uint8 [T*k, I/2] + E8M0 uint8 [T*k, I/32])."""
     T, D = x.shape
     E, twoI, _ = w1.shape
     I = twoI // 2
+    if dtype == "mxfp4":
+        D *= 2
     dev = x.device
     if a is None:
-        a = torch.empty(T * topk, I, dtype=torch.bfloat16 if dtype == "bf16" else torch.uint8, device=dev)
+        shape = (T * topk, I // 2) if dtype == "mxfp4" else (T * topk, I)
+        a = torch.empty(*shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.uint8, device=dev)
     if dtype == "fp8" and a_scale is None:
         a_scale = torch.empty(T * topk, dtype=torch.float32, device=dev)
-    if workspace is None and dtype == "fp8":
+    if dtype == "mxfp4" and a_scale is None:
+        a_scale = torch.empty(T * topk, I // 32, dtype=torch.uint8, device=dev)
+    if workspace is None and dtype in ("fp8", "mxfp4"):
         workspace = torch.empty(max(moe_gemm1_workspace_bytes(dtype, T, topk, I), 1), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sid = route["sorted_token_ids"]
@@ -181,6 +187,8 @@ def moe_gemm2_down(dtype: str, a, w2, route: dict, T: int, topk: int, block_m: i
     """Stage 2: returns y (ATOMIC: fp32 [T, D] accumulated into; REDUCE: fp32 [T*k, D];
     ATOMIC_BF16: bf16 [T, D] accumulated into)."""
     E, D, I = w2.shape
+    if dtype == "mxfp4":
+        I *= 2
     dev = a.device
     if y is None:
         if mode == "atomic_bf16":
@@ -212,6 +220,8 @@ def moe_forward(dtype: str, logits, x, w1, w2, topk: int, block_m: int, mode: st
     T, D = x.shape
     E, twoI, _ = w1.shape
     I = twoI // 2
+    if dtype == "mxfp4":
+        D *= 2
     total, offs = moe_forward_workspace_layout(dtype, mode, T, E, topk, D, I, block_m)
     dev = x.device
     if workspace is None:
@@ -244,8 +254,10 @@ def workspace_views(workspace, offs: dict, dtype: str, mode: str, T: int, E: int
         "sorted_token_ids": view("sorted_token_ids", cap, torch.int32, (cap,)),
         "expert_ids": view("expert_ids", cap // block_m, torch.int32, (cap // block_m,)),
         "num_valid": view("num_valid", 1, torch.int32, (1,)),
-        "a": view("a", n * I, torch.bfloat16 if dtype == "bf16" else torch.uint8, (n, I)),
-        "a_scale": view("a_scale", n, torch.float32, (n,)),
+        "a": (view("a", n * I // 2, torch.uint8, (n, I // 2)) if dtype == "mxfp4" else
+              view("a", n * I, torch.bfloat16 if dtype == "bf16" else torch.uint8, (n, I))),
+        "a_scale": (view("a_scale", n * I // 32, torch.uint8, (n, I // 32)) if dtype == "mxfp4" else
+                    view("a_scale", n, torch.float32, (n,))),
         "a_pre": view("gemm1_scratch", n * I, torch.bfloat16, (n, I)),
     }
     rows = T if mode == "atomic" else n

@@ -26,11 +26,15 @@ int check_route_dims(int T, int E, int topk, int block_m) {
   return MOE_OK;
 }
 
+bool quantised(int dtype) { return dtype == MOE_FP8_E4M3 || dtype == MOE_MXFP4; }
+
 int check_layer_dims(int dtype, int T, int E, int topk, int D, int I, int block_m) {
-  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_EINVAL;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3 && dtype != MOE_MXFP4) return MOE_EINVAL;
   int st = check_route_dims(T, E, topk, block_m);
   if (st) return st;
   if (D < 64 || I < 64 || D % 64 || I % 64) return MOE_EUNSUPPORTED;
+  // mxfp4: whole 16x16x128 MFMAs along K (two per 128-byte chunk)
+  if (dtype == MOE_MXFP4 && (D % 128 || I % 128)) return MOE_EUNSUPPORTED;
   const int64_t eb = dtype == MOE_BF16 ? 2 : 1;
   // row offsets inside the kernels are 32-bit per slot row; element counts are 64-bit
   if ((int64_t)T * topk * I > INT_MAX || (int64_t)T * topk * D > INT_MAX) return MOE_ERANGE;
@@ -66,9 +70,12 @@ Layout forward_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
   const int64_t rws = moe::route_workspace_bytes(T, E, topk);
   if (rws > 0) take(5, rws);
   else L.off[5] = -1;
-  take(6, n * I * (dtype == MOE_BF16 ? 2 : 1));
+  take(6, dtype == MOE_BF16 ? n * I * 2 : dtype == MOE_FP8_E4M3 ? n * I : n * I / 2);
   if (dtype == MOE_FP8_E4M3) {
     take(7, n * 4);
+    take(8, n * I * 2);
+  } else if (dtype == MOE_MXFP4) {
+    take(7, n * I / 32);
     take(8, n * I * 2);
   } else {
     L.off[7] = -1;
@@ -109,10 +116,10 @@ int64_t moe_route_workspace_bytes(int T, int E, int topk, int block_m) {
 }
 
 int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I) {
-  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_EINVAL;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3 && dtype != MOE_MXFP4) return MOE_EINVAL;
   if (T < 0 || topk < 1 || I < 64 || I % 64) return MOE_EINVAL;
   if (dtype == MOE_BF16) return 0;
-  return (int64_t)T * topk * I * 2;
+  return (int64_t)T * topk * I * 2;  // the bf16 rows before the requant
 }
 
 int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
@@ -161,30 +168,29 @@ static int check_gemm_common(int dtype, int T, int E, int topk, int D, int I, in
   return MOE_OK;
 }
 
-int moe_gemm1_gateup(int dtype, const void* x, const float* x_scale, const void* w1,
-                     const float* w1_scale, const int32_t* sorted_token_ids,
+int moe_gemm1_gateup(int dtype, const void* x, const void* x_scale, const void* w1,
+                     const void* w1_scale, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int64_t sorted_cap,
-                     int T, int E, int topk, int D, int I, int block_m, void* a, float* a_scale,
+                     int T, int E, int topk, int D, int I, int block_m, void* a, void* a_scale,
                      void* workspace, size_t ws_bytes, void* stream) {
   int st = check_gemm_common(dtype, T, E, topk, D, I, block_m, sorted_cap, sorted_token_ids,
                              expert_ids, num_valid);
   if (st) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(a)) return MOE_EINVAL;
-  const bool fp8 = dtype == MOE_FP8_E4M3;
-  if (fp8) {
+  if (quantised(dtype)) {
     if (!ok_ptr(x_scale) || !ok_ptr(w1_scale) || !ok_ptr(a_scale)) return MOE_EINVAL;
     if ((int64_t)ws_bytes < moe_gemm1_workspace_bytes(dtype, T, topk, I)) return MOE_ENOSPC;
     if (!ok_ptr(workspace)) return MOE_EINVAL;
   }
   const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
-  return launch_status(moe::launch_gemm1(fp8, x, x_scale, w1, w1_scale, sorted_token_ids,
+  return launch_status(moe::launch_gemm1(dtype, x, x_scale, w1, w1_scale, sorted_token_ids,
                                          expert_ids, num_valid, cap, T, E, topk, D, I, block_m, a,
                                          a_scale, workspace, nullptr, 0, (hipStream_t)stream));
 }
 
-int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w2,
-                   const float* w2_scale, const float* topk_weights,
+int moe_gemm2_down(int dtype, const void* a, const void* a_scale, const void* w2,
+                   const void* w2_scale, const float* topk_weights,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
                    const int32_t* num_valid, int64_t sorted_cap, int T, int E, int topk, int D,
                    int I, int block_m, int mode, void* y, void* stream) {
@@ -194,10 +200,9 @@ int moe_gemm2_down(int dtype, const void* a, const float* a_scale, const void* w
   if (st) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(a) || !ok_ptr(w2) || !ok_ptr(topk_weights) || !ok_ptr(y)) return MOE_EINVAL;
-  const bool fp8 = dtype == MOE_FP8_E4M3;
-  if (fp8 && (!ok_ptr(a_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
+  if (quantised(dtype) && (!ok_ptr(a_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
   const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
-  return launch_status(moe::launch_gemm2(fp8, a, a_scale, w2, w2_scale, topk_weights,
+  return launch_status(moe::launch_gemm2(dtype, a, a_scale, w2, w2_scale, topk_weights,
                                          sorted_token_ids, expert_ids, num_valid, cap, T, E, topk,
                                          D, I, block_m, mode, y, (hipStream_t)stream));
 }
@@ -212,8 +217,8 @@ int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out
 }
 
 int moe_forward(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
-                const float* x_scale, const void* w1, const float* w1_scale, const void* w2,
-                const float* w2_scale, int T, int E, int topk, int D, int I, int block_m,
+                const void* x_scale, const void* w1, const void* w1_scale, const void* w2,
+                const void* w2_scale, int T, int E, int topk, int D, int I, int block_m,
                 void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
   if (!ok_mode(mode)) return MOE_EINVAL;
   if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
@@ -221,11 +226,10 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
   if (st) return st;
   if (T == 0) return MOE_OK;
-  const bool fp8 = dtype == MOE_FP8_E4M3;
   if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(w2) || !ok_ptr(out) ||
       !ok_ptr(workspace))
     return MOE_EINVAL;
-  if (fp8 && (!ok_ptr(x_scale) || !ok_ptr(w1_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
+  if (quantised(dtype) && (!ok_ptr(x_scale) || !ok_ptr(w1_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
   const Layout L = forward_layout(dtype, mode, T, E, topk, D, I, block_m);
   if ((int64_t)ws_bytes < L.total) return MOE_ENOSPC;
 
@@ -238,7 +242,7 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   int32_t* nvalid = static_cast<int32_t*>(at(4));
   void* rws = at(5);
   void* a = at(6);
-  float* a_scale = static_cast<float*>(at(7));
+  void* a_scale = at(7);
   void* g1ws = at(8);
   float* y = static_cast<float*>(at(9));
   // ATOMIC clears the fp32 accumulator, ATOMIC_BF16 the bf16 output (T*D/2 floats' worth)
@@ -252,10 +256,10 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   hipError_t e = moe::launch_route(logits, T, E, topk, score, renorm, block_m, topk_w, topk_ids, sorted,
                           cap, eids, nvalid, rws, s);
   if (e == hipSuccess)
-    e = moe::launch_gemm1(fp8, x, x_scale, w1, w1_scale, sorted, eids, nvalid, cap, T, E, topk,
+    e = moe::launch_gemm1(dtype, x, x_scale, w1, w1_scale, sorted, eids, nvalid, cap, T, E, topk,
                           D, I, block_m, a, a_scale, g1ws, zero, zero_n, s);
   if (e == hipSuccess)
-    e = moe::launch_gemm2(fp8, a, a_scale, w2, w2_scale, topk_w, sorted, eids, nvalid, cap, T,
+    e = moe::launch_gemm2(dtype, a, a_scale, w2, w2_scale, topk_w, sorted, eids, nvalid, cap, T,
                           E, topk, D, I, block_m, mode, y2, s);
   if (e == hipSuccess) e = moe::launch_finalize(mode, y, T, topk, D, out, s);
   return launch_status(e);

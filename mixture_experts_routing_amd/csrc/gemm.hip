@@ -110,22 +110,54 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t& acc, const i32x4_t (&a)[2], 
   }
 }
 
+// Element types of the GEMM operands (moe_dtype).
+enum { DT_BF16 = 0, DT_FP8 = 1, DT_FP4 = 2 };
+
+// MXFP4 chunk (128 bytes = 256 E2M1 elements per row): two 16x16x128 MFMAs in format 4
+// (FP4 E2M1).  Lane (i, g) holds bytes [16g, 16g+16) of row i for the first and
+// [64+16g, 64+16g+16) for the second: 32 elements each, exactly one MX block, whose E8M0
+// scale the lane supplies (sa*, sb* in the low byte).  The MFMA reads four registers per
+// operand in this format; the upper four are left undefined.
+__device__ __forceinline__ void mfma_fp4(f32x4_t& acc, const i32x4_t (&a)[2], const i32x4_t (&b)[2],
+                                         int sa0, int sa1, int sb0, int sb1) {
+  const i32x8_t a0 = __builtin_shufflevector(a[0], a[0], 0, 1, 2, 3, -1, -1, -1, -1);
+  const i32x8_t b0 = __builtin_shufflevector(b[0], b[0], 0, 1, 2, 3, -1, -1, -1, -1);
+  const i32x8_t a1 = __builtin_shufflevector(a[1], a[1], 0, 1, 2, 3, -1, -1, -1, -1);
+  const i32x8_t b1 = __builtin_shufflevector(b[1], b[1], 0, 1, 2, 3, -1, -1, -1, -1);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b0, acc, 4, 4, 0, sa0, 0, sb0);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b1, acc, 4, 4, 0, sa1, 0, sb1);
+}
+
 // Streams the byte range [kb0, kb1) of K (rows are kbytes long; kb0, kb1 multiples of
 // 128) for NG weight-row groups against NT gathered activation tiles.  wrow[ng]: this
 // lane's weight row; xrow[tt]: this lane's activation row (nullptr = padding row,
 // contributes zero).  Within a 128-byte chunk, lane group g takes bytes [16g, 16g+16)
 // and [64+16g, 64+16g+16), so each load instruction covers 64 contiguous bytes per row.
-// The last chunk of an fp8 row may be half (64 bytes); its second half reads as zero.
-template <bool FP8, int NG, int NT, int U>
+// The last chunk of an fp8 (fp4) row may be half: 64 bytes; its second half reads as zero.
+// FP4: wsc / xsc point at the rows' E8M0 scales (8 per chunk); lane group g takes the
+// scales of blocks g and 4 + g of each chunk (a padding row takes 2^0).
+template <int DT, int NG, int NT, int U>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
-                                         const uint8_t* const (&xrow)[NT], int kb0, int kb1,
+                                         const uint8_t* const (&xrow)[NT],
+                                         const uint8_t* const (&wsc)[NG],
+                                         const uint8_t* const (&xsc)[NT], int kb0, int kb1,
                                          int kbytes, f32x4_t (&acc)[NG][NT]) {
-  const int g16 = (lane_id() >> 4) * 16;
+  constexpr bool FP4 = DT == DT_FP4;
+  const int g = lane_id() >> 4, g16 = g * 16;
   const i32x4_t zero = {0, 0, 0, 0};
+  // scale bytes of chunk kb for blocks (g, 4 + g); a half chunk has no second block
+  auto scales = [&](const uint8_t* r, int kb, bool in1, int& s0, int& s1) {
+    s0 = s1 = 127;
+    if (r) {
+      s0 = (int)((*reinterpret_cast<const uint32_t*>(r + kb / 16) >> (8 * g)) & 0xFFu);
+      if (in1) s1 = (int)((*reinterpret_cast<const uint32_t*>(r + kb / 16 + 4) >> (8 * g)) & 0xFFu);
+    }
+  };
   int kb = kb0;
   const int kend_full = kb1 < (kbytes & ~127) ? kb1 : (kbytes & ~127);
   for (; kb + 128 * U <= kend_full; kb += 128 * U) {
     i32x4_t wa[U][NG][2], xb[U][NT][2];
+    int wsa[U][NG][2], xsa[U][NT][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int off = kb + 128 * u + g16;
@@ -133,11 +165,13 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
       for (int ng = 0; ng < NG; ++ng) {
         wa[u][ng][0] = ld16(wrow[ng] + off);
         wa[u][ng][1] = ld16(wrow[ng] + off + 64);
+        if constexpr (FP4) scales(wsc[ng], kb + 128 * u, true, wsa[u][ng][0], wsa[u][ng][1]);
       }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         xb[u][tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
         xb[u][tt][1] = xrow[tt] ? ld16(xrow[tt] + off + 64) : zero;
+        if constexpr (FP4) scales(xsc[tt], kb + 128 * u, true, xsa[u][tt][0], xsa[u][tt][1]);
       }
     }
 #pragma unroll
@@ -145,26 +179,39 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) mfma_chunk<FP8>(acc[ng][tt], wa[u][ng], xb[u][tt]);
+        for (int tt = 0; tt < NT; ++tt) {
+          if constexpr (FP4)
+            mfma_fp4(acc[ng][tt], wa[u][ng], xb[u][tt], wsa[u][ng][0], wsa[u][ng][1], xsa[u][tt][0], xsa[u][tt][1]);
+          else
+            mfma_chunk<DT == DT_FP8>(acc[ng][tt], wa[u][ng], xb[u][tt]);
+        }
   }
   for (; kb < kb1 && kb < kbytes; kb += 128) {
     const int off = kb + g16;
     const bool in1 = kb + 64 < kbytes;
     i32x4_t wa[NG][2], xb[NT][2];
+    int wsa[NG][2], xsa[NT][2];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
       wa[ng][0] = ld16(wrow[ng] + off);
       wa[ng][1] = in1 ? ld16(wrow[ng] + off + 64) : zero;
+      if constexpr (FP4) scales(wsc[ng], kb, in1, wsa[ng][0], wsa[ng][1]);
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       xb[tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
       xb[tt][1] = (in1 && xrow[tt]) ? ld16(xrow[tt] + off + 64) : zero;
+      if constexpr (FP4) scales(xsc[tt], kb, in1, xsa[tt][0], xsa[tt][1]);
     }
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) mfma_chunk<FP8>(acc[ng][tt], wa[ng], xb[tt]);
+      for (int tt = 0; tt < NT; ++tt) {
+        if constexpr (FP4)
+          mfma_fp4(acc[ng][tt], wa[ng], xb[tt], wsa[ng][0], wsa[ng][1], xsa[tt][0], xsa[tt][1]);
+        else
+          mfma_chunk<DT == DT_FP8>(acc[ng][tt], wa[ng], xb[tt]);
+      }
   }
 }
 
@@ -209,16 +256,18 @@ __device__ __forceinline__ bool reduce_k_split(f32x4_t (&acc)[NG][NT], int rg, i
 // row blocks (see block_tile).  Output: bf16 rows a[s, I] (for fp8 the pre-requant
 // rows).  If zero_y is set, the blocks first clear that fp32 buffer (stage 2's
 // accumulator), which saves a launch.
-template <int BM, bool FP8, int U, int KS>
+template <int BM, int DT, int U, int KS>
 __global__ void __launch_bounds__(256) gemm1_kernel(
-    const uint8_t* __restrict__ x, const float* __restrict__ x_scale,
-    const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale,
+    const uint8_t* __restrict__ x, const void* __restrict__ x_scale_v,
+    const uint8_t* __restrict__ w1, const void* __restrict__ w1_scale_v,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ expert_ids,
     const int32_t* __restrict__ num_valid, int T, int E, int k, int D, int I, int mbs,
     uint16_t* __restrict__ a_out, float4* __restrict__ zero_y, int64_t zero_n4) {
   constexpr int NT = BM / 16;
   constexpr int RG = 4 / KS;
-  constexpr int EB = FP8 ? 1 : 2;
+  constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
+  const float* x_scale = static_cast<const float*>(x_scale_v);
+  const float* w1_scale = static_cast<const float*>(w1_scale_v);
   __shared__ f32x4_t red[KS > 1 ? (KS - 1) * RG * 2 * NT * 64 : 1];
   if (zero_y)
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 256)
@@ -233,16 +282,26 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
   const int i16 = lane & 15, g = lane >> 4;
   const int n_w = nt * 16 * RG + rg * 16;  // first gate channel of this row group
   const int n_slots = T * k;
-  const int rowb = D * EB;
+  const int rowb = DT == DT_BF16 ? D * 2 : DT == DT_FP8 ? D : D / 2;
+  const int rows_s = D / 32;  // FP4: E8M0 scales per row
   const uint8_t* wrow[2] = {w1 + ((size_t)e * 2 * I + n_w + i16) * rowb,
                             w1 + ((size_t)e * 2 * I + I + n_w + i16) * rowb};
+  const uint8_t* wsc[2] = {nullptr, nullptr};
+  if constexpr (FP4) {
+    const uint8_t* ws8 = static_cast<const uint8_t*>(w1_scale_v);
+    wsc[0] = ws8 + ((size_t)e * 2 * I + n_w + i16) * rows_s;
+    wsc[1] = ws8 + ((size_t)e * 2 * I + I + n_w + i16) * rows_s;
+  }
   const uint8_t* xrow[NT];
+  const uint8_t* xsc[NT];
   int slot[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int s = sorted_ids[mb * BM + tt * 16 + i16];
     slot[tt] = s;
-    xrow[tt] = (unsigned)s < (unsigned)n_slots ? x + (size_t)(s / k) * rowb : nullptr;
+    const bool real = (unsigned)s < (unsigned)n_slots;
+    xrow[tt] = real ? x + (size_t)(s / k) * rowb : nullptr;
+    xsc[tt] = FP4 && real ? static_cast<const uint8_t*>(x_scale_v) + (size_t)(s / k) * rows_s : nullptr;
   }
   f32x4_t acc[2][NT];
 #pragma unroll
@@ -251,7 +310,7 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
     for (int tt = 0; tt < NT; ++tt) acc[a][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  mainloop<FP8, 2, NT, U>(wrow, xrow, kb0, kb1, rowb, acc);
+  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
   if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
 
   const int n0 = n_w + 4 * g;  // this lane's 4 channels
@@ -321,19 +380,71 @@ __global__ void __launch_bounds__(256) requant_rows_kernel(const uint16_t* __res
   if (lane == 0) a_scale[row] = scale;
 }
 
+// MXFP4: each block of 32 consecutive bf16 values of a slot row becomes one E8M0 scale
+// 2^(floor(log2 amax) - 2) (an all-zero block takes 2^0) and 32 E2M1 codes of value/scale,
+// rounded to nearest even on the E2M1 grid (0, 0.5, 1, 1.5, 2, 3, 4, 6) and saturated at 6;
+// element 2j in the low nibble.  value/scale is exact (a power-of-two scaling), so only the
+// final rounding decides, on exact values.  One thread per block.
+__device__ __forceinline__ uint32_t e2m1_code(float v, int shift) {
+  const float y = fabsf(ldexpf(v, shift));
+  const uint32_t m = y <= 0.25f ? 0u : y < 0.75f ? 1u : y <= 1.25f ? 2u : y < 1.75f ? 3u
+                   : y <= 2.5f  ? 4u : y < 3.5f  ? 5u : y <= 5.0f  ? 6u : 7u;
+  return m | (__float_as_uint(v) >> 31 << 3);
+}
+__global__ void __launch_bounds__(256) requant_mx_kernel(const uint16_t* __restrict__ a_bf16,
+                                                         int64_t nblocks,
+                                                         uint8_t* __restrict__ a_codes,
+                                                         uint8_t* __restrict__ a_scale) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(a_bf16 + b * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = src[q];
+    w[4 * q] = v.x;
+    w[4 * q + 1] = v.y;
+    w[4 * q + 2] = v.z;
+    w[4 * q + 3] = v.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[q] >> 16))));
+  int ex = 0;
+  frexpf(amax, &ex);  // amax = m 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+  const int e = amax > 0.f ? min(254, max(0, ex - 1 - 2 + 127)) : 127;
+  const int shift = 127 - e;  // value / 2^(e - 127)
+  uint32_t out[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t p = w[4 * q + h];
+      o |= (e2m1_code(bf16_bits_to_f32(p & 0xFFFFu), shift) | (e2m1_code(bf16_bits_to_f32(p >> 16), shift) << 4)) << (8 * h);
+    }
+    out[q] = o;
+  }
+  *reinterpret_cast<uint4*>(a_codes + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  a_scale[b] = (uint8_t)e;
+}
+
 // ----------------------------------------------------------------------------- stage 2
 // Block = 4 waves = RG = 4/KS row groups x KS parts of K; a row group is 32
 // model_dim rows.  grid: ceil(D/(32*RG)) channel tiles x cap/BM row blocks.
-template <int BM, bool FP8, int U, int OM, int KS>
+template <int BM, int DT, int U, int OM, int KS>
 __global__ void __launch_bounds__(256) gemm2_kernel(
-    const uint8_t* __restrict__ a, const float* __restrict__ a_scale,
-    const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
+    const uint8_t* __restrict__ a, const void* __restrict__ a_scale_v,
+    const uint8_t* __restrict__ w2, const void* __restrict__ w2_scale_v,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
     int k, int D, int I, int mbs, void* __restrict__ y) {
   constexpr int NT = BM / 16;
   constexpr int RG = 4 / KS;
-  constexpr int EB = FP8 ? 1 : 2;
+  constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
+  const float* a_scale = static_cast<const float*>(a_scale_v);
+  const float* w2_scale = static_cast<const float*>(w2_scale_v);
   __shared__ f32x4_t red[KS > 1 ? (KS - 1) * RG * 2 * NT * 64 : 1];
   int mb, nt;
   if (!block_tile(mbs, (D + 32 * RG - 1) / (32 * RG), mb, nt)) return;
@@ -348,16 +459,26 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
   const int i16 = lane & 15, g = lane >> 4;
   const int n_slots = T * k;
-  const int rowb = I * EB;
+  const int rowb = DT == DT_BF16 ? I * 2 : DT == DT_FP8 ? I : I / 2;
+  const int rows_s = I / 32;  // FP4: E8M0 scales per row
   const uint8_t* wrow[2] = {w2 + ((size_t)e * D + d_w + i16) * rowb,
                             w2 + ((size_t)e * D + d_w + 16 + i16) * rowb};
+  const uint8_t* wsc[2] = {nullptr, nullptr};
+  if constexpr (FP4) {
+    const uint8_t* ws8 = static_cast<const uint8_t*>(w2_scale_v);
+    wsc[0] = ws8 + ((size_t)e * D + d_w + i16) * rows_s;
+    wsc[1] = ws8 + ((size_t)e * D + d_w + 16 + i16) * rows_s;
+  }
   const uint8_t* xrow[NT];
+  const uint8_t* xsc[NT];
   int slot[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int s = sorted_ids[mb * BM + tt * 16 + i16];
     slot[tt] = s;
-    xrow[tt] = (unsigned)s < (unsigned)n_slots ? a + (size_t)s * rowb : nullptr;
+    const bool real = (unsigned)s < (unsigned)n_slots;
+    xrow[tt] = real ? a + (size_t)s * rowb : nullptr;
+    xsc[tt] = FP4 && real ? static_cast<const uint8_t*>(a_scale_v) + (size_t)s * rows_s : nullptr;
   }
   f32x4_t acc[2][NT];
 #pragma unroll
@@ -366,7 +487,7 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     for (int tt = 0; tt < NT; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  mainloop<FP8, 2, NT, U>(wrow, xrow, kb0, kb1, rowb, acc);
+  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
   if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
 
   float ws[2][4];
@@ -790,63 +911,78 @@ static int pick_ks(int64_t waves_ks1) {
   return 4;
 }
 
-template <int BM, bool FP8, int KS>
-static void gemm1_go(const void* x, const float* x_scale, const void* w1, const float* w1_scale,
+template <int BM, int DT, int KS>
+static void gemm1_go(const void* x, const void* x_scale, const void* w1, const void* w1_scale,
                      const int32_t* sorted_ids, const int32_t* expert_ids,
                      const int32_t* num_valid, int mbs, int T, int E, int k, int D, int I,
                      uint16_t* a_bf16, float* zero_y, int64_t zero_n, hipStream_t st) {
   constexpr int U = BM == 64 ? 2 : 4;
   constexpr int RG = 4 / KS;
   const dim3 grid(xcd_grid(mbs, I / (16 * RG)));
-  gemm1_kernel<BM, FP8, U, KS><<<grid, 256, 0, st>>>(
+  gemm1_kernel<BM, DT, U, KS><<<grid, 256, 0, st>>>(
       (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, sorted_ids, expert_ids, num_valid,
       T, E, k, D, I, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
 }
 
-template <int BM, bool FP8>
-static void gemm1_ks(int ks, const void* x, const float* x_scale, const void* w1,
-                     const float* w1_scale, const int32_t* sorted_ids, const int32_t* expert_ids,
+template <int BM, int DT>
+static void gemm1_ks(int ks, const void* x, const void* x_scale, const void* w1,
+                     const void* w1_scale, const int32_t* sorted_ids, const int32_t* expert_ids,
                      const int32_t* num_valid, int mbs, int T, int E, int k, int D, int I,
                      uint16_t* a_bf16, float* zero_y, int64_t zero_n, hipStream_t st) {
   if (ks == 4)
-    gemm1_go<BM, FP8, 4>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+    gemm1_go<BM, DT, 4>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
   else if (ks == 2)
-    gemm1_go<BM, FP8, 2>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+    gemm1_go<BM, DT, 2>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
   else
-    gemm1_go<BM, FP8, 1>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+    gemm1_go<BM, DT, 1>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
 }
 
-hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void* w1,
-                        const float* w1_scale, const int32_t* sorted_ids,
+// The quantised types write bf16 rows to the workspace, then requantise them into a.
+static hipError_t requant(int dt, const uint16_t* a_bf16, int T, int k, int I, void* a, void* a_scale,
+                          hipStream_t st) {
+  const int rows = T * k;
+  if (dt == DT_FP8) {
+    requant_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>(a_bf16, rows, I, reinterpret_cast<uint8_t*>(a),
+                                                         static_cast<float*>(a_scale));
+  } else {
+    const int64_t nblocks = (int64_t)rows * (I / 32);
+    requant_mx_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, st>>>(
+        a_bf16, nblocks, reinterpret_cast<uint8_t*>(a), static_cast<uint8_t*>(a_scale));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* w1,
+                        const void* w1_scale, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
-                        int E, int k, int D, int I, int B, void* a, float* a_scale, void* ws,
+                        int E, int k, int D, int I, int B, void* a, void* a_scale, void* ws,
                         float* zero_y, int64_t zero_n, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  uint16_t* a_bf16 = fp8 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
+  uint16_t* a_bf16 = dt != DT_BF16 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
   const int mbs = (int)(cap / B);
-  if (use_prefill(B, T, k, E, D, I)) {
+  if (dt != DT_FP4 && use_prefill(B, T, k, E, D, I)) {
     const dim3 grid(xcd_grid(mbs, (I + 127) / 128));
-    if (fp8)
+    if (dt == DT_FP8)
       gemm_prefill_kernel<true, PF_G1><<<grid, 512, 0, st>>>(
-          (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, nullptr, sorted_ids, expert_ids,
-          num_valid, T, E, k, I, D, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
+          (const uint8_t*)x, static_cast<const float*>(x_scale), (const uint8_t*)w1,
+          static_cast<const float*>(w1_scale), nullptr, sorted_ids, expert_ids, num_valid, T, E, k, I, D,
+          mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
     else
       gemm_prefill_kernel<false, PF_G1><<<grid, 512, 0, st>>>(
-          (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, nullptr, sorted_ids, expert_ids,
+          (const uint8_t*)x, nullptr, (const uint8_t*)w1, nullptr, nullptr, sorted_ids, expert_ids,
           num_valid, T, E, k, I, D, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || !fp8) return err;
-    const int rows = T * k;
-    requant_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>(a_bf16, rows, I, reinterpret_cast<uint8_t*>(a), a_scale);
-    return hipGetLastError();
+    if (err != hipSuccess || dt == DT_BF16) return err;
+    return requant(dt, a_bf16, T, k, I, a, a_scale, st);
   }
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int ks = pick_ks(n_act * (I / 16));  // a block covers 16*(4/ks) channels; I % 64 == 0
-#define MOE_G1(BMV)                                                                                   \
-  if (fp8)                                                                                            \
-    gemm1_ks<BMV, true>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st); \
-  else                                                                                                \
-    gemm1_ks<BMV, false>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+#define MOE_G1_DT(BMV, DTV) \
+  gemm1_ks<BMV, DTV>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st)
+#define MOE_G1(BMV)                          \
+  if (dt == DT_FP8) MOE_G1_DT(BMV, DT_FP8);   \
+  else if (dt == DT_FP4) MOE_G1_DT(BMV, DT_FP4); \
+  else MOE_G1_DT(BMV, DT_BF16);
   if (B == 16) {
     MOE_G1(16)
   } else if (B == 32) {
@@ -855,56 +991,56 @@ hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void
     MOE_G1(64)
   }
 #undef MOE_G1
+#undef MOE_G1_DT
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || !fp8) return err;
-  const int rows = T * k;
-  requant_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>(a_bf16, rows, I, reinterpret_cast<uint8_t*>(a), a_scale);
-  return hipGetLastError();
+  if (err != hipSuccess || dt == DT_BF16) return err;
+  return requant(dt, a_bf16, T, k, I, a, a_scale, st);
 }
 
-template <int BM, bool FP8, int OM, int KS>
-static void gemm2_go(int mbs, const void* a, const float* a_scale, const void* w2,
-                     const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+template <int BM, int DT, int OM, int KS>
+static void gemm2_go(int mbs, const void* a, const void* a_scale, const void* w2,
+                     const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
                      int D, int I, void* y, hipStream_t st) {
   constexpr int U = BM == 64 ? 2 : 4;
   constexpr int RG = 4 / KS;
   const dim3 grid(xcd_grid(mbs, (D + 32 * RG - 1) / (32 * RG)));
-  gemm2_kernel<BM, FP8, U, OM, KS><<<grid, 256, 0, st>>>(
+  gemm2_kernel<BM, DT, U, OM, KS><<<grid, 256, 0, st>>>(
       (const uint8_t*)a, a_scale, (const uint8_t*)w2, w2_scale, topk_w, sorted_ids, expert_ids,
       num_valid, T, E, k, D, I, mbs, y);
 }
 
-template <int BM, bool FP8, int OM>
-static void gemm2_ks(int ks, int mbs, const void* a, const float* a_scale, const void* w2,
-                     const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+template <int BM, int DT, int OM>
+static void gemm2_ks(int ks, int mbs, const void* a, const void* a_scale, const void* w2,
+                     const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
                      int D, int I, void* y, hipStream_t st) {
   if (ks == 4)
-    gemm2_go<BM, FP8, OM, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, DT, OM, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
   else if (ks == 2)
-    gemm2_go<BM, FP8, OM, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, DT, OM, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
   else
-    gemm2_go<BM, FP8, OM, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, DT, OM, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
 }
 
-hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void* w2,
-                        const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* w2,
+                        const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
                         int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int mbs = (int)(cap / B);
-  if (use_prefill(B, T, k, E, D, I)) {
+  if (dt != DT_FP4 && use_prefill(B, T, k, E, D, I)) {
     const dim3 grid(xcd_grid(mbs, (D + 255) / 256));
-#define MOE_PF2(F8, MD)                                                                              \
-  gemm_prefill_kernel<F8, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,  \
-                                                   w2_scale, topk_w, sorted_ids, expert_ids,        \
-                                                   num_valid, T, E, k, D, I, mbs, y, nullptr, 0)
+#define MOE_PF2(F8, MD)                                                                                \
+  gemm_prefill_kernel<F8, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, static_cast<const float*>(a_scale), \
+                                                   (const uint8_t*)w2, static_cast<const float*>(w2_scale), \
+                                                   topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, \
+                                                   mbs, y, nullptr, 0)
 #define MOE_PF2_MODES(F8)                                   \
   if (mode == OM_REDUCE) MOE_PF2(F8, PF_G2_REDUCE);         \
   else if (mode == OM_ATOMIC) MOE_PF2(F8, PF_G2_ATOMIC);    \
   else MOE_PF2(F8, PF_G2_ATOMIC_BF16);
-    if (fp8) {
+    if (dt == DT_FP8) {
       MOE_PF2_MODES(true)
     } else {
       MOE_PF2_MODES(false)
@@ -915,17 +1051,19 @@ hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void
   }
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int ks = pick_ks(n_act * (D / 32));  // ks >= 2 needs D % 64 == 0, which always holds
-#define MOE_G2_OM(BMV, F8, OMV) \
-  gemm2_ks<BMV, F8, OMV>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st)
-#define MOE_G2_F8(BMV, F8)                                 \
-  if (mode == OM_REDUCE) MOE_G2_OM(BMV, F8, OM_REDUCE);     \
-  else if (mode == OM_ATOMIC) MOE_G2_OM(BMV, F8, OM_ATOMIC); \
-  else MOE_G2_OM(BMV, F8, OM_ATOMIC_BF16);
-#define MOE_G2(BMV)          \
-  if (fp8) {                 \
-    MOE_G2_F8(BMV, true)     \
-  } else {                   \
-    MOE_G2_F8(BMV, false)    \
+#define MOE_G2_OM(BMV, DTV, OMV) \
+  gemm2_ks<BMV, DTV, OMV>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st)
+#define MOE_G2_DT(BMV, DTV)                                  \
+  if (mode == OM_REDUCE) MOE_G2_OM(BMV, DTV, OM_REDUCE);      \
+  else if (mode == OM_ATOMIC) MOE_G2_OM(BMV, DTV, OM_ATOMIC); \
+  else MOE_G2_OM(BMV, DTV, OM_ATOMIC_BF16);
+#define MOE_G2(BMV)                             \
+  if (dt == DT_FP8) {                           \
+    MOE_G2_DT(BMV, DT_FP8)                      \
+  } else if (dt == DT_FP4) {                    \
+    MOE_G2_DT(BMV, DT_FP4)                      \
+  } else {                                      \
+    MOE_G2_DT(BMV, DT_BF16)                     \
   }
   if (B == 16) {
     MOE_G2(16)
@@ -935,7 +1073,7 @@ hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void
     MOE_G2(64)
   }
 #undef MOE_G2
-#undef MOE_G2_F8
+#undef MOE_G2_DT
 #undef MOE_G2_OM
   return hipGetLastError();
 }

@@ -30,14 +30,14 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int score, int
                         float* topk_w, int32_t* topk_ids, int32_t* sorted_ids, int64_t cap,
                         int32_t* expert_ids, int32_t* num_valid, void* ws, hipStream_t st);
 
-hipError_t launch_gemm1(int fp8, const void* x, const float* x_scale, const void* w1,
-                        const float* w1_scale, const int32_t* sorted_ids,
+hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* w1,
+                        const void* w1_scale, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
-                        int E, int k, int D, int I, int B, void* a, float* a_scale, void* ws,
+                        int E, int k, int D, int I, int B, void* a, void* a_scale, void* ws,
                         float* zero_y, int64_t zero_n, hipStream_t st);
 
-hipError_t launch_gemm2(int fp8, const void* a, const float* a_scale, const void* w2,
-                        const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* w2,
+                        const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
                         int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st);
 

@@ -54,18 +54,18 @@ def test_sorted_capacity_matches_oracle(lib, T, E, k, B):
 
 def test_workspace_layout(lib):
     import mixture_experts_routing_amd as m
-    for dtype in ("bf16", "fp8"):
+    for dtype in ("bf16", "fp8", "mxfp4"):
         for mode in ("atomic", "reduce", "atomic_bf16"):
-            for (T, E, k, D, I, B) in [(4, 8, 2, 128, 64, 16), (8192, 2304, 36, 64, 64, 32),
+            for (T, E, k, D, I, B) in [(4, 8, 2, 128, 128, 16), (8192, 2304, 36, 128, 128, 32),
                                        (16, 256, 8, 7168, 2048, 16)]:
                 total, offs = m.moe_forward_workspace_layout(dtype, mode, T, E, k, D, I, B)
                 n, cap = T * k, oracle.sorted_capacity(T, E, k, B)
                 sizes = {"topk_weights": 4 * n, "topk_ids": 4 * n, "sorted_token_ids": 4 * cap,
                          "expert_ids": 4 * cap // B, "num_valid": 4,
                          "route_scratch": m.moe_route_workspace_bytes(T, E, k, B),
-                         "a": n * I * (2 if dtype == "bf16" else 1),
-                         "a_scale": 4 * n if dtype == "fp8" else 0,
-                         "gemm1_scratch": 2 * n * I if dtype == "fp8" else 0,
+                         "a": n * I * 2 if dtype == "bf16" else n * I if dtype == "fp8" else n * I // 2,
+                         "a_scale": 4 * n if dtype == "fp8" else n * I // 32 if dtype == "mxfp4" else 0,
+                         "gemm1_scratch": 2 * n * I if dtype in ("fp8", "mxfp4") else 0,
                          "y": 0 if mode == "atomic_bf16" else 4 * D * (T if mode == "atomic" else n)}
                 spans = []
                 for f, o in offs.items():
@@ -122,7 +122,13 @@ def gemm1_call(lib, dtype=0, T=4, E=8, k=2, D=128, I=64, B=16, cap=None, ptrs=No
 
 
 def test_gemm1_validation(lib):
-    assert gemm1_call(lib, dtype=2) == EINVAL
+    assert gemm1_call(lib, dtype=3) == EINVAL
+    # mxfp4 needs whole 128-element MFMA steps along D and I
+    assert gemm1_call(lib, dtype=2, D=128, I=64) == EUNSUP
+    assert gemm1_call(lib, dtype=2, D=192, I=128) == EUNSUP
+    for key in ("xs", "w1s", "as_", "ws"):
+        assert gemm1_call(lib, dtype=2, I=128, ptrs={key: None}) == EINVAL
+    assert gemm1_call(lib, dtype=2, I=128, ws_bytes=4 * 2 * 128 * 2 - 1) == ENOSPC
     assert gemm1_call(lib, D=100) == EUNSUP
     assert gemm1_call(lib, I=96) == EUNSUP
     assert gemm1_call(lib, D=0) == EUNSUP

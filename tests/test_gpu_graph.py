@@ -32,6 +32,7 @@ CASES = [
     (300, 8, 2, 320, 576, 64, "fp8", "atomic"),
     (300, 8, 2, 320, 192, 64, "bf16", "atomic_bf16"),
     (37, 16, 4, 384, 192, 16, "bf16", "atomic_bf16"),
+    (37, 16, 4, 384, 256, 16, "mxfp4", "atomic"),
 ]
 
 

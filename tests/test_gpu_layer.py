@@ -35,7 +35,7 @@ def oracle_layer(inp, route_ref, dtype, tokens=None):
     w1 = PerExpert(inp["w1"])
     w2 = PerExpert(inp["w2"])
     kw = {}
-    if dtype == "fp8":
+    if dtype in ("fp8", "mxfp4"):
         kw = dict(x_scale=inp["x_scale"].cpu().numpy(), w1_scale=PerExpert(inp["w1_scale"]),
                   w2_scale=PerExpert(inp["w2_scale"]))
     return oracle.moe_layer(host_bits(inp["x"]), w1, w2, route_ref.ids, route_ref.weights, dtype,
@@ -48,18 +48,33 @@ def run_forward(inp, k, B, dtype, mode):
                                   x_scale=inp.get("x_scale"), w1_scale=inp.get("w1_scale"),
                                   w2_scale=inp.get("w2_scale"))
     torch.cuda.synchronize()
-    T, D = inp["x"].shape
+    T = inp["x"].shape[0]
     E, twoI, _ = inp["w1"].shape
+    D = inp["w2"].shape[1]  # (x is packed two values per byte in mxfp4)
     views = m.workspace_views(ws, offs, dtype, mode, T, E, k, D, twoI // 2, B)
     return out, views
 
 
+def check_a_mx(codes_packed, scales, want_codes, want_scales):
+    """mxfp4 intermediate: the block exponents and the E2M1 codes are exact functions of the
+    bf16 row, so they match the oracle's except where a bf16 value sits one rounding step
+    away (rare); at most 1e-3 of the codes and of the scales may differ."""
+    got = oracle.fp4_unpack(codes_packed)
+    assert got.shape == want_codes.shape
+    assert (got != want_codes).mean() <= 1e-3, f"codes differ at {(got != want_codes).mean():.2e}"
+    assert (scales != want_scales).mean() <= 1e-3, f"scales differ at {(scales != want_scales).mean():.2e}"
+
+
 def check_intermediate(views, ref, dtype, rows):
-    """Diagnostic check of the intermediate a (after the output checks).  For fp8 the bf16
-    rows before the requant are held to the bf16 rule too."""
+    """Diagnostic check of the intermediate a (after the output checks).  For fp8 and mxfp4
+    the bf16 rows before the requant are held to the bf16 rule too."""
     want = oracle.bf16_decode(ref.a_bits[rows])
     if dtype == "bf16":
         check_a_bf16(views["a"].float().cpu().double().numpy()[rows], want)
+    elif dtype == "mxfp4":
+        check_a_bf16(views["a_pre"].float().cpu().double().numpy()[rows], want)
+        check_a_mx(views["a"].cpu().numpy()[rows], views["a_scale"].cpu().numpy()[rows],
+                   ref.a_codes[rows], ref.a_scale[rows])
     else:
         check_a_bf16(views["a_pre"].float().cpu().double().numpy()[rows], want)
         check_a_fp8(views["a"].cpu().numpy()[rows], views["a_scale"].cpu().numpy()[rows],
@@ -97,7 +112,17 @@ SMALL_FP8 = [
     # long fp8 rows; 2112-byte rows end in a half 128-byte chunk
     (200, 4, 2, 2112, 2112, 64),
 ]
-SMALL = [(*c, "bf16") for c in SMALL_BF16] + [(*c, "fp8") for c in SMALL_FP8]
+# mxfp4: D and I multiples of 128; every BLOCK_M runs the decode kernels; D = 384 and
+# I = 640 end in a half 128-byte chunk (one of the two MFMAs of a chunk)
+SMALL_MX = [
+    (4, 8, 2, 128, 128, 16),
+    (37, 16, 4, 384, 256, 16),
+    (37, 16, 4, 256, 640, 32),
+    (61, 12, 3, 256, 512, 64),
+    (300, 8, 2, 384, 384, 64),
+]
+SMALL = ([(*c, "bf16") for c in SMALL_BF16] + [(*c, "fp8") for c in SMALL_FP8] +
+         [(*c, "mxfp4") for c in SMALL_MX])
 
 
 @pytest.mark.parametrize("mode", ["atomic", "reduce"])
@@ -209,6 +234,8 @@ FULL = [
     ("kimi", 64, [0, 33, 63]),
     ("kimi", 4096, [5, 2048, 4095]),
     ("kimi", 16384, [0, 8191, 16383]),
+    ("kimi_mxfp4", 64, [0, 33, 63]),
+    ("kimi_mxfp4", 4096, [5, 2048, 4095]),
 ]
 
 
