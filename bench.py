@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="deepseek", choices=["deepseek", "gptoss", "kimi", "tiny"])
+    ap.add_argument("--workload", default="deepseek", choices=["deepseek", "gptoss", "kimi", "kimi_mxfp4", "tiny"])
     ap.add_argument("--T", type=int, default=16)
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

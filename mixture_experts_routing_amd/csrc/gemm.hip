@@ -135,7 +135,9 @@ __device__ __forceinline__ void mfma_fp4(f32x4_t& acc, const i32x4_t (&a)[2], co
 // and [64+16g, 64+16g+16), so each load instruction covers 64 contiguous bytes per row.
 // The last chunk of an fp8 (fp4) row may be half: 64 bytes; its second half reads as zero.
 // FP4: wsc / xsc point at the rows' E8M0 scales (8 per chunk); lane group g takes the
-// scales of blocks g and 4 + g of each chunk (a padding row takes 2^0).
+// scales of blocks g and 4 + g of each chunk (a padding row takes 2^0), with one 8-byte load
+// per row and chunk when the scale rows are 8-byte aligned (K % 256 == 0), else two 4-byte
+// loads.
 template <int DT, int NG, int NT, int U>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
                                          const uint8_t* const (&xrow)[NT],
@@ -145,19 +147,21 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
   constexpr bool FP4 = DT == DT_FP4;
   const int g = lane_id() >> 4, g16 = g * 16;
   const i32x4_t zero = {0, 0, 0, 0};
+  const bool pair8 = (kbytes & 127) == 0;  // scale rows of kbytes / 16 bytes, a multiple of 8
   // scale bytes of chunk kb for blocks (g, 4 + g); a half chunk has no second block
-  auto scales = [&](const uint8_t* r, int kb, bool in1, int& s0, int& s1) {
-    s0 = s1 = 127;
-    if (r) {
-      s0 = (int)((*reinterpret_cast<const uint32_t*>(r + kb / 16) >> (8 * g)) & 0xFFu);
-      if (in1) s1 = (int)((*reinterpret_cast<const uint32_t*>(r + kb / 16 + 4) >> (8 * g)) & 0xFFu);
-    }
+  // the two scale words of chunk kb (a padding row: 2^0 everywhere)
+  auto scales = [&](const uint8_t* r, int kb, bool in1) -> uint2 {
+    if (!r) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    if (in1 && pair8) return *reinterpret_cast<const uint2*>(r + kb / 16);
+    const uint32_t lo = *reinterpret_cast<const uint32_t*>(r + kb / 16);
+    return make_uint2(lo, in1 ? *reinterpret_cast<const uint32_t*>(r + kb / 16 + 4) : 0x7F7F7F7Fu);
   };
+  auto byte_g = [&](uint32_t w) { return (int)((w >> (8 * g)) & 0xFFu); };
   int kb = kb0;
   const int kend_full = kb1 < (kbytes & ~127) ? kb1 : (kbytes & ~127);
   for (; kb + 128 * U <= kend_full; kb += 128 * U) {
     i32x4_t wa[U][NG][2], xb[U][NT][2];
-    int wsa[U][NG][2], xsa[U][NT][2];
+    uint2 wsa[U][NG], xsa[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int off = kb + 128 * u + g16;
@@ -165,13 +169,13 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
       for (int ng = 0; ng < NG; ++ng) {
         wa[u][ng][0] = ld16(wrow[ng] + off);
         wa[u][ng][1] = ld16(wrow[ng] + off + 64);
-        if constexpr (FP4) scales(wsc[ng], kb + 128 * u, true, wsa[u][ng][0], wsa[u][ng][1]);
+        if constexpr (FP4) wsa[u][ng] = scales(wsc[ng], kb + 128 * u, true);
       }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         xb[u][tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
         xb[u][tt][1] = xrow[tt] ? ld16(xrow[tt] + off + 64) : zero;
-        if constexpr (FP4) scales(xsc[tt], kb + 128 * u, true, xsa[u][tt][0], xsa[u][tt][1]);
+        if constexpr (FP4) xsa[u][tt] = scales(xsc[tt], kb + 128 * u, true);
       }
     }
 #pragma unroll
@@ -181,7 +185,8 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
           if constexpr (FP4)
-            mfma_fp4(acc[ng][tt], wa[u][ng], xb[u][tt], wsa[u][ng][0], wsa[u][ng][1], xsa[u][tt][0], xsa[u][tt][1]);
+            mfma_fp4(acc[ng][tt], wa[u][ng], xb[u][tt], byte_g(wsa[u][ng].x), byte_g(wsa[u][ng].y),
+                     byte_g(xsa[u][tt].x), byte_g(xsa[u][tt].y));
           else
             mfma_chunk<DT == DT_FP8>(acc[ng][tt], wa[u][ng], xb[u][tt]);
         }
@@ -190,25 +195,26 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
     const int off = kb + g16;
     const bool in1 = kb + 64 < kbytes;
     i32x4_t wa[NG][2], xb[NT][2];
-    int wsa[NG][2], xsa[NT][2];
+    uint2 wsa[NG], xsa[NT];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
       wa[ng][0] = ld16(wrow[ng] + off);
       wa[ng][1] = in1 ? ld16(wrow[ng] + off + 64) : zero;
-      if constexpr (FP4) scales(wsc[ng], kb, in1, wsa[ng][0], wsa[ng][1]);
+      if constexpr (FP4) wsa[ng] = scales(wsc[ng], kb, in1);
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       xb[tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
       xb[tt][1] = (in1 && xrow[tt]) ? ld16(xrow[tt] + off + 64) : zero;
-      if constexpr (FP4) scales(xsc[tt], kb, in1, xsa[tt][0], xsa[tt][1]);
+      if constexpr (FP4) xsa[tt] = scales(xsc[tt], kb, in1);
     }
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         if constexpr (FP4)
-          mfma_fp4(acc[ng][tt], wa[ng], xb[tt], wsa[ng][0], wsa[ng][1], xsa[tt][0], xsa[tt][1]);
+          mfma_fp4(acc[ng][tt], wa[ng], xb[tt], byte_g(wsa[ng].x), byte_g(wsa[ng].y), byte_g(xsa[tt].x),
+                   byte_g(xsa[tt].y));
         else
           mfma_chunk<DT == DT_FP8>(acc[ng][tt], wa[ng], xb[tt]);
       }
