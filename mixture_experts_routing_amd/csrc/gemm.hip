@@ -148,6 +148,11 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
   const int g = lane_id() >> 4, g16 = g * 16;
   const i32x4_t zero = {0, 0, 0, 0};
   const bool pair8 = (kbytes & 127) == 0;  // scale rows of kbytes / 16 bytes, a multiple of 8
+  // activation tiles with at least one real row (wave-uniform): a tile of padding rows
+  // issues no loads at all (at decode sizes most tiles of a 64-row block are padding)
+  bool live[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) live[tt] = __ballot(xrow[tt] != nullptr) != 0;
   // scale bytes of chunk kb for blocks (g, 4 + g); a half chunk has no second block
   // the two scale words of chunk kb (a padding row: 2^0 everywhere)
   auto scales = [&](const uint8_t* r, int kb, bool in1) -> uint2 {
@@ -173,9 +178,13 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
       }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        xb[u][tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
-        xb[u][tt][1] = xrow[tt] ? ld16(xrow[tt] + off + 64) : zero;
-        if constexpr (FP4) xsa[u][tt] = scales(xsc[tt], kb + 128 * u, true);
+        xb[u][tt][0] = xb[u][tt][1] = zero;
+        if constexpr (FP4) xsa[u][tt] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+        if (live[tt]) {
+          xb[u][tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
+          xb[u][tt][1] = xrow[tt] ? ld16(xrow[tt] + off + 64) : zero;
+          if constexpr (FP4) xsa[u][tt] = scales(xsc[tt], kb + 128 * u, true);
+        }
       }
     }
 #pragma unroll
@@ -204,9 +213,13 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      xb[tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
-      xb[tt][1] = (in1 && xrow[tt]) ? ld16(xrow[tt] + off + 64) : zero;
-      if constexpr (FP4) xsa[tt] = scales(xsc[tt], kb, in1);
+      xb[tt][0] = xb[tt][1] = zero;
+      if constexpr (FP4) xsa[tt] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      if (live[tt]) {
+        xb[tt][0] = xrow[tt] ? ld16(xrow[tt] + off) : zero;
+        xb[tt][1] = (in1 && xrow[tt]) ? ld16(xrow[tt] + off + 64) : zero;
+        if constexpr (FP4) xsa[tt] = scales(xsc[tt], kb, in1);
+      }
     }
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
