@@ -47,6 +47,8 @@ from .routing import (
     RouteResult,
     route,
     routing_weights,
+    routing_weights_backward,
+    routing_weights_f64,
     select_topk,
     sort_slots,
     sorted_capacity,
@@ -72,6 +74,8 @@ __all__ = [
     "RouteResult",
     "route",
     "routing_weights",
+    "routing_weights_backward",
+    "routing_weights_f64",
     "select_topk",
     "sort_slots",
     "sorted_capacity",

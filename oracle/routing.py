@@ -66,6 +66,27 @@ def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k].astype(np.int32)
 
 
+def _scores_f64(l: np.ndarray, score: str) -> np.ndarray:
+    """Score of every expert: softmax over the token's E logits, or the sigmoid."""
+    if score == "softmax":
+        z = l - l.max(axis=1, keepdims=True)
+        ez = np.exp(z)
+        return ez / ez.sum(axis=1, keepdims=True)
+    return 1.0 / (1.0 + np.exp(-l))
+
+
+def routing_weights_f64(logits: np.ndarray, ids: np.ndarray, score: str = "softmax",
+                        renorm: bool = True) -> np.ndarray:
+    """The routed weights in float64, unrounded (see routing_weights)."""
+    if score not in SCORES:
+        raise ValueError(f"score must be one of {SCORES}")
+    l = np.asarray(logits, dtype=np.float64)
+    sel = np.take_along_axis(_scores_f64(l, score), ids.astype(np.int64), axis=1)
+    if renorm:
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    return sel
+
+
 def routing_weights(logits: np.ndarray, ids: np.ndarray, score: str = "softmax",
                     renorm: bool = True) -> np.ndarray:
     """Routed weights of the selected experts, float64 arithmetic, rounded once to fp32.
@@ -74,19 +95,54 @@ def routing_weights(logits: np.ndarray, ids: np.ndarray, score: str = "softmax",
     p = 1 / (1 + exp(-logit)).  With renorm the selected p are divided by their
     sum, so each token's k weights sum to 1.
     """
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    return routing_weights_f64(l, ids, score, renorm).astype(np.float32)
+
+
+def routing_weights_backward(logits: np.ndarray, ids: np.ndarray, grad_w: np.ndarray,
+                             score: str = "softmax", renorm: bool = True) -> np.ndarray:
+    """Gradient of the routed weights with respect to the logits, float64 [T, E].
+
+    "[Common] Optimize fused router forward/backward kernels" (TransformerEngine #3012),
+    "Changes / Backward kernels": the router's backward.  The pages give no formula;
+    reading taken: the derivative of routing_weights at the selection the forward made
+    (the selection is piecewise constant, so nothing flows through it).  Written as the
+    Jacobian of w_j(l) contracted with grad_w, expert by expert:
+    * softmax, renorm: w_j = e^{l_j} / sum_{i in S} e^{l_i}, dw_j/dl_m = w_j (d_jm - w_m), m in S;
+    * sigmoid, renorm: w_j = s_j / sum_{i in S} s_i, dw_j/dl_m = s_m (1 - s_m) (d_jm - w_j) / sum s;
+    * softmax over all E (no renorm): dw_j/dl_m = p_j (d_{e_j m} - p_m) for every expert m;
+    * sigmoid (no renorm): dw_j/dl_m = s_j (1 - s_j) d_{e_j m}.
+    """
     if score not in SCORES:
         raise ValueError(f"score must be one of {SCORES}")
     l = np.asarray(logits, dtype=np.float32).astype(np.float64)
-    if score == "softmax":
-        z = l - l.max(axis=1, keepdims=True)
-        ez = np.exp(z)
-        p = ez / ez.sum(axis=1, keepdims=True)
-    else:
-        p = 1.0 / (1.0 + np.exp(-l))
-    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    if renorm:
-        sel = sel / sel.sum(axis=1, keepdims=True)
-    return sel.astype(np.float32)
+    ids = np.asarray(ids, dtype=np.int64)
+    g = np.asarray(grad_w, dtype=np.float64)
+    T, E = l.shape
+    k = ids.shape[1]
+    p = _scores_f64(l, score)
+    out = np.zeros((T, E))
+    for t in range(T):
+        sel = p[t, ids[t]]
+        if renorm:
+            w = sel / sel.sum()
+            for j in range(k):
+                for mi in range(k):
+                    m = ids[t, mi]
+                    d = 1.0 if mi == j else 0.0
+                    if score == "softmax":
+                        jac = w[j] * (d - w[mi])
+                    else:
+                        jac = sel[mi] * (1.0 - sel[mi]) * (d - w[j]) / sel.sum()
+                    out[t, m] += g[t, j] * jac
+        else:
+            for j in range(k):
+                e = ids[t, j]
+                if score == "softmax":
+                    out[t] += g[t, j] * p[t, e] * ((np.arange(E) == e) - p[t])
+                else:
+                    out[t, e] += g[t, j] * sel[j] * (1.0 - sel[j])
+    return out
 
 
 def sort_slots(ids: np.ndarray, E: int, block_m: int, cap: int | None = None):

@@ -179,3 +179,50 @@ def test_host_checks():
         select_topk(l, 0)
     with pytest.raises(ValueError):
         select_topk(l, 5)
+
+
+# ---------------------------------------------------------------------------- backward
+from oracle import routing_weights_backward, routing_weights_f64  # noqa: E402
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 5), (33, 1)])
+def test_backward_matches_finite_differences(score, renorm, E, k):
+    # central differences of the float64 forward at the fixed selection
+    rng = np.random.default_rng(E * 10 + k)
+    T = 3
+    l = rng.standard_normal((T, E)).astype(np.float32).astype(np.float64)
+    ids = select_topk(l.astype(np.float32), k)
+    g = rng.standard_normal((T, k))
+    got = routing_weights_backward(l, ids, g, score, renorm)
+    h = 1e-6
+    fd = np.zeros((T, E))
+    for t in range(T):
+        for m in range(E):
+            lp, lm = l.copy(), l.copy()
+            lp[t, m] += h
+            lm[t, m] -= h
+            dw = (routing_weights_f64(lp, ids, score, renorm) - routing_weights_f64(lm, ids, score, renorm)) / (2 * h)
+            fd[t, m] = (dw[t] * g[t]).sum()
+    assert np.allclose(got, fd, atol=1e-8, rtol=1e-6)
+
+
+def test_backward_special_cases():
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal((4, 12))
+    ids = select_topk(l.astype(np.float32), 1)
+    # one renormalised pick has weight 1 whatever the logits: zero gradient
+    for score in ("softmax", "sigmoid"):
+        assert not routing_weights_backward(l, ids, rng.standard_normal((4, 1)), score, True).any()
+    # renormalised softmax is invariant to adding a constant to the picked logits, so each
+    # token's gradient sums to zero; with a gradient equal on all picks it vanishes
+    ids3 = select_topk(l.astype(np.float32), 3)
+    gr = routing_weights_backward(l, ids3, rng.standard_normal((4, 3)), "softmax", True)
+    assert np.allclose(gr.sum(axis=1), 0.0, atol=1e-15)
+    assert np.allclose(routing_weights_backward(l, ids3, np.ones((4, 3)), "softmax", True), 0.0, atol=1e-15)
+    # unpicked experts get no gradient except through the full softmax
+    mask = np.zeros_like(l, dtype=bool)
+    np.put_along_axis(mask, ids3, True, axis=1)
+    for score, renorm in (("softmax", True), ("sigmoid", True), ("sigmoid", False)):
+        assert not routing_weights_backward(l, ids3, np.ones((4, 3)) * 0.7, score, renorm)[~mask].any()
