@@ -240,9 +240,32 @@ def measure_router(env, E, k, score, steps, warmup):
     us = ms * 1e3
     alg = 4 * T * E + 8 * T * k + 4 * nv + 4 * (nv // B) + 4
     gbs = alg / (us * 1e-6) / 1e9
-    return {"router": f"{E}/{k}", "score": score, "T": T, "block_m": B, "us_per_call": round(us, 2),
-            "alg_bytes": alg, "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "rotating_input_sets": R, "timing": how}
+    res = {"router": f"{E}/{k}", "score": score, "T": T, "block_m": B, "us_per_call": round(us, 2),
+           "alg_bytes": alg, "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "rotating_input_sets": R, "timing": how}
+
+    # backward of the weights at each set's picks: reads the picks' ids, weights and weight
+    # gradients (sigmoid: also the picked logits), writes the dense [T, E] logit gradient
+    picks = []
+    for r in range(R):
+        m.moe_topk_softmax_sort(sets[r], k, B, score, out=rt, workspace=ws, stream=stream)
+        picks.append((rt["topk_ids"].clone(), rt["topk_weights"].clone()))
+    gw = torch.randn(T, k, device=dev)
+    gl = torch.empty(T, E, device=dev)
+
+    def bwd(i, st):
+        ids, w = picks[i % R]
+        m.moe_topk_softmax_backward(sets[i % R], ids, w, gw, score, True, grad_logits=gl, stream=st)
+
+    for i in range(warmup):
+        bwd(i, stream)
+    torch.cuda.synchronize()
+    ms_b, _ = graph_ms_per_call(torch, bwd, max(steps, R))
+    alg_b = 4 * T * E + 12 * T * k + (4 * T * k if score == "sigmoid" else 0)
+    gbs_b = alg_b / (ms_b * 1e-3) / 1e9
+    res["backward"] = {"us_per_call": round(ms_b * 1e3, 2), "alg_bytes": alg_b, "GB/s": round(gbs_b, 1),
+                       "hbm_frac": round(gbs_b / HBM_PEAK_GBS, 4)}
+    return res
 
 
 KERNEL_SOURCES = ("mixture_experts_routing_amd/csrc/gemm.hip", "mixture_experts_routing_amd/csrc/moe_device.h")

@@ -130,6 +130,29 @@ int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score
                           int32_t* sorted_token_ids, int64_t sorted_cap, int32_t* expert_ids,
                           int32_t* num_valid, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- routing backward
+ * [P3] "Changes / Backward kernels" and the summary's "Backward (E=2304, K=36)": the fused
+ * router's backward.  The gradient of the weights moe_topk_softmax_sort returned, with
+ * respect to the logits, at the selection it made (nothing flows through the selection,
+ * which is piecewise constant).  Per token, with g = grad_topk_weights, w = topk_weights,
+ * S its picks, s = sigmoid(logit):
+ *   softmax, renorm=1:  dl[e_j] = w_j (g_j - sum_i w_i g_i)
+ *   sigmoid, renorm=1:  dl[e_j] = s_j (1 - s_j) (g_j - sum_i w_i g_i) / sum_i s_i
+ *   softmax, renorm=0:  dl[e]   = p_e (G_e - sum_j w_j g_j), p = softmax over all E,
+ *                                 G_e = g_j if e = e_j, else 0   (every expert)
+ *   sigmoid, renorm=0:  dl[e_j] = s_j (1 - s_j) g_j
+ * and dl = 0 for every other expert.  fp32 arithmetic.
+ *
+ *   logits             fp32  [T, E]   the forward's input
+ *   topk_ids           int32 [T, k]   and topk_weights fp32 [T, k]: the forward's outputs
+ *   grad_topk_weights  fp32  [T, k]
+ *   grad_logits        fp32  [T, E]   out, every element written
+ * Validation as for moe_topk_softmax_sort (no block_m, no sort outputs). */
+int moe_topk_softmax_backward(const float* logits, const int32_t* topk_ids,
+                              const float* topk_weights, const float* grad_topk_weights, int T,
+                              int E, int topk, int score, int renorm, float* grad_logits,
+                              void* stream);
+
 /* ---------------------------------------------------------------- stage 1
  * [P2] gate-up helper and stage-1 commits ("silu(gate)*up with optional fp8
  * weight/act dequant -> bf16"; B-first MFMA with the weight as the first

@@ -26,6 +26,7 @@ __all__ = [
     "moe_gemm1_gateup",
     "moe_gemm2_down",
     "moe_finalize",
+    "moe_topk_softmax_backward",
     "moe_forward",
     "SCORE",
     "DTYPE",
@@ -63,6 +64,7 @@ _SIGS = {
     "moe_strerror": (ctypes.c_char_p, [_I]),
     "moe_topk_softmax_sort": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "moe_gemm1_gateup": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "moe_topk_softmax_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_gemm2_down": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_finalize": (_I, [_I, _P, _I, _I, _I, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P, _P]),
@@ -152,6 +154,19 @@ def moe_topk_softmax_sort(logits: torch.Tensor, topk: int, block_m: int, score: 
         _ptr(out["expert_ids"]), _ptr(out["num_valid"]), _ptr(workspace), ws_bytes, _stream(stream)),
         "moe_topk_softmax_sort")
     return out
+
+
+def moe_topk_softmax_backward(logits, topk_ids, topk_weights, grad_topk_weights, score: str = "softmax",
+                              renorm: bool = True, grad_logits=None, stream=None):
+    """Gradient of the routed weights with respect to the logits: fp32 [T, E]."""
+    T, E = logits.shape
+    k = topk_ids.shape[1]
+    if grad_logits is None:
+        grad_logits = torch.empty(T, E, dtype=torch.float32, device=logits.device)
+    _check(load_library().moe_topk_softmax_backward(
+        _ptr(logits), _ptr(topk_ids), _ptr(topk_weights), _ptr(grad_topk_weights), T, E, k, SCORE[score],
+        int(renorm), _ptr(grad_logits), _stream(stream)), "moe_topk_softmax_backward")
+    return grad_logits
 
 
 def moe_gemm1_gateup(dtype: str, x, w1, route: dict, topk: int, block_m: int, x_scale=None,

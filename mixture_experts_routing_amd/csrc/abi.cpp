@@ -168,6 +168,23 @@ static int check_gemm_common(int dtype, int T, int E, int topk, int D, int I, in
   return MOE_OK;
 }
 
+int moe_topk_softmax_backward(const float* logits, const int32_t* topk_ids,
+                              const float* topk_weights, const float* grad_topk_weights, int T,
+                              int E, int topk, int score, int renorm, float* grad_logits,
+                              void* stream) {
+  if (T < 0 || E < 1 || topk < 1 || topk > E) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+  if ((int64_t)T * E > INT_MAX) return MOE_ERANGE;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (renorm != 0 && renorm != 1) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights) || !ok_ptr(grad_topk_weights) ||
+      !ok_ptr(grad_logits))
+    return MOE_EINVAL;
+  return launch_status(moe::launch_route_backward(logits, topk_ids, topk_weights, grad_topk_weights, T, E,
+                                                  topk, score, renorm, grad_logits, (hipStream_t)stream));
+}
+
 int moe_gemm1_gateup(int dtype, const void* x, const void* x_scale, const void* w1,
                      const void* w1_scale, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int64_t sorted_cap,

@@ -41,6 +41,10 @@ hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* 
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
                         int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st);
 
+hipError_t launch_route_backward(const float* logits, const int32_t* topk_ids, const float* topk_w,
+                                 const float* grad_w, int T, int E, int k, int score, int renorm,
+                                 float* grad_logits, hipStream_t st);
+
 hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16_t* out,
                            hipStream_t st);
 

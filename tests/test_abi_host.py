@@ -197,6 +197,25 @@ def test_finalize_and_forward_validation(lib):
         assert fwd(dtype=1, ws_bytes=total8, **{key: None}) == EINVAL
 
 
+def test_route_backward_validation(lib):
+    def call(T=4, E=8, k=2, score=0, renorm=1, **ptrs):
+        p = dict(l=GOOD, ids=GOOD, w=GOOD, g=GOOD, out=GOOD)
+        p.update(ptrs)
+        return lib.moe_topk_softmax_backward(p["l"], p["ids"], p["w"], p["g"], T, E, k, score, renorm, p["out"], None)
+
+    assert call(k=0) == EINVAL
+    assert call(k=9) == EINVAL
+    assert call(T=-1) == EINVAL
+    assert call(E=9000, k=2) == EUNSUP
+    assert call(score=2) == EINVAL
+    assert call(renorm=2) == EINVAL
+    assert call(T=300000, E=8000, k=2) == ERANGE
+    assert call(T=0, l=None, out=None) == OK
+    for key in ("l", "ids", "w", "g", "out"):
+        assert call(**{key: None}) == EINVAL
+        assert call(**{key: BAD_ALIGN}) == EINVAL
+
+
 def test_strerror(lib):
     import mixture_experts_routing_amd as m
     texts = {m.moe_strerror(s) for s in (OK, EINVAL, ERANGE, ENOSPC, EUNSUP, ELAUNCH)}

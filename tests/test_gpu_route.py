@@ -134,3 +134,37 @@ def test_route_skewed_load():
     logits[:, :4] += 3.0
     got = run_route(logits.cuda(), k, B)
     check_route(got, oracle_route(logits, k, B), T, k)
+
+
+# ---------------------------------------------------------------------------- backward
+BWD_CASES = [
+    # (T, E, k): a single pick; decode-sized; the router stress shapes; k > 64 (two passes)
+    (5, 8, 1), (16, 256, 8), (300, 512, 22), (64, 2304, 36), (40, 100, 70), (8192, 512, 4),
+]
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("T,E,k", BWD_CASES)
+def test_route_backward(T, E, k, score, renorm):
+    """Gradient of the routed weights against the oracle's Jacobian, at the forward's picks:
+    max|err| <= 1e-5 * max|ref| per call (fp32 arithmetic against float64)."""
+    import oracle
+    import mixture_experts_routing_amd as m
+    lg = synth.logits(T, E, seed=T + E + k).cuda()
+    r = m.moe_topk_softmax_sort(lg, k, 16, score=score, renorm=renorm)
+    g = torch.randn(T, k, generator=torch.Generator().manual_seed(k), dtype=torch.float32).cuda()
+    got = m.moe_topk_softmax_backward(lg, r["topk_ids"], r["topk_weights"], g, score, renorm)
+    torch.cuda.synchronize()
+    ids = r["topk_ids"].cpu().numpy()
+    rows = np.arange(T) if T <= 400 else np.arange(0, T, 97)  # the oracle loops in Python
+    ref = oracle.routing_weights_backward(lg.cpu().numpy()[rows], ids[rows], g.cpu().numpy()[rows],
+                                          score, renorm)
+    out = got.cpu().double().numpy()[rows]
+    scale = np.abs(ref).max()
+    assert scale > 0 or k == 1
+    assert np.abs(out - ref).max() <= 1e-5 * max(scale, 1e-30), f"max err {np.abs(out - ref).max():.3g}, scale {scale:.3g}"
+    if renorm or score == "sigmoid":  # only the picks carry a gradient
+        mask = np.zeros_like(out, dtype=bool)
+        np.put_along_axis(mask, ids[rows].astype(np.int64), True, axis=1)
+        assert not out[~mask].any()
