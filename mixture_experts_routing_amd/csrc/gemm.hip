@@ -90,6 +90,15 @@ __device__ __forceinline__ void dma16_to_lds_s(const void* base, uint32_t off, u
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
+// 4 bytes per lane (lane l's at lds + 4 l), the same way; base must be wave-uniform.
+__device__ __forceinline__ void dma4_to_lds_s(const void* base, uint32_t off, uint32_t lds) {
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(reinterpret_cast<const void*>(ub)),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 __device__ __forceinline__ void dma16_to_lds(const void* g, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory");
@@ -568,9 +577,9 @@ constexpr int kPfRingBytes = 160 * 1024 - kPfMaxRows * 4;  // LDS of one CU, les
 
 struct PfArgs {
   const uint8_t* act;
-  const float* act_scale;
+  const void* act_scale;  // fp8: fp32 per row; mxfp4: E8M0 bytes [rows, K/32]
   const uint8_t* w;
-  const float* w_scale;
+  const void* w_scale;    // fp8: fp32 per row; mxfp4: E8M0 bytes [E, rows, K/32]
   const float* topk_w;
   int T, k, N, K, e, nt;
   void* out;
@@ -584,23 +593,29 @@ struct PfArgs {
 // 8 consecutive lanes read one full 128-byte line, and the 16 rows that an MFMA operand
 // reads (one 16-byte segment each) land in 16 different bank groups.  The per-lane parts of
 // the load addresses are fixed; each chunk only advances the wave-uniform bases.
-template <bool FP8, int MODE, int NB>
+// mxfp4: a chunk is 256 E2M1 elements (two MFMAs per fragment pair), and its E8M0 scales (8
+// bytes per row) follow the rows in each buffer as [row][8]: the slot rows', then the weight
+// rows'.  They come by 4-byte direct-to-LDS loads, 32 rows x 8 B per instruction, exactly two
+// per wave and chunk (a wave with fewer rows left repeats its first, writing the same bytes),
+// so they are waited for with the chunk's rows.
+template <int DT, int MODE, int NB>
 __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restrict__ s_slot,
                                              uint8_t* __restrict__ ring) {
   constexpr bool G1 = MODE == PF_G1;
-  constexpr int EB = FP8 ? 1 : 2;
+  constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
   constexpr int MH = 2 * NB;  // slot-row groups per wave
-  // LDS ring: NBUF buffers of (slot rows | weight rows) for one 128-byte chunk each; short
-  // tiles fit three buffers and load two chunks ahead
-  constexpr int TOKB = kPfRows * NB * 128, BUF = TOKB + 256 * 128;
+  // LDS ring: NBUF buffers of (slot rows | weight rows | mxfp4 scales) for one 128-byte chunk
+  // each; short tiles fit three buffers and load two chunks ahead
+  constexpr int TOKB = kPfRows * NB * 128, DATB = TOKB + 256 * 128;
+  constexpr int BUF = DATB + (FP4 ? (kPfRows * NB + 256) * 8 : 0);
   constexpr int NBUF = 3 * BUF <= kPfRingBytes ? 3 : 2;
-  constexpr int NDMA = NB + 4;  // load instructions per wave and chunk
+  constexpr int NDMA = NB + 4 + (FP4 ? 2 : 0);  // load instructions per wave and chunk
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wr = wave & 3, th = wave >> 2;
   const int i16 = lane & 15, g = lane >> 4;
   const int n_slots = p.T * p.k;
-  const int rowb = p.K * EB;
+  const int rowb = DT == DT_BF16 ? p.K * 2 : DT == DT_FP8 ? p.K : p.K / 2;
   const int N = p.N;
   const int pseg = lane & 7, rsub = lane >> 3;
   // ((8 j + rsub) / 2) % 8 = (4 (j % 2) + rsub / 2) % 8; every instruction of this wave has
@@ -636,6 +651,32 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
   const bool on = row0 < N;
   const int nch = (rowb + 127) >> 7;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  // mxfp4 scale loads: instruction j < 2 NB covers slot rows 32 j .. + 31, the others weight
+  // rows 32 (j - 2 NB) .. + 31; lane l takes row l / 2, bytes 4 (l % 2) .. + 3 of the chunk's 8
+  const int srow = p.K / 32;  // scale bytes per row
+  uint32_t soff[2] = {0u, 0u}, sdst[2] = {0u, 0u};
+  const uint8_t* wscale = nullptr;
+  if constexpr (FP4) {
+    wscale = static_cast<const uint8_t*>(p.w_scale) + (size_t)p.e * (G1 ? 2 * N : N) * srow;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      int j = wave + 8 * x;
+      if (j >= 2 * NB + 8) j = wave;  // repeat the wave's first load
+      const int r = lane >> 1;
+      if (j < 2 * NB) {
+        const int s = s_slot[32 * j + r];
+        const bool ok = (unsigned)s < (unsigned)n_slots;
+        soff[x] = (uint32_t)((ok ? (G1 ? s / p.k : s) : 0) * srow) + 4u * (lane & 1);
+        sdst[x] = (uint32_t)(DATB + 256 * j);
+      } else {
+        const int br = 32 * (j - 2 * NB) + r, wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
+        const int ch = G1 ? p.nt * 128 + 32 * wg + 16 * (q & 1) + i : p.nt * 256 + br;
+        const int row = G1 && q >= 2 ? N + ch : ch;
+        soff[x] = (uint32_t)((ch < N ? row : 0) * srow) + 4u * (lane & 1);
+        sdst[x] = (uint32_t)(DATB + kPfRows * NB * 8 + 256 * (j - 2 * NB));
+      }
+    }
+  }
   // chunk c's loads into buffer c % NBUF.  In a half last chunk (fp8, K % 128 == 64) the
   // lanes of the missing half read the present half again; their weight operand bytes are
   // zeroed.
@@ -648,6 +689,15 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     for (int v = 0; v < NB; ++v) dma16_to_lds_s(tb, toff[v] + lo, bo + (wave + 8 * v) * 1024);
 #pragma unroll
     for (int u = 0; u < 4; ++u) dma16_to_lds_s(wb, woff[u] + lo, bo + TOKB + (wave + 8 * u) * 1024);
+    if constexpr (FP4) {
+      const uint8_t* sa = static_cast<const uint8_t*>(p.act_scale) + (size_t)c * 8;
+      const uint8_t* sw = wscale + (size_t)c * 8;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const bool tokrow = sdst[x] < (uint32_t)(DATB + kPfRows * NB * 8);
+        dma4_to_lds_s(tokrow ? sa : sw, soff[x], bo + sdst[x]);
+      }
+    }
   };
 
   f32x4_t acc[4][MH];
@@ -667,6 +717,16 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     if (more) issue(c + NBUF - 1);
     const uint8_t* tb = ring + (c % NBUF) * BUF;
     const uint8_t* wbuf = tb + TOKB + (64 * wr) * 128;
+    // mxfp4: this lane's scale bytes (blocks g and 4 + g of the chunk) of its weight rows
+    int wsc0[4] = {127, 127, 127, 127}, wsc1[4] = {127, 127, 127, 127};
+    if constexpr (FP4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint2 v = *reinterpret_cast<const uint2*>(tb + DATB + kPfRows * NB * 8 + (64 * wr + 16 * q + i16) * 8);
+        wsc0[q] = (int)((v.x >> (8 * g)) & 0xFFu);
+        wsc1[q] = (int)((v.y >> (8 * g)) & 0xFFu);
+      }
+    }
     i32x4_t wf[4][2];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -680,11 +740,17 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     }
     // slot-row fragments: a ring of 4, read 3 groups ahead of the MFMAs that use them
     i32x4_t tf[4][2];
+    int tsc0[4], tsc1[4];
     auto rd = [&](int m) {
       const int tt = 2 * m + th;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         tf[m & 3][h] = *reinterpret_cast<const i32x4_t*>(&tb[(tt * 16 + i16) * 128 + 16 * ((4 * h + g) ^ fsw)]);
+      if constexpr (FP4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(tb + DATB + (tt * 16 + i16) * 8);
+        tsc0[m & 3] = (int)((v.x >> (8 * g)) & 0xFFu);
+        tsc1[m & 3] = (int)((v.y >> (8 * g)) & 0xFFu);
+      }
     };
 #pragma unroll
     for (int m = 0; m < 3 && m < MH; ++m) rd(m);
@@ -693,8 +759,13 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
       if (m + 3 < MH) rd(m + 3);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if constexpr (G1) mfma_chunk<FP8>(acc[q][m], wf[q], tf[m & 3]);
-        else mfma_chunk<FP8>(acc[q][m], tf[m & 3], wf[q]);
+        if constexpr (FP4) {
+          if constexpr (G1) mfma_fp4(acc[q][m], wf[q], tf[m & 3], wsc0[q], wsc1[q], tsc0[m & 3], tsc1[m & 3]);
+          else mfma_fp4(acc[q][m], tf[m & 3], wf[q], tsc0[m & 3], tsc1[m & 3], wsc0[q], wsc1[q]);
+        } else {
+          if constexpr (G1) mfma_chunk<FP8>(acc[q][m], wf[q], tf[m & 3]);
+          else mfma_chunk<FP8>(acc[q][m], tf[m & 3], wf[q]);
+        }
       }
     }
     // chunk c + 1 has landed (only the loads issued in this chunk may still be in flight)
@@ -714,7 +785,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
       const int n0 = row0 + 16 * h + 4 * g;
       float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
       if constexpr (FP8) {
-        const float* ws = p.w_scale + (size_t)p.e * 2 * I;
+        const float* ws = static_cast<const float*>(p.w_scale) + (size_t)p.e * 2 * I;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           sg[r] = ws[n0 + r];
@@ -726,7 +797,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
         const int s = s_slot[(2 * m + th) * 16 + i16];
         if ((unsigned)s >= (unsigned)n_slots) continue;
         float xs = 1.f;
-        if constexpr (FP8) xs = p.act_scale[s / p.k];
+        if constexpr (FP8) xs = static_cast<const float*>(p.act_scale)[s / p.k];
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -743,7 +814,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     float ws[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (FP8) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ws[q] = p.w_scale[(size_t)p.e * D + row0 + 16 * q + i16];
+      for (int q = 0; q < 4; ++q) ws[q] = static_cast<const float*>(p.w_scale)[(size_t)p.e * D + row0 + 16 * q + i16];
     }
     if constexpr (MODE == PF_G2_ATOMIC_BF16) {
       // channel pairs (2c, 2c+1) sit in lanes i16 = 2c and 2c+1: the even lane adds the pairs
@@ -761,7 +832,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
           sc[r] = 0.f;
           if ((unsigned)sr[r] < (unsigned)n_slots) {
             sc[r] = p.topk_w[sr[r]];
-            if constexpr (FP8) sc[r] *= p.act_scale[sr[r]];
+            if constexpr (FP8) sc[r] *= static_cast<const float*>(p.act_scale)[sr[r]];
           }
         }
         const int s_a = odd ? sr[2] : sr[0], s_b = odd ? sr[3] : sr[1];
@@ -788,7 +859,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
           const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
           if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
           float sc = p.topk_w[s];
-          if constexpr (FP8) sc *= p.act_scale[s];
+          if constexpr (FP8) sc *= static_cast<const float*>(p.act_scale)[s];
           float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / p.k) * D + row0 + i16;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -806,10 +877,10 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
 // from the expert's first block (the workgroups of the tile's other blocks exit at once) x one
 // tile of 256 weight rows (gemm1: 128 gate and the matching 128 up channels; gemm2: 256
 // model_dim rows).
-template <bool FP8, int MODE>
+template <int DT, int MODE>
 __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
-    const uint8_t* __restrict__ act, const float* __restrict__ act_scale,
-    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
+    const uint8_t* __restrict__ act, const void* __restrict__ act_scale,
+    const uint8_t* __restrict__ w, const void* __restrict__ w_scale,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
     int k, int N, int K, int mbs, void* __restrict__ out, float4* __restrict__ zero_y,
@@ -845,10 +916,10 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
   __syncthreads();  // s_slot
   const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out};
   switch (nb) {
-    case 1: prefill_tile<FP8, MODE, 1>(p, s_slot, ring); break;
-    case 2: prefill_tile<FP8, MODE, 2>(p, s_slot, ring); break;
-    case 3: prefill_tile<FP8, MODE, 3>(p, s_slot, ring); break;
-    default: prefill_tile<FP8, MODE, 4>(p, s_slot, ring); break;
+    case 1: prefill_tile<DT, MODE, 1>(p, s_slot, ring); break;
+    case 2: prefill_tile<DT, MODE, 2>(p, s_slot, ring); break;
+    case 3: prefill_tile<DT, MODE, 3>(p, s_slot, ring); break;
+    default: prefill_tile<DT, MODE, 4>(p, s_slot, ring); break;
   }
 }
 
@@ -856,8 +927,10 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
 // direct-to-LDS loads take 32-bit byte offsets: the activation rows and one expert's
 // weights must each span less than 2 GB (larger shapes run the decode kernels, which
 // address in 64 bits).
-static bool use_prefill(int B, int64_t T, int k, int E, int64_t D, int64_t I) {
+// mxfp4 needs K % 256 == 0 on both GEMMs (whole 8-byte scale groups per chunk).
+static bool use_prefill(int dt, int B, int64_t T, int k, int E, int64_t D, int64_t I) {
   const int64_t kMax = (int64_t)1 << 31;
+  if (dt == DT_FP4 && (D % 256 || I % 256)) return false;
   return B == kPfRows && T * k >= 32LL * E && T * k * (D > I ? D : I) * 2 < kMax &&
          2 * I * D * 2 < kMax;
 }
@@ -979,17 +1052,20 @@ hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* 
   if (T == 0) return hipSuccess;
   uint16_t* a_bf16 = dt != DT_BF16 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
   const int mbs = (int)(cap / B);
-  if (dt != DT_FP4 && use_prefill(B, T, k, E, D, I)) {
+  if (use_prefill(dt, B, T, k, E, D, I)) {
     const dim3 grid(xcd_grid(mbs, (I + 127) / 128));
+#define MOE_PF1(DTV)                                                                                   \
+  gemm_prefill_kernel<DTV, PF_G1><<<grid, 512, 0, st>>>((const uint8_t*)x, x_scale, (const uint8_t*)w1, \
+                                                       w1_scale, nullptr, sorted_ids, expert_ids,       \
+                                                       num_valid, T, E, k, I, D, mbs, a_bf16,           \
+                                                       reinterpret_cast<float4*>(zero_y), zero_n / 4)
     if (dt == DT_FP8)
-      gemm_prefill_kernel<true, PF_G1><<<grid, 512, 0, st>>>(
-          (const uint8_t*)x, static_cast<const float*>(x_scale), (const uint8_t*)w1,
-          static_cast<const float*>(w1_scale), nullptr, sorted_ids, expert_ids, num_valid, T, E, k, I, D,
-          mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
+      MOE_PF1(DT_FP8);
+    else if (dt == DT_FP4)
+      MOE_PF1(DT_FP4);
     else
-      gemm_prefill_kernel<false, PF_G1><<<grid, 512, 0, st>>>(
-          (const uint8_t*)x, nullptr, (const uint8_t*)w1, nullptr, nullptr, sorted_ids, expert_ids,
-          num_valid, T, E, k, I, D, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
+      MOE_PF1(DT_BF16);
+#undef MOE_PF1
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || dt == DT_BF16) return err;
     return requant(dt, a_bf16, T, k, I, a, a_scale, st);
@@ -1048,21 +1124,22 @@ hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* 
                         int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int mbs = (int)(cap / B);
-  if (dt != DT_FP4 && use_prefill(B, T, k, E, D, I)) {
+  if (use_prefill(dt, B, T, k, E, D, I)) {
     const dim3 grid(xcd_grid(mbs, (D + 255) / 256));
-#define MOE_PF2(F8, MD)                                                                                \
-  gemm_prefill_kernel<F8, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, static_cast<const float*>(a_scale), \
-                                                   (const uint8_t*)w2, static_cast<const float*>(w2_scale), \
-                                                   topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, \
-                                                   mbs, y, nullptr, 0)
+#define MOE_PF2(DTV, MD)                                                                                \
+  gemm_prefill_kernel<DTV, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,    \
+                                                    w2_scale, topk_w, sorted_ids, expert_ids, num_valid, \
+                                                    T, E, k, D, I, mbs, y, nullptr, 0)
 #define MOE_PF2_MODES(F8)                                   \
   if (mode == OM_REDUCE) MOE_PF2(F8, PF_G2_REDUCE);         \
   else if (mode == OM_ATOMIC) MOE_PF2(F8, PF_G2_ATOMIC);    \
   else MOE_PF2(F8, PF_G2_ATOMIC_BF16);
     if (dt == DT_FP8) {
-      MOE_PF2_MODES(true)
+      MOE_PF2_MODES(DT_FP8)
+    } else if (dt == DT_FP4) {
+      MOE_PF2_MODES(DT_FP4)
     } else {
-      MOE_PF2_MODES(false)
+      MOE_PF2_MODES(DT_BF16)
     }
 #undef MOE_PF2_MODES
 #undef MOE_PF2

@@ -120,6 +120,11 @@ SMALL_MX = [
     (37, 16, 4, 256, 640, 32),
     (61, 12, 3, 256, 512, 64),
     (300, 8, 2, 384, 384, 64),
+    # BLOCK_M = 64, T*k >= 32*E and D, I multiples of 256: the tiled prefill kernel with its
+    # staged block scales (runs of 1-4 blocks, a partial model_dim tile)
+    (300, 8, 2, 512, 256, 64),
+    (640, 8, 4, 256, 512, 64),
+    (256, 4, 2, 1024, 768, 64),
 ]
 SMALL = ([(*c, "bf16") for c in SMALL_BF16] + [(*c, "fp8") for c in SMALL_FP8] +
          [(*c, "mxfp4") for c in SMALL_MX])
@@ -236,6 +241,7 @@ FULL = [
     ("kimi", 16384, [0, 8191, 16383]),
     ("kimi_mxfp4", 64, [0, 33, 63]),
     ("kimi_mxfp4", 4096, [5, 2048, 4095]),
+    ("kimi_mxfp4", 16384, [0, 8191, 16383]),
 ]
 
 
