@@ -45,11 +45,18 @@ from .codecs import (
 )
 from .routing import (
     RouteResult,
+    aux_loss_scores,
+    aux_loss_scores_backward,
+    aux_loss_scores_f64,
+    group_scores,
     route,
+    route_grouped,
     routing_weights,
     routing_weights_backward,
     routing_weights_f64,
+    select_groups,
     select_topk,
+    select_topk_grouped,
     sort_slots,
     sorted_capacity,
 )
@@ -72,11 +79,18 @@ __all__ = [
     "E4M3_MAX",
     "MX_BLOCK",
     "RouteResult",
+    "aux_loss_scores",
+    "aux_loss_scores_backward",
+    "aux_loss_scores_f64",
+    "group_scores",
     "route",
+    "route_grouped",
     "routing_weights",
     "routing_weights_backward",
     "routing_weights_f64",
+    "select_groups",
     "select_topk",
+    "select_topk_grouped",
     "sort_slots",
     "sorted_capacity",
     "LayerResult",

@@ -203,3 +203,148 @@ def route(logits: np.ndarray, k: int, block_m: int, score: str = "softmax",
     cap = sorted_capacity(T, E, k, block_m)
     sids, eids, nv = sort_slots(ids, E, block_m, cap)
     return RouteResult(ids, w, sids, eids, nv, cap)
+
+
+def group_scores(logits: np.ndarray, k: int, n_group: int, topk_group: int,
+                 score: str = "softmax") -> np.ndarray:
+    """Score of each expert group, float64 [T, n_group] (group-limited routing).
+
+    "[Common] Optimize fused router forward/backward kernels" (TransformerEngine #3012),
+    "Hardening" (topk must be a multiple of group_topk) and the review's note on the group
+    scores of the forward kernels.  The pages give no formula; reading taken: the E experts
+    form n_group groups of E/n_group consecutive experts, and a group's score is the sum of
+    its m = k/topk_group largest expert scores (softmax over all E, or the sigmoid), added
+    best first.
+    """
+    if score not in SCORES:
+        raise ValueError(f"score must be one of {SCORES}")
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    T, E = l.shape
+    _check_groups(E, k, n_group, topk_group)
+    m = k // topk_group
+    p = _scores_f64(l, score)
+    gs = np.zeros((T, n_group))
+    size = E // n_group
+    for t in range(T):
+        for g in range(n_group):
+            vals = p[t, g * size:(g + 1) * size]
+            order = np.argsort(-vals, kind="stable")
+            for r in range(m):
+                gs[t, g] += vals[order[r]]
+    return gs
+
+
+def _check_groups(E: int, k: int, n_group: int, topk_group: int) -> None:
+    if not (1 <= k <= E):
+        raise ValueError("topk must lie in [1, E]")
+    if n_group < 1 or E % n_group:
+        raise ValueError("n_group must divide E")
+    if not (1 <= topk_group <= n_group):
+        raise ValueError("topk_group must lie in [1, n_group]")
+    if k % topk_group:
+        raise ValueError("topk must be a multiple of topk_group")
+    if k > topk_group * (E // n_group):
+        raise ValueError("the kept groups must hold at least topk experts")
+
+
+def select_groups(gs: np.ndarray, topk_group: int) -> np.ndarray:
+    """The topk_group groups with the largest scores per token, ties to the lower group
+    index; bool [T, n_group]."""
+    T, G = gs.shape
+    order = np.argsort(-gs, axis=1, kind="stable")
+    keep = np.zeros((T, G), dtype=bool)
+    np.put_along_axis(keep, order[:, :topk_group], True, axis=1)
+    return keep
+
+
+def select_topk_grouped(logits: np.ndarray, k: int, n_group: int, topk_group: int,
+                        score: str = "softmax") -> np.ndarray:
+    """Group-limited top-k: the k best experts among the topk_group best groups.
+
+    Reading (see group_scores): first the groups are ranked by their score and the best
+    topk_group kept; the experts of the other groups are then excluded and the k largest
+    logits among the rest are picked, best first, ties to the lower expert index.
+    n_group = 1 (or topk_group = n_group) is the ungrouped select_topk.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    gs = group_scores(logits, k, n_group, topk_group, score)
+    keep = select_groups(gs, topk_group)
+    allowed = np.repeat(keep, E // n_group, axis=1)
+    neg = np.where(allowed, -logits.astype(np.float64), np.inf)
+    order = np.argsort(neg, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def route_grouped(logits: np.ndarray, k: int, block_m: int, n_group: int, topk_group: int,
+                  score: str = "softmax", renorm: bool = True) -> RouteResult:
+    """Routing with group-limited selection; weights and sort as in route()."""
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if T * E > 2**31 - 1:
+        raise ValueError("tokens*experts must fit in int32")
+    ids = select_topk_grouped(logits, k, n_group, topk_group, score)
+    w = routing_weights(logits, ids, score, renorm)
+    cap = sorted_capacity(T, E, k, block_m)
+    sids, eids, nv = sort_slots(ids, E, block_m, cap)
+    return RouteResult(ids, w, sids, eids, nv, cap)
+
+
+def aux_loss_scores(logits: np.ndarray, k: int, score: str = "softmax"):
+    """Per-token expert scores and routing map for the load-balancing auxiliary loss.
+
+    "[Common] Optimize fused router forward/backward kernels" (TransformerEngine #3012):
+    the summary and the file table name a kernel computing the scores for the MoE
+    auxiliary loss, forward and backward, benchmarked beside the top-k kernel.  The pages
+    give no formula; reading taken: the balance loss averages a distribution over the
+    experts per token and counts the tokens routed to each expert, so
+    * scores [T, E] float64: softmax over all E; or the sigmoid divided by its sum over
+      all E (a distribution as well);
+    * routing map [T, E] bool: True at the token's top-k experts (select_topk).
+    """
+    l = np.asarray(logits, dtype=np.float32)
+    T, E = l.shape
+    ids = select_topk(l, k)
+    rmap = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(rmap, ids.astype(np.int64), True, axis=1)
+    return aux_loss_scores_f64(l.astype(np.float64), score), rmap
+
+
+def aux_loss_scores_f64(logits: np.ndarray, score: str = "softmax") -> np.ndarray:
+    """The scores of aux_loss_scores from float64 logits, unrounded."""
+    if score not in SCORES:
+        raise ValueError(f"score must be one of {SCORES}")
+    s = _scores_f64(np.asarray(logits, dtype=np.float64), score)
+    if score == "sigmoid":
+        s = s / s.sum(axis=1, keepdims=True)
+    return s
+
+
+def aux_loss_scores_backward(logits: np.ndarray, grad_scores: np.ndarray,
+                             score: str = "softmax") -> np.ndarray:
+    """Gradient of aux_loss_scores' scores with respect to the logits, float64 [T, E].
+
+    Written as the Jacobian of the scores contracted with grad_scores, entry by entry:
+    * softmax: dp_e/dl_c = p_e (d_ec - p_c);
+    * normalised sigmoid, q_e = s_e / S with S = sum_i s_i:
+      dq_e/dl_c = s_c (1 - s_c) (d_ec - q_e) / S.
+    The routing map is piecewise constant and passes no gradient.
+    """
+    if score not in SCORES:
+        raise ValueError(f"score must be one of {SCORES}")
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    g = np.asarray(grad_scores, dtype=np.float64)
+    T, E = l.shape
+    out = np.zeros((T, E))
+    eye = np.eye(E)
+    for t in range(T):
+        if score == "softmax":
+            p = _scores_f64(l[t:t + 1], "softmax")[0]
+            jac = p[:, None] * (eye - p[None, :])          # [e, c]
+        else:
+            s = 1.0 / (1.0 + np.exp(-l[t]))
+            S = s.sum()
+            q = s / S
+            jac = (eye - q[:, None]) * (s * (1.0 - s))[None, :] / S
+        out[t] = g[t] @ jac
+    return out
