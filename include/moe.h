@@ -130,6 +130,29 @@ int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score
                           int32_t* sorted_token_ids, int64_t sorted_cap, int32_t* expert_ids,
                           int32_t* num_valid, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- group-limited routing
+ * [P3] "Hardening" (topk must be a multiple of group_topk) and the review's group scores of
+ * the forward kernels: top-k limited to the best groups of experts.  The E experts form
+ * n_group groups of E/n_group consecutive experts.  A group's score is the sum of its
+ * m = topk/topk_group largest expert scores (softmax over all E, or the sigmoid; fp64,
+ * best first); the topk_group groups with the largest scores are kept (ties to the lower
+ * group index) and the top-k of the logits is taken among their experts, as in
+ * moe_topk_softmax_sort.  Weights, sort and outputs are those of moe_topk_softmax_sort
+ * (with renorm = 0 and softmax the weight is still the softmax over all E).  Group
+ * decisions depend on fp64 sums; two groups whose scores agree to rounding may be ranked
+ * either way.
+ *   n_group     >= 1, divides E; 1 (or topk_group = n_group) is the plain top-k
+ *   topk_group  in [1, n_group]; topk % topk_group == 0 and topk <= topk_group * E/n_group,
+ *               else MOE_EINVAL
+ * Group-limited selection needs n_group <= 64 and E <= 4096 (MOE_EUNSUPPORTED otherwise).
+ * Workspace and capacity as for moe_topk_softmax_sort. */
+int moe_topk_softmax_sort_grouped(const float* logits, int T, int E, int topk, int n_group,
+                                  int topk_group, int score, int renorm, int block_m,
+                                  float* topk_weights, int32_t* topk_ids,
+                                  int32_t* sorted_token_ids, int64_t sorted_cap,
+                                  int32_t* expert_ids, int32_t* num_valid, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- routing backward
  * [P3] "Changes / Backward kernels" and the summary's "Backward (E=2304, K=36)": the fused
  * router's backward.  The gradient of the weights moe_topk_softmax_sort returned, with
@@ -152,6 +175,31 @@ int moe_topk_softmax_backward(const float* logits, const int32_t* topk_ids,
                               const float* topk_weights, const float* grad_topk_weights, int T,
                               int E, int topk, int score, int renorm, float* grad_logits,
                               void* stream);
+
+/* ---------------------------------------------------------------- auxiliary-loss scores
+ * [P3] the summary, the "aux_loss fprop / bprop" benchmark rows and the file table: the
+ * router kernel that computes the scores of the load-balancing auxiliary loss, forward and
+ * backward.  Per token, over all E experts:
+ *   scores       fp32  [T, E]  out: softmax of the logits, or the sigmoids divided by
+ *                              their sum (score = MOE_SCORE_SIGMOID); each row sums to 1
+ *   routing_map  uint8 [T, E]  out: 1 at the token's topk experts (largest logits, ties
+ *                              to the lower index, as moe_topk_softmax_sort), else 0
+ *   logits       fp32  [T, E]  in
+ * Accuracy: relative error of a few fp32 ulp per score for any logit range.
+ * Validation: topk in [1, E], E <= 4096 (else MOE_EUNSUPPORTED), T*E within int32, pointers
+ * non-null and 16-byte aligned when T > 0.  T = 0 writes nothing. */
+int moe_aux_loss_scores(const float* logits, int T, int E, int topk, int score, float* scores,
+                        uint8_t* routing_map, void* stream);
+
+/* Gradient of moe_aux_loss_scores' scores with respect to the logits (the routing map is
+ * piecewise constant and passes none).  g = grad_scores, p the softmax, s the sigmoids,
+ * S = sum_e s_e, q = s / S:
+ *   softmax:  dl_c = p_c (g_c - sum_e p_e g_e)
+ *   sigmoid:  dl_c = s_c (1 - s_c) / S * (g_c - sum_e q_e g_e)
+ *   logits, grad_scores  fp32 [T, E] in;  grad_logits  fp32 [T, E] out, every element.
+ * fp32 arithmetic with fp64 sums.  Validation as for moe_aux_loss_scores. */
+int moe_aux_loss_scores_backward(const float* logits, const float* grad_scores, int T, int E,
+                                 int score, float* grad_logits, void* stream);
 
 /* ---------------------------------------------------------------- stage 1
  * [P2] gate-up helper and stage-1 commits ("silu(gate)*up with optional fp8

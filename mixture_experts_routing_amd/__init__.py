@@ -27,6 +27,9 @@ __all__ = [
     "moe_gemm2_down",
     "moe_finalize",
     "moe_topk_softmax_backward",
+    "moe_topk_softmax_sort_grouped",
+    "moe_aux_loss_scores",
+    "moe_aux_loss_scores_backward",
     "moe_forward",
     "SCORE",
     "DTYPE",
@@ -65,6 +68,10 @@ _SIGS = {
     "moe_topk_softmax_sort": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "moe_gemm1_gateup": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_topk_softmax_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_topk_softmax_sort_grouped": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _P, _P, _P,
+                                           _SZ, _P]),
+    "moe_aux_loss_scores": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_aux_loss_scores_backward": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "moe_gemm2_down": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_finalize": (_I, [_I, _P, _I, _I, _I, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P, _P]),
@@ -130,9 +137,7 @@ def moe_forward_workspace_layout(dtype: str, mode: str, T: int, E: int, topk: in
     return total, {f: (None if offs[i] < 0 else offs[i]) for i, f in enumerate(WS_FIELDS)}
 
 
-def moe_topk_softmax_sort(logits: torch.Tensor, topk: int, block_m: int, score: str = "softmax",
-                          renorm: bool = True, out: dict | None = None, workspace=None, stream=None):
-    """Routing outputs: dict(topk_weights, topk_ids, sorted_token_ids, expert_ids, num_valid)."""
+def _route_buffers(logits, topk, block_m, out, workspace):
     T, E = logits.shape
     dev = logits.device
     cap = moe_sorted_capacity(T, E, topk, block_m)
@@ -148,12 +153,60 @@ def moe_topk_softmax_sort(logits: torch.Tensor, topk: int, block_m: int, score: 
         nbytes = moe_route_workspace_bytes(T, E, topk, block_m)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return out, workspace, ws_bytes
+
+
+def moe_topk_softmax_sort(logits: torch.Tensor, topk: int, block_m: int, score: str = "softmax",
+                          renorm: bool = True, out: dict | None = None, workspace=None, stream=None):
+    """Routing outputs: dict(topk_weights, topk_ids, sorted_token_ids, expert_ids, num_valid)."""
+    T, E = logits.shape
+    out, workspace, ws_bytes = _route_buffers(logits, topk, block_m, out, workspace)
     _check(load_library().moe_topk_softmax_sort(
         _ptr(logits), T, E, topk, SCORE[score], int(renorm), block_m, _ptr(out["topk_weights"]),
         _ptr(out["topk_ids"]), _ptr(out["sorted_token_ids"]), out["sorted_token_ids"].numel(),
         _ptr(out["expert_ids"]), _ptr(out["num_valid"]), _ptr(workspace), ws_bytes, _stream(stream)),
         "moe_topk_softmax_sort")
     return out
+
+
+def moe_topk_softmax_sort_grouped(logits: torch.Tensor, topk: int, n_group: int, topk_group: int,
+                                  block_m: int, score: str = "softmax", renorm: bool = True,
+                                  out: dict | None = None, workspace=None, stream=None):
+    """Group-limited routing; outputs as moe_topk_softmax_sort."""
+    T, E = logits.shape
+    out, workspace, ws_bytes = _route_buffers(logits, topk, block_m, out, workspace)
+    _check(load_library().moe_topk_softmax_sort_grouped(
+        _ptr(logits), T, E, topk, n_group, topk_group, SCORE[score], int(renorm), block_m,
+        _ptr(out["topk_weights"]), _ptr(out["topk_ids"]), _ptr(out["sorted_token_ids"]),
+        out["sorted_token_ids"].numel(), _ptr(out["expert_ids"]), _ptr(out["num_valid"]),
+        _ptr(workspace), ws_bytes, _stream(stream)), "moe_topk_softmax_sort_grouped")
+    return out
+
+
+def moe_aux_loss_scores(logits, topk: int, score: str = "softmax", scores=None, routing_map=None,
+                        stream=None):
+    """Auxiliary-loss scores fp32 [T, E] and routing map bool [T, E]."""
+    T, E = logits.shape
+    if scores is None:
+        scores = torch.empty(T, E, dtype=torch.float32, device=logits.device)
+    if routing_map is None:
+        routing_map = torch.empty(T, E, dtype=torch.bool, device=logits.device)
+    _check(load_library().moe_aux_loss_scores(
+        _ptr(logits), T, E, topk, SCORE[score], _ptr(scores), _ptr(routing_map), _stream(stream)),
+        "moe_aux_loss_scores")
+    return scores, routing_map
+
+
+def moe_aux_loss_scores_backward(logits, grad_scores, score: str = "softmax", grad_logits=None,
+                                 stream=None):
+    """Gradient of the auxiliary-loss scores with respect to the logits: fp32 [T, E]."""
+    T, E = logits.shape
+    if grad_logits is None:
+        grad_logits = torch.empty(T, E, dtype=torch.float32, device=logits.device)
+    _check(load_library().moe_aux_loss_scores_backward(
+        _ptr(logits), _ptr(grad_scores), T, E, SCORE[score], _ptr(grad_logits), _stream(stream)),
+        "moe_aux_loss_scores_backward")
+    return grad_logits
 
 
 def moe_topk_softmax_backward(logits, topk_ids, topk_weights, grad_topk_weights, score: str = "softmax",

@@ -133,11 +133,25 @@ int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk
   return L.total;
 }
 
-int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score, int renorm,
-                          int block_m, float* topk_weights, int32_t* topk_ids,
-                          int32_t* sorted_token_ids, int64_t sorted_cap, int32_t* expert_ids,
-                          int32_t* num_valid, void* workspace, size_t ws_bytes, void* stream) {
+// [P3] "Hardening": topk a multiple of group_topk.  A selection over the kept groups needs
+// at least topk experts in them.
+static int check_groups(int E, int topk, int n_group, int topk_group) {
+  if (n_group < 1 || E % n_group) return MOE_EINVAL;
+  if (topk_group < 1 || topk_group > n_group) return MOE_EINVAL;
+  if (topk % topk_group) return MOE_EINVAL;
+  if ((int64_t)topk > (int64_t)topk_group * (E / n_group)) return MOE_EINVAL;
+  if (moe::route_is_grouped(E, n_group, topk_group) && (n_group > 64 || E > 4096))
+    return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+static int route_impl(const float* logits, int T, int E, int topk, int n_group, int topk_group,
+                      int score, int renorm, int block_m, float* topk_weights, int32_t* topk_ids,
+                      int32_t* sorted_token_ids, int64_t sorted_cap, int32_t* expert_ids,
+                      int32_t* num_valid, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_route_dims(T, E, topk, block_m);
+  if (st) return st;
+  st = check_groups(E, topk, n_group, topk_group);
   if (st) return st;
   if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
   if (renorm != 0 && renorm != 1) return MOE_EINVAL;
@@ -152,9 +166,58 @@ int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score
   if ((int64_t)ws_bytes < need) return MOE_ENOSPC;
   if (need > 0 && !ok_ptr(workspace)) return MOE_EINVAL;
   const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
-  return launch_status(moe::launch_route(logits, T, E, topk, score, renorm, block_m, topk_weights,
-                                         topk_ids, sorted_token_ids, cap, expert_ids, num_valid,
-                                         workspace, (hipStream_t)stream));
+  return launch_status(moe::launch_route(logits, T, E, topk, score, renorm, n_group, topk_group,
+                                         block_m, topk_weights, topk_ids, sorted_token_ids, cap,
+                                         expert_ids, num_valid, workspace, (hipStream_t)stream));
+}
+
+int moe_topk_softmax_sort(const float* logits, int T, int E, int topk, int score, int renorm,
+                          int block_m, float* topk_weights, int32_t* topk_ids,
+                          int32_t* sorted_token_ids, int64_t sorted_cap, int32_t* expert_ids,
+                          int32_t* num_valid, void* workspace, size_t ws_bytes, void* stream) {
+  return route_impl(logits, T, E, topk, 1, 1, score, renorm, block_m, topk_weights, topk_ids,
+                    sorted_token_ids, sorted_cap, expert_ids, num_valid, workspace, ws_bytes,
+                    stream);
+}
+
+int moe_topk_softmax_sort_grouped(const float* logits, int T, int E, int topk, int n_group,
+                                  int topk_group, int score, int renorm, int block_m,
+                                  float* topk_weights, int32_t* topk_ids,
+                                  int32_t* sorted_token_ids, int64_t sorted_cap,
+                                  int32_t* expert_ids, int32_t* num_valid, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  return route_impl(logits, T, E, topk, n_group, topk_group, score, renorm, block_m,
+                    topk_weights, topk_ids, sorted_token_ids, sorted_cap, expert_ids, num_valid,
+                    workspace, ws_bytes, stream);
+}
+
+static int check_aux_dims(int T, int E, int topk) {
+  if (T < 0 || E < 1) return MOE_EINVAL;
+  if (topk < 1 || topk > E) return MOE_EINVAL;
+  if (E > 4096) return MOE_EUNSUPPORTED;
+  if ((int64_t)T * E > INT_MAX) return MOE_ERANGE;
+  return MOE_OK;
+}
+
+int moe_aux_loss_scores(const float* logits, int T, int E, int topk, int score, float* scores,
+                        uint8_t* routing_map, void* stream) {
+  const int st = check_aux_dims(T, E, topk);
+  if (st) return st;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (T > 0 && (!ok_ptr(logits) || !ok_ptr(scores) || !ok_ptr(routing_map))) return MOE_EINVAL;
+  return launch_status(
+      moe::launch_aux_scores(logits, T, E, topk, score, scores, routing_map, (hipStream_t)stream));
+}
+
+int moe_aux_loss_scores_backward(const float* logits, const float* grad_scores, int T, int E,
+                                 int score, float* grad_logits, void* stream) {
+  const int st = check_aux_dims(T, E, 1);
+  if (st) return st;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (T > 0 && (!ok_ptr(logits) || !ok_ptr(grad_scores) || !ok_ptr(grad_logits)))
+    return MOE_EINVAL;
+  return launch_status(moe::launch_aux_scores_backward(logits, grad_scores, T, E, score,
+                                                       grad_logits, (hipStream_t)stream));
 }
 
 static int check_gemm_common(int dtype, int T, int E, int topk, int D, int I, int block_m,
@@ -270,8 +333,8 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   hipStream_t s = (hipStream_t)stream;
 
   // the atomic accumulator is cleared by the gate-up kernel's blocks on their way in
-  hipError_t e = moe::launch_route(logits, T, E, topk, score, renorm, block_m, topk_w, topk_ids, sorted,
-                          cap, eids, nvalid, rws, s);
+  hipError_t e = moe::launch_route(logits, T, E, topk, score, renorm, 1, 1, block_m, topk_w, topk_ids,
+                                   sorted, cap, eids, nvalid, rws, s);
   if (e == hipSuccess)
     e = moe::launch_gemm1(dtype, x, x_scale, w1, w1_scale, sorted, eids, nvalid, cap, T, E, topk,
                           D, I, block_m, a, a_scale, g1ws, zero, zero_n, s);

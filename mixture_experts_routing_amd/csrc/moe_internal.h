@@ -26,9 +26,20 @@ bool route_is_oneshot(int T, int E, int k);
 bool route_is_twostage(int T, int E, int k);
 int64_t route_workspace_bytes(int T, int E, int k);
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int score, int renorm, int B,
-                        float* topk_w, int32_t* topk_ids, int32_t* sorted_ids, int64_t cap,
-                        int32_t* expert_ids, int32_t* num_valid, void* ws, hipStream_t st);
+// Group-limited selection runs when n_group > 1 and topk_group < n_group (n_group = 1 is the
+// plain top-k); requires n_group <= 64, E <= 4096, E % n_group == 0, k % topk_group == 0.
+bool route_is_grouped(int E, int n_group, int topk_group);
+hipError_t launch_route(const float* logits, int T, int E, int k, int score, int renorm,
+                        int n_group, int topk_group, int B, float* topk_w, int32_t* topk_ids,
+                        int32_t* sorted_ids, int64_t cap, int32_t* expert_ids,
+                        int32_t* num_valid, void* ws, hipStream_t st);
+
+// Auxiliary-loss scores (E <= 4096): scores [T, E] fp32 and routing map [T, E] bytes; and
+// the gradient of the scores with respect to the logits.
+hipError_t launch_aux_scores(const float* logits, int T, int E, int k, int score, float* scores,
+                             uint8_t* routing_map, hipStream_t st);
+hipError_t launch_aux_scores_backward(const float* logits, const float* grad_scores, int T, int E,
+                                      int score, float* grad_logits, hipStream_t st);
 
 hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* w1,
                         const void* w1_scale, const int32_t* sorted_ids,

@@ -4,18 +4,11 @@
 // top-k gating softmax and the MoE sorting step run as one launch for decode-sized
 // token counts.  [P3] "Optimize fused router forward/backward kernels"
 // (NVIDIA/TransformerEngine #3012), "Changes / Forward kernels": score function,
-// then top-k selection, with a cheaper path for small k.
+// then top-k selection, with a cheaper path for small k; "Hardening": group-limited
+// routing (topk a multiple of group_topk).
 //
 // Design (gfx950, wave64):
-//  * one wavefront per token.  Lane l holds the logits of experts l, l+64, ...
-//    as order-preserving u32 keys.
-//  * selection: the lanes form G groups (G the power of two >= 2k, at most 64); the
-//    k-th largest of the G group maxima is a threshold that at least k keys reach.
-//    The keys at or above it (typically a few to a few dozen) are compacted into LDS
-//    (a ballot per register gives each lane its slot), and each candidate's rank is
-//    the number of larger (key, ~expert) pairs among them.  All cross-lane steps are
-//    DPP/permlane exchanges or scalar broadcasts.  If more than 128 keys reach the
-//    threshold (heavy ties) or k > 64, a slower exact path extracts the maximum k times.
+//  * one wavefront per token; the selection (plain or group-limited) is in route_select.h.
 //  * sort: experts are ranked per token in descending order, slots s = t*k + j.
 //    A token never picks an expert twice, so a slot's rank inside its expert's
 //    list is the number of earlier tokens that picked the same expert.  Waves
@@ -30,181 +23,9 @@
 //    offsets and writes the block experts (four launches, 64-token chunks).
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_select.h"
 
 namespace moe {
-
-constexpr int kMaxCand = 128;
-
-// Weight arithmetic runs in fp64 and is rounded to fp32 once: exp of an fp32
-// logit difference loses |l - m| * 2^-24 relative accuracy in fp32, which for
-// wide logit ranges exceeds the 1e-6 contract.
-__device__ __forceinline__ double score_of(double l, double m, bool softmax) {
-  return softmax ? exp(l - m) : 1.0 / (1.0 + exp(-l));
-}
-
-// Softmax denominator over all E logits of the token (only for softmax without
-// renormalisation): sum exp(l - max).  Empty slots hold NaN.
-template <int NV>
-__device__ double full_softmax_denominator(const float (&x)[NV], double m) {
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (x[i] == x[i]) s += exp((double)x[i] - m);
-  return wave_sum_f64(s);
-}
-
-// Exact selection for heavy ties (more than 128 keys at the threshold) and k > 64: the
-// maximum (key, ~expert) pair strictly below the previous pick, k times, 64 ranks per
-// pass.  Reads the row again from memory and keeps no per-register state, so that it does
-// not raise the register budget of the common path.  The picked logit is parked in w_out
-// and turned into the weight once the denominator is known.
-template <int NV, class OnPick>
-__device__ void select_token_exact(const float* __restrict__ row, int E, int k,
-                                                bool softmax, int renorm,
-                                                float* __restrict__ w_out,
-                                                int32_t* __restrict__ id_out, OnPick on_pick) {
-  const int lane = lane_id();
-  double m = 0.0, denom_all = 1.0, part = 0.0;
-  uint64_t prev = ~0ull;
-  for (int p = 0; p * 64 < k; ++p) {
-    uint64_t mine = 0;
-    const int nr = min(64, k - p * 64);
-    for (int jj = 0; jj < nr; ++jj) {
-      uint64_t best = 0;
-#pragma unroll 4
-      for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E) {
-          const uint64_t pk = pick_key(logit_key(row[e]), e);
-          if (pk < prev && pk > best) best = pk;
-        }
-      }
-      best = wave_max_u64(best);
-      if (p == 0 && jj == 0) {
-        m = (double)key_logit(pick_logit_key(best));
-        if (softmax && !renorm) {
-          double s = 0.0;
-#pragma unroll 4
-          for (int i = 0; i < NV; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E) s += exp((double)row[e] - m);
-          }
-          denom_all = wave_sum_f64(s);
-        }
-      }
-      prev = best;
-      if (lane == jj) mine = best;
-    }
-    if (lane < nr) {
-      const int r = p * 64 + lane;
-      const float l = key_logit(pick_logit_key(mine));
-      part += score_of((double)l, m, softmax);
-      const int e = pick_expert(mine);
-      w_out[r] = l;
-      id_out[r] = e;
-      on_pick(r, e);
-    }
-  }
-  double denom = 1.0;
-  if (renorm) denom = wave_sum_f64(part);
-  else if (softmax) denom = denom_all;
-  for (int r = lane; r < k; r += 64)  // same lane parked w_out[r]
-    w_out[r] = (float)(score_of((double)w_out[r], m, softmax) / denom);
-}
-
-// Selects the top-k experts of one token (row of E logits) with the calling wave.
-// Writes topk weights/ids for ranks 0..k-1 and calls on_pick(rank, expert) once per
-// rank, on the lane that owns it.
-template <int NV, class OnPick>
-__device__ void select_token(const float* __restrict__ row, int E, int k, int score, int renorm,
-                             uint64_t* __restrict__ cand, float* __restrict__ w_out,
-                             int32_t* __restrict__ id_out, OnPick on_pick) {
-  const int lane = lane_id();
-  const bool softmax = score == 0;
-  if (k <= 64) {
-    // lane l holds experts l, l+64, ...; empty slots hold NaN, which no comparison selects
-    float x[NV];
-    const float* rl = row + lane;
-    if (E == 64 * NV) {  // every register full (wave-uniform): unpredicated loads
-#pragma unroll
-      for (int i = 0; i < NV; ++i) x[i] = __builtin_nontemporal_load(rl + 64 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        x[i] = lane + 64 * i < E ? __builtin_nontemporal_load(rl + 64 * i) : __builtin_nanf("");
-    }
-    float lm = x[0];
-#pragma unroll
-    for (int i = 1; i < NV; ++i) lm = fmaxf(lm, x[i]);
-    // threshold: k-th largest of the G group maxima (as order-preserving keys, 0 = empty)
-    uint32_t lk = lm == lm ? logit_key(lm) : 0u;
-    int G = 2;
-    while (G < 2 * k && G < 64) G <<= 1;
-    const int L = 64 / G;
-#pragma unroll
-    for (int mm = 1; mm < 64; mm <<= 1)
-      if (mm < L) {
-        const uint32_t o = shfl_xor_u32(lk, mm);
-        lk = o > lk ? o : lk;
-      }
-    const uint32_t srt = bitonic64_desc_grouped(lk, L);
-    const uint32_t top = readlane_u32(srt, 0);  // the token's largest key
-    const uint32_t tk = readlane_u32(srt, (k - 1) * L);
-    const float tau = tk == 0u ? -__builtin_inff() : key_logit(tk);
-    // compaction of the logits >= tau: a ballot per register gives each lane its slot
-    int c = 0;  // wave-uniform
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const bool p = x[i] >= tau;
-      const uint64_t mask = __ballot(p);
-      if (mask) {
-        const int pos = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (p && pos < kMaxCand) cand[pos] = pick_key(logit_key(x[i]), lane + 64 * i);
-        c += __popcll(mask);
-      }
-    }
-    if (c <= kMaxCand) {
-      wave_lds_sync();
-      const uint64_t v0 = lane < c ? cand[lane] : 0ull;
-      const uint64_t v1 = lane + 64 < c ? cand[lane + 64] : 0ull;
-      // rank = number of larger candidates (broadcast reads); pick keys are distinct
-      int r0 = 0, r1 = 0;
-      if (c <= 64) {
-        for (int i = 0; i < c; ++i) r0 += cand[i] > v0;
-      } else {
-        for (int i = 0; i < c; ++i) {
-          const uint64_t o = cand[i];
-          r0 += o > v0;
-          r1 += o > v1;
-        }
-      }
-      wave_lds_sync();  // the candidate buffer is reused by the next token
-      const bool in0 = lane < c && r0 < k, in1 = lane + 64 < c && r1 < k;
-      const double m = (double)key_logit(top);
-      const double sc0 = in0 ? score_of((double)key_logit(pick_logit_key(v0)), m, softmax) : 0.0;
-      const double sc1 = in1 ? score_of((double)key_logit(pick_logit_key(v1)), m, softmax) : 0.0;
-      double denom = 1.0;
-      if (renorm) denom = wave_sum_f64(sc0 + sc1);
-      else if (softmax) denom = full_softmax_denominator<NV>(x, m);
-      if (in0) {
-        const int e = pick_expert(v0);
-        w_out[r0] = (float)(sc0 / denom);
-        id_out[r0] = e;
-        on_pick(r0, e);
-      }
-      if (in1) {
-        const int e = pick_expert(v1);
-        w_out[r1] = (float)(sc1 / denom);
-        id_out[r1] = e;
-        on_pick(r1, e);
-      }
-      return;
-    }
-    wave_lds_sync();
-  }
-  select_token_exact<NV>(row, E, k, softmax, renorm, w_out, id_out, on_pick);
-}
 
 // Sentinel fill of sorted_ids [cap) and -1 fill of expert_ids [cap/B): share `part` of
 // `nparts`, written with nthreads threads (int4 stores; cap is a multiple of B >= 16).
@@ -277,12 +98,13 @@ __device__ int block_prefix_scan(uint8_t* s_hist, int32_t* s_cnt, int32_t* s_off
 
 // ----------------------------------------------------------------------------- single workgroup
 // Dynamic LDS: cand [16][128] u64 | hist [16][E4] u8 | cnt [E4] i32 | off [E4] i32 |
-//              wsum [20] i32 | ids [T*k] i32
-template <int NV>
+//              wsum [20] i32 | ids [T*k] i32 | (GROUPED) keys [16][E4] u32
+template <int NV, bool GROUPED>
 __global__ void __launch_bounds__(1024) route_oneshot_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int score, int renorm, int B,
-    float* __restrict__ topk_w, int32_t* __restrict__ topk_ids, int32_t* __restrict__ sorted_ids,
-    int cap, int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_valid) {
+    const float* __restrict__ logits, int T, int E, int k, int score, int renorm, GroupSel gs,
+    int B, float* __restrict__ topk_w, int32_t* __restrict__ topk_ids,
+    int32_t* __restrict__ sorted_ids, int cap, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ num_valid) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* s_cand = reinterpret_cast<uint64_t*>(smem);
   uint8_t* s_hist = smem + 16 * kMaxCand * sizeof(uint64_t);
@@ -293,6 +115,7 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
   int32_t* s_ids = s_wsum + 20;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  if constexpr (GROUPED) gs.keys = reinterpret_cast<uint32_t*>(s_ids + T * k) + w * E4;
   const int sentinel = T * k;
   prefill_share(sorted_ids, cap, expert_ids, B, sentinel, 0, 1, tid, 1024);
   for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
@@ -303,11 +126,12 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
   const int t0 = w * tw, t1 = min(T, t0 + tw);
   uint8_t* my_hist = s_hist + w * E4;
   for (int t = t0; t < t1; ++t) {
-    select_token<NV>(logits + (size_t)t * E, E, k, score, renorm, s_cand + w * kMaxCand,
-                     topk_w + (size_t)t * k, topk_ids + (size_t)t * k, [&](int r, int e) {
-                       s_ids[t * k + r] = e;
-                       if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
-                     });
+    select_token<NV, GROUPED, true>(logits + (size_t)t * E, E, k, score, renorm, gs,
+                                    s_cand + w * kMaxCand, topk_w + (size_t)t * k,
+                                    topk_ids + (size_t)t * k, [&](int r, int e) {
+                                      s_ids[t * k + r] = e;
+                                      if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
+                                    });
     wave_lds_sync();
   }
   __threadfence();  // the fill stores complete before any slot is written over them
@@ -333,22 +157,25 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
 
 // ----------------------------------------------------------------------------- multi workgroup
 // One token per wave; each workgroup also writes one share of the sentinel / -1 fill of
-// sorted_ids and expert_ids.
-template <int NV>
+// sorted_ids and expert_ids.  Dynamic LDS (GROUPED): keys [4][E4] u32.
+template <int NV, bool GROUPED>
 __global__ void __launch_bounds__(256) route_select_kernel(const float* __restrict__ logits,
                                                            int T, int E, int k, int score,
-                                                           int renorm, int B, int cap,
-                                                           float* __restrict__ topk_w,
+                                                           int renorm, GroupSel gs, int B,
+                                                           int cap, float* __restrict__ topk_w,
                                                            int32_t* __restrict__ topk_ids,
                                                            int32_t* __restrict__ sorted_ids,
                                                            int32_t* __restrict__ expert_ids) {
   __shared__ uint64_t s_cand[4][kMaxCand];
+  extern __shared__ __align__(16) unsigned char s_dyn[];
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
   prefill_share(sorted_ids, cap, expert_ids, B, T * k, blockIdx.x, gridDim.x, threadIdx.x, 256);
   if (t >= T) return;
-  select_token<NV>(logits + (size_t)t * E, E, k, score, renorm, s_cand[w],
-                   topk_w + (size_t)t * k, topk_ids + (size_t)t * k, [](int, int) {});
+  if constexpr (GROUPED) gs.keys = reinterpret_cast<uint32_t*>(s_dyn) + w * ((E + 3) & ~3);
+  select_token<NV, GROUPED, true>(logits + (size_t)t * E, E, k, score, renorm, gs, s_cand[w],
+                                  topk_w + (size_t)t * k, topk_ids + (size_t)t * k,
+                                  [](int, int) {});
 }
 
 // Single-workgroup sort after the select kernel (T <= kSort1MaxT, E <= kSort1MaxE): 16
@@ -571,64 +398,110 @@ int64_t route_workspace_bytes(int T, int E, int k) {
   return align256(nchunks * E * 4) + align256((int64_t)E * 4) * 2 + align256(128 * 4);
 }
 
-template <int NV>
+template <int NV, bool GROUPED>
 static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int score, int renorm,
-                                  int B, float* topk_w, int32_t* topk_ids, int32_t* sorted_ids,
-                                  int64_t cap, int32_t* expert_ids, int32_t* num_valid, void* ws,
-                                  hipStream_t st) {
-  const int E4 = (E + 3) & ~3;
-  if (route_is_oneshot(T, E, k)) {
-    if constexpr (NV <= kOneShotMaxE / 64) {
-      // at most 16 KB + 24 KB + 80 B + 16 KB (E <= 1024, T*k <= 4096): below the 64 KB default
-      const size_t lds = 16 * kMaxCand * sizeof(uint64_t) + 16 * (size_t)E4 + 2 * 4 * (size_t)E4 + 20 * 4 +
-                         4 * (size_t)T * k;
-      route_oneshot_kernel<NV><<<1, 1024, lds, st>>>(logits, T, E, k, score, renorm, B, topk_w,
-                                                     topk_ids, sorted_ids, (int)cap, expert_ids,
-                                                     num_valid);
+                                  const GroupSel& gs, int B, float* topk_w, int32_t* topk_ids,
+                                  int32_t* sorted_ids, int64_t cap, int32_t* expert_ids,
+                                  int32_t* num_valid, void* ws, hipStream_t st) {
+  if constexpr (GROUPED && NV > kGroupMaxE / 64) {
+    return hipErrorInvalidValue;
+  } else {
+    const int E4 = (E + 3) & ~3;
+    if (route_is_oneshot(T, E, k)) {
+      if constexpr (NV <= kOneShotMaxE / 64) {
+        // at most 16 KB + 24 KB + 80 B + 16 KB (E <= 1024, T*k <= 4096), plus 64 KB of keys
+        // for group-limited selection
+        const size_t lds = 16 * kMaxCand * sizeof(uint64_t) + 16 * (size_t)E4 + 2 * 4 * (size_t)E4 +
+                           20 * 4 + 4 * (size_t)T * k + (GROUPED ? 16 * 4 * (size_t)E4 : 0);
+        if (lds > 64 * 1024) {
+          const hipError_t err =
+              hipFuncSetAttribute((const void*)route_oneshot_kernel<NV, GROUPED>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (err != hipSuccess) return err;
+        }
+        route_oneshot_kernel<NV, GROUPED><<<1, 1024, lds, st>>>(
+            logits, T, E, k, score, renorm, gs, B, topk_w, topk_ids, sorted_ids, (int)cap,
+            expert_ids, num_valid);
+        return hipGetLastError();
+      }
+    }
+    // keys of 4 waves for group-limited selection (<= 64 KB for E <= 4096) beside the 4 KB
+    // of static candidate buffers
+    const size_t sel_lds = GROUPED ? 4 * 4 * (size_t)E4 : 0;
+    if (GROUPED && sel_lds + 4 * kMaxCand * sizeof(uint64_t) > 64 * 1024) {
+      const hipError_t err =
+          hipFuncSetAttribute((const void*)route_select_kernel<NV, GROUPED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
+      if (err != hipSuccess) return err;
+    }
+    if (route_is_twostage(T, E, k)) {
+      route_select_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
+          logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
+          expert_ids);
+      const size_t lds = 24 * (size_t)E4 + 20 * 4;  // <= 61.5 KB for E <= 2560
+      route_sort1_kernel<<<1, 1024, lds, st>>>(topk_ids, T, E, k, B, sorted_ids, expert_ids,
+                                               num_valid);
       return hipGetLastError();
     }
-  }
-  if (route_is_twostage(T, E, k)) {
-    route_select_kernel<NV><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, score, renorm, B, (int)cap,
-                                                          topk_w, topk_ids, sorted_ids, expert_ids);
-    const size_t lds = 24 * (size_t)E4 + 20 * 4;  // <= 61.5 KB for E <= 2560
-    route_sort1_kernel<<<1, 1024, lds, st>>>(topk_ids, T, E, k, B, sorted_ids, expert_ids, num_valid);
+    const int nch = (T + kChunkTokens - 1) / kChunkTokens;
+    char* wsb = reinterpret_cast<char*>(ws);
+    int32_t* cnt = reinterpret_cast<int32_t*>(wsb);
+    int32_t* tot = reinterpret_cast<int32_t*>(wsb + align256((int64_t)nch * E * 4));
+    int32_t* loff =
+        reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tot) + align256((int64_t)E * 4));
+    int32_t* gsum =
+        reinterpret_cast<int32_t*>(reinterpret_cast<char*>(loff) + align256((int64_t)E * 4));
+    route_select_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
+        logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
+        expert_ids);
+    route_count_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt);
+    route_colscan_kernel<<<(E + 63) / 64, 1024, 0, st>>>(cnt, nch, E, B, tot, loff, gsum);
+    const size_t lds = 16 * (size_t)E4;
+    if (lds > 64 * 1024) {
+      // byte histograms of 16 waves for E > 4096 need more than the default 64 KB of LDS
+      const hipError_t err = hipFuncSetAttribute((const void*)route_scatter_kernel,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+      if (err != hipSuccess) return err;
+    }
+    route_scatter_kernel<<<nch, 1024, lds, st>>>(topk_ids, T, E, k, B, nch, cnt, tot, loff,
+                                                 gsum, sorted_ids, expert_ids, num_valid);
     return hipGetLastError();
   }
-  const int nch = (T + kChunkTokens - 1) / kChunkTokens;
-  char* wsb = reinterpret_cast<char*>(ws);
-  int32_t* cnt = reinterpret_cast<int32_t*>(wsb);
-  int32_t* tot = reinterpret_cast<int32_t*>(wsb + align256((int64_t)nch * E * 4));
-  int32_t* loff = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tot) + align256((int64_t)E * 4));
-  int32_t* gsum = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(loff) + align256((int64_t)E * 4));
-  route_select_kernel<NV><<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, score, renorm, B, (int)cap, topk_w,
-                                                      topk_ids, sorted_ids, expert_ids);
-  route_count_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt);
-  route_colscan_kernel<<<(E + 63) / 64, 1024, 0, st>>>(cnt, nch, E, B, tot, loff, gsum);
-  const size_t lds = 16 * (size_t)E4;
-  if (lds > 64 * 1024) {
-    // byte histograms of 16 waves for E > 4096 need more than the default 64 KB of LDS
-    const hipError_t err = hipFuncSetAttribute((const void*)route_scatter_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-  }
-  route_scatter_kernel<<<nch, 1024, lds, st>>>(topk_ids, T, E, k, B, nch, cnt, tot, loff,
-                                               gsum, sorted_ids, expert_ids, num_valid);
-  return hipGetLastError();
 }
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int score, int renorm, int B,
-                        float* topk_w, int32_t* topk_ids, int32_t* sorted_ids, int64_t cap,
-                        int32_t* expert_ids, int32_t* num_valid, void* ws, hipStream_t st) {
+bool route_is_grouped(int E, int n_group, int topk_group) {
+  return n_group > 1 && topk_group < n_group && E % n_group == 0;
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int score, int renorm,
+                        int n_group, int topk_group, int B, float* topk_w, int32_t* topk_ids,
+                        int32_t* sorted_ids, int64_t cap, int32_t* expert_ids,
+                        int32_t* num_valid, void* ws, hipStream_t st) {
   if (T == 0) {
     write_zero_i32<<<1, 1, 0, st>>>(num_valid);
     return hipGetLastError();
   }
+  const bool grouped = route_is_grouped(E, n_group, topk_group);
+  GroupSel gs;
+  if (grouped) {
+    if (n_group > kGroupMaxGroups || E > kGroupMaxE || k % topk_group != 0 ||
+        k > topk_group * (E / n_group))
+      return hipErrorInvalidValue;
+    gs.n = n_group;
+    gs.keep = topk_group;
+    gs.size = E / n_group;
+    gs.m = k / topk_group;
+  }
   const int nv = (E + 63) / 64;
-#define MOE_ROUTE_NV(N)                                                                        \
-  if (nv <= N)                                                                                 \
-    return launch_route_nv<N>(logits, T, E, k, score, renorm, B, topk_w, topk_ids, sorted_ids, \
-                              cap, expert_ids, num_valid, ws, st);
+#define MOE_ROUTE_NV(N)                                                                          \
+  if (nv <= N)                                                                                   \
+    return grouped ? launch_route_nv<N, true>(logits, T, E, k, score, renorm, gs, B, topk_w,     \
+                                              topk_ids, sorted_ids, cap, expert_ids, num_valid,  \
+                                              ws, st)                                            \
+                   : launch_route_nv<N, false>(logits, T, E, k, score, renorm, gs, B, topk_w,    \
+                                               topk_ids, sorted_ids, cap, expert_ids, num_valid, \
+                                               ws, st);
   MOE_ROUTE_NV(1)
   MOE_ROUTE_NV(2)
   MOE_ROUTE_NV(4)

@@ -216,6 +216,48 @@ def test_route_backward_validation(lib):
         assert call(**{key: BAD_ALIGN}) == EINVAL
 
 
+def test_grouped_route_validation(lib):
+    def call(T=4, E=16, k=4, G=4, TG=2, score=0, renorm=1, B=16, **ptrs):
+        cap = max(oracle.sorted_capacity(T, E, k, B), 16) if 1 <= k <= E else 1 << 20
+        p = dict(logits=GOOD, w=GOOD, ids=GOOD, sorted=GOOD, eids=GOOD, nv=GOOD)
+        p.update(ptrs)
+        return lib.moe_topk_softmax_sort_grouped(p["logits"], T, E, k, G, TG, score, renorm, B, p["w"],
+                                                 p["ids"], p["sorted"], cap, p["eids"], p["nv"], 0, 0, None)
+
+    assert call(G=3) == EINVAL          # n_group does not divide E
+    assert call(G=0) == EINVAL
+    assert call(TG=0) == EINVAL
+    assert call(TG=5) == EINVAL         # topk_group > n_group
+    assert call(k=3, TG=2) == EINVAL    # topk not a multiple of topk_group
+    assert call(k=6, G=8, TG=2) == EINVAL  # 2 kept groups of 2 experts hold fewer than 6
+    assert call(E=256, k=8, G=128, TG=4) == EUNSUP  # more than 64 groups
+    assert call(E=8000, k=8, G=8, TG=4) == EUNSUP   # group-limited needs E <= 4096
+    # every group kept: the plain top-k, so E = 8000 passes (the null pointer stops the call)
+    assert call(E=8000, k=8, G=8, TG=8, nv=None) == EINVAL
+    assert call(k=0) == EINVAL
+    assert call(score=2) == EINVAL
+    for key in ("logits", "w", "ids", "sorted", "eids", "nv"):
+        assert call(**{key: None}) == EINVAL
+
+
+def test_aux_scores_validation(lib):
+    def fwd(T=4, E=8, k=2, score=0, l=GOOD, s=GOOD, m=GOOD):
+        return lib.moe_aux_loss_scores(l, T, E, k, score, s, m, None)
+
+    def bwd(T=4, E=8, score=0, l=GOOD, g=GOOD, o=GOOD):
+        return lib.moe_aux_loss_scores_backward(l, g, T, E, score, o, None)
+
+    assert fwd(k=0) == EINVAL and fwd(k=9) == EINVAL and fwd(T=-1) == EINVAL
+    assert fwd(E=5000, k=2) == EUNSUP and bwd(E=5000) == EUNSUP
+    assert fwd(T=600000, E=4096) == ERANGE and bwd(T=600000, E=4096) == ERANGE
+    assert fwd(score=2) == EINVAL and bwd(score=2) == EINVAL
+    assert fwd(T=0, l=None, s=None, m=None) == OK and bwd(T=0, l=None, g=None, o=None) == OK
+    for key in ("l", "s", "m"):
+        assert fwd(**{key: None}) == EINVAL and fwd(**{key: BAD_ALIGN}) == EINVAL
+    for key in ("l", "g", "o"):
+        assert bwd(**{key: None}) == EINVAL and bwd(**{key: BAD_ALIGN}) == EINVAL
+
+
 def test_strerror(lib):
     import mixture_experts_routing_amd as m
     texts = {m.moe_strerror(s) for s in (OK, EINVAL, ERANGE, ENOSPC, EUNSUP, ELAUNCH)}
