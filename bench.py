@@ -11,7 +11,9 @@ The JSON line also carries the roofline of the dominant kernel (HIP events on th
 stream it runs on), the CPU oracle's time on a bounded sample, and (unless
 --headline-only) secondary lines: GPT-OSS decode/prefill and Kimi fp8 layer times
 with per-GEMM TFLOPS, the DeepSeek and Kimi layers again with packed bf16 atomics into
-the output, the Kimi shape in mxfp4 (a4w4), and router-only GB/s at T=8192.
+the output, the Kimi shape in mxfp4 (a4w4), router-only GB/s at T=8192 (forward and
+backward), the group-limited router at the DeepSeek-V3 routing shape, and the auxiliary-loss
+scores forward and backward at T=8192.
 """
 
 from __future__ import annotations
@@ -268,6 +270,78 @@ def measure_router(env, E, k, score, steps, warmup):
     return res
 
 
+def measure_router_grouped(env, T, E, k, n_group, topk_group, score, B, steps, warmup):
+    """Group-limited router (top-k over the best topk_group of n_group expert groups, then the
+    sort) at the DeepSeek-V3 routing shape, beside the plain router on the same inputs."""
+    m, torch, np, synth, dev = env
+    R = min(256, max(4, -(-512 * 2**20 // (4 * T * E))))
+    sets = [synth.logits(T, E, seed=300 + r).to(dev) for r in range(R)]
+    cap = m.moe_sorted_capacity(T, E, k, B)
+    rt = {"topk_weights": torch.empty(T, k, device=dev), "topk_ids": torch.empty(T, k, dtype=torch.int32, device=dev),
+          "sorted_token_ids": torch.empty(cap, dtype=torch.int32, device=dev),
+          "expert_ids": torch.empty(cap // B, dtype=torch.int32, device=dev),
+          "num_valid": torch.empty(1, dtype=torch.int32, device=dev)}
+    nb = m.moe_route_workspace_bytes(T, E, k, B)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def grouped(i, st):
+        m.moe_topk_softmax_sort_grouped(sets[i % R], k, n_group, topk_group, B, score, True, out=rt,
+                                        workspace=ws, stream=st)
+
+    def plain(i, st):
+        m.moe_topk_softmax_sort(sets[i % R], k, B, score, True, out=rt, workspace=ws, stream=st)
+
+    res = {"router_grouped": f"{E}/{k}, {n_group} groups, keep {topk_group}", "score": score, "T": T,
+           "block_m": B, "rotating_input_sets": R}
+    for name, fn in (("grouped", grouped), ("plain", plain)):
+        for i in range(warmup):
+            fn(i, stream)
+        torch.cuda.synchronize()
+        ms, how = graph_ms_per_call(torch, fn, max(steps, R))
+        res[f"{name}_us_per_call"] = round(ms * 1e3, 2)
+        res["timing"] = how
+    nv = int(rt["num_valid"].item())
+    alg = 4 * T * E + 8 * T * k + 4 * nv + 4 * (nv // B) + 4
+    res["alg_bytes"] = alg
+    res["GB/s"] = round(alg / (res["grouped_us_per_call"] * 1e-6) / 1e9, 1)
+    return res
+
+
+def measure_aux(env, E, k, score, steps, warmup):
+    """Auxiliary-loss scores at T = 8192 (the pages' router benchmark size), forward (scores
+    and routing map) and backward, input sets rotated past the last-level cache."""
+    m, torch, np, synth, dev = env
+    T = synth.ROUTER_T
+    R = max(2, -(-512 * 2**20 // (4 * T * E)))
+    sets = [synth.logits(T, E, seed=400 + r).to(dev) for r in range(R)]
+    sc = torch.empty(T, E, device=dev)
+    rmap = torch.empty(T, E, dtype=torch.bool, device=dev)
+    g = torch.randn(T, E, device=dev)
+    gl = torch.empty(T, E, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd(i, st):
+        m.moe_aux_loss_scores(sets[i % R], k, score, scores=sc, routing_map=rmap, stream=st)
+
+    def bwd(i, st):
+        m.moe_aux_loss_scores_backward(sets[i % R], g, score, grad_logits=gl, stream=st)
+
+    res = {"aux_scores": f"{E}/{k}", "score": score, "T": T, "rotating_input_sets": R}
+    # forward: logits in, scores and map out (9 B per element); backward: logits and the
+    # score gradient in, logit gradient out (12 B per element)
+    for name, fn, per in (("forward", fwd, 9), ("backward", bwd, 12)):
+        for i in range(warmup):
+            fn(i, stream)
+        torch.cuda.synchronize()
+        ms, how = graph_ms_per_call(torch, fn, max(steps, R))
+        alg = per * T * E
+        gbs = alg / (ms * 1e-3) / 1e9
+        res[name] = {"us_per_call": round(ms * 1e3, 2), "alg_bytes": alg, "GB/s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "timing": how}
+    return res
+
+
 KERNEL_SOURCES = ("mixture_experts_routing_amd/csrc/gemm.hip", "mixture_experts_routing_amd/csrc/moe_device.h")
 
 
@@ -444,6 +518,12 @@ def main():
         for (E, k) in synth.ROUTER_CASES:
             for score in ("softmax", "sigmoid"):
                 secondary.append(measure_router(env, E, k, score, args.steps, 3))
+        torch.cuda.empty_cache()
+        for T, B in ((16, 16), (synth.ROUTER_T, synth.ROUTER_BLOCK_M)):
+            secondary.append(measure_router_grouped(env, T, 256, 8, 8, 4, "sigmoid", B, args.steps, 3))
+        for (E, k) in synth.AUX_CASES:
+            for score in ("softmax", "sigmoid"):
+                secondary.append(measure_aux(env, E, k, score, args.steps, 3))
         torch.cuda.empty_cache()
 
     res = {

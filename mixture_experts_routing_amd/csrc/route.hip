@@ -115,7 +115,9 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
   int32_t* s_ids = s_wsum + 20;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  if constexpr (GROUPED) gs.keys = reinterpret_cast<uint32_t*>(s_ids + T * k) + w * E4;
+  if constexpr (GROUPED)  // 16-byte aligned for the spread scan's 16-byte reads
+    gs.keys = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(s_ids + T * k) + 15) & ~(uintptr_t)15) +
+              w * E4;
   const int sentinel = T * k;
   prefill_share(sorted_ids, cap, expert_ids, B, sentinel, 0, 1, tid, 1024);
   for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
@@ -412,7 +414,7 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
         // at most 16 KB + 24 KB + 80 B + 16 KB (E <= 1024, T*k <= 4096), plus 64 KB of keys
         // for group-limited selection
         const size_t lds = 16 * kMaxCand * sizeof(uint64_t) + 16 * (size_t)E4 + 2 * 4 * (size_t)E4 +
-                           20 * 4 + 4 * (size_t)T * k + (GROUPED ? 16 * 4 * (size_t)E4 : 0);
+                           20 * 4 + 4 * (size_t)T * k + (GROUPED ? 16 + 16 * 4 * (size_t)E4 : 0);
         if (lds > 64 * 1024) {
           const hipError_t err =
               hipFuncSetAttribute((const void*)route_oneshot_kernel<NV, GROUPED>,
@@ -492,6 +494,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int score, int
     gs.keep = topk_group;
     gs.size = E / n_group;
     gs.m = k / topk_group;
+    // spread scan: n a power of two, each group an equal number of keys on each of its lanes
+    const int L = 64 / n_group;
+    if ((n_group & (n_group - 1)) == 0 && gs.size % L == 0 && gs.m <= 4) {
+      gs.lanes = L;
+      gs.per = gs.size / L;
+    }
   }
   const int nv = (E + 63) / 64;
 #define MOE_ROUTE_NV(N)                                                                          \

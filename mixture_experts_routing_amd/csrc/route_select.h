@@ -18,7 +18,10 @@
 // experts; a group's score is the sum of its m = k/topk_group best expert scores (softmax
 // numerators exp(l - max) or sigmoids, fp64, best first).  The topk_group best groups stay
 // (ties to the lower group index) and the logits of the other groups are masked out before
-// the selection above.  The token's keys are staged in LDS and lane j scans group j.
+// the selection above.  The token's keys are staged in LDS.  With n a power of two, m <= 4
+// and E/n a multiple of 64/n, each group is spread over 64/n lanes: a lane keeps the top 4
+// of its contiguous slice of keys and the lists are merged across the group's lanes by a
+// butterfly; otherwise lane j scans group j alone.
 #pragma once
 
 #include "moe_device.h"
@@ -37,8 +40,38 @@ struct GroupSel {
   int keep = 1;   // groups kept (topk_group)
   int size = 1;   // experts per group
   int m = 1;      // best experts summed per group (k / keep)
+  int lanes = 0;  // lanes per group in the spread scan (64 / n), 0 = one lane per group
+  int per = 0;    // keys per lane in the spread scan (size / lanes)
   uint32_t* keys = nullptr;
 };
+
+// Inserts key x into the descending list t (0 = empty slot).
+__device__ __forceinline__ void top4_insert(uint32_t (&t)[4], uint32_t x) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const uint32_t hi = max(t[i], x);
+    x = min(t[i], x);
+    t[i] = hi;
+  }
+  t[3] = max(t[3], x);
+}
+
+// t := the 4 largest of t and the list of lane ^ M (both descending).  The elementwise
+// maximum of one list and the other reversed holds them as a bitonic sequence, which two
+// compare stages sort.
+template <int M>
+__device__ __forceinline__ void top4_merge(uint32_t (&t)[4]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = xor_lane<M>(t[i]);
+  const uint32_t p0 = max(t[0], o[3]), p1 = max(t[1], o[2]), p2 = max(t[2], o[1]),
+                 p3 = max(t[3], o[0]);
+  const uint32_t a0 = max(p0, p2), a2 = min(p0, p2), a1 = max(p1, p3), a3 = min(p1, p3);
+  t[0] = max(a0, a1);
+  t[1] = min(a0, a1);
+  t[2] = max(a2, a3);
+  t[3] = min(a2, a3);
+}
 
 // Weight arithmetic runs in fp64 and is rounded to fp32 once: exp of an fp32
 // logit difference loses |l - m| * 2^-24 relative accuracy in fp32, which for
@@ -78,6 +111,43 @@ __device__ uint64_t group_keep_mask(const float (&x)[NV], int E, bool softmax, d
     if (e < E) gs.keys[e] = logit_key(x[i]);
   }
   wave_lds_sync();
+  uint64_t keep = 0;
+  if (gs.lanes > 0) {
+    // spread scan: lanes [g*L, (g+1)*L) hold group g, each a contiguous slice of `per` keys
+    const int L = gs.lanes, c = gs.per;
+    const int g = lane >> __builtin_ctz(L), sub = lane & (L - 1);
+    const uint32_t* p = gs.keys + g * gs.size + sub * c;
+    uint32_t t[4] = {0u, 0u, 0u, 0u};
+    if ((c & 3) == 0) {
+      for (int q = 0; q < c; q += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p + q);
+        top4_insert(t, v.x);
+        top4_insert(t, v.y);
+        top4_insert(t, v.z);
+        top4_insert(t, v.w);
+      }
+    } else {
+      for (int q = 0; q < c; ++q) top4_insert(t, p[q]);
+    }
+    wave_lds_sync();  // the key buffer is reused by the next token
+    if (L > 1) top4_merge<1>(t);
+    if (L > 2) top4_merge<2>(t);
+    if (L > 4) top4_merge<4>(t);
+    if (L > 8) top4_merge<8>(t);
+    if (L > 16) top4_merge<16>(t);
+    if (L > 32) top4_merge<32>(t);
+    double sc = 0.0;
+    for (int r = 0; r < gs.m; ++r) sc += score_of((double)key_logit(t[r]), m_all, softmax);
+    int rank = 0;
+    const uint64_t sb = __builtin_bit_cast(uint64_t, sc);
+    for (int j = 0; j < gs.n; ++j) {
+      const double o = __builtin_bit_cast(double, readlane_u64(sb, j * L));
+      rank += (o > sc) || (o == sc && j < g);
+    }
+    const uint64_t lead = __ballot(sub == 0 && rank < gs.keep);
+    for (int j = 0; j < gs.n; ++j) keep |= ((lead >> (j * L)) & 1ull) << j;
+    return keep;
+  }
   double sc = -1.0;  // group scores are >= 0; lanes past the groups never rank ahead
   if (lane < gs.n) {
     const int b = lane * gs.size;

@@ -14,6 +14,9 @@ share on the aiter mxfp4 page):
 * deepseek: T in {1,2,4,8,16}, E=256, topk=8, D=7168, I=2048, BLOCK_M=16, bf16, atomic
 * gptoss:   E=128, topk=4, D=I=2880, T=16 (decode) / 4096 (prefill), BLOCK_M=64, bf16, reduce
 * router:   T=8192, E/topk in {512/4, 512/22, 2304/36}, softmax|sigmoid, BLOCK_M=32
+* router_grouped: E=256, topk=8 in 8 groups of 32, 4 groups kept (the DeepSeek-V3 routing
+            shape), sigmoid, T=16 (BLOCK_M=16) and T=8192 (BLOCK_M=32)
+* aux scores: T=8192, E/topk in {512/22, 2304/36}, softmax|sigmoid
 * kimi:     E=385, topk=9, D=7168, I=512, T in {64, 4096, 16384}, BLOCK_M=64, fp8, atomic
 * kimi_mxfp4: the kimi shape with mxfp4 (a4w4) activations and weights
 
@@ -71,6 +74,9 @@ MX_W_EXP = (119, 121)
 ROUTER_T = 8192
 ROUTER_BLOCK_M = 32
 ROUTER_CASES = ((512, 4), (512, 22), (2304, 36))
+# Auxiliary-loss score shapes (E, topk): the two configurations with aux_loss rows in the
+# fused-router benchmark tables.
+AUX_CASES = ((512, 22), (2304, 36))
 
 
 def _gen(seed: int, device) -> torch.Generator:
