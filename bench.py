@@ -11,7 +11,8 @@ The JSON line also carries the roofline of the dominant kernel (HIP events on th
 stream it runs on), the CPU oracle's time on a bounded sample, and (unless
 --headline-only) secondary lines: GPT-OSS decode/prefill and Kimi fp8 layer times
 with per-GEMM TFLOPS, the DeepSeek and Kimi layers again with packed bf16 atomics into
-the output, the Kimi shape in mxfp4 (a4w4), router-only GB/s at T=8192 (forward and
+the output, the Kimi shape in mxfp4 (a4w4), the Kimi prefill with the reduce-mode combine
+(per-slot rows summed by the finalize kernel) instead of atomics, router-only GB/s at T=8192 (forward and
 backward), the group-limited router at the DeepSeek-V3 routing shape, and the auxiliary-loss
 scores forward and backward at T=8192.
 """
@@ -510,7 +511,8 @@ def main():
                               ("kimi", 4096, None), ("kimi", 16384, None), ("deepseek", 16, "atomic_bf16"),
                               ("kimi", 4096, "atomic_bf16"), ("kimi", 16384, "atomic_bf16"),
                               ("kimi_mxfp4", 64, None), ("kimi_mxfp4", 4096, None),
-                              ("kimi_mxfp4", 16384, None)):
+                              ("kimi_mxfp4", 16384, None), ("kimi", 4096, "reduce"),
+                              ("kimi", 16384, "reduce"), ("kimi_mxfp4", 16384, "reduce")):
             r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2, mode)
             del kp
             torch.cuda.empty_cache()

@@ -573,7 +573,8 @@ enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2, PF_G2_ATOMIC_BF16 = 3 };
 constexpr int kPfRows = 64;                          // rows of one sorted block
 constexpr int kPfMaxBlocks = 4;                      // sorted blocks per tile
 constexpr int kPfMaxRows = kPfRows * kPfMaxBlocks;   // 256
-constexpr int kPfRingBytes = 160 * 1024 - kPfMaxRows * 4;  // LDS of one CU, less the slot ids
+// LDS of one CU, less the slot ids and the per-row epilogue factors
+constexpr int kPfRingBytes = 160 * 1024 - kPfMaxRows * 8;
 
 struct PfArgs {
   const uint8_t* act;
@@ -598,8 +599,12 @@ struct PfArgs {
 // rows'.  They come by 4-byte direct-to-LDS loads, 32 rows x 8 B per instruction, exactly two
 // per wave and chunk (a wave with fewer rows left repeats its first, writing the same bytes),
 // so they are waited for with the chunk's rows.
+// s_fac[row]: the row's epilogue factor, read from LDS so that the epilogue issues no
+// dependent global loads (gate-up: the token's fp8 scale; down: the routed weight, times the
+// slot's fp8 scale; 0 for padding rows).
 template <int DT, int MODE, int NB>
 __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restrict__ s_slot,
+                                             const float* __restrict__ s_fac,
                                              uint8_t* __restrict__ ring) {
   constexpr bool G1 = MODE == PF_G1;
   constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
@@ -797,7 +802,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
         const int s = s_slot[(2 * m + th) * 16 + i16];
         if ((unsigned)s >= (unsigned)n_slots) continue;
         float xs = 1.f;
-        if constexpr (FP8) xs = static_cast<const float*>(p.act_scale)[s / p.k];
+        if constexpr (FP8) xs = s_fac[(2 * m + th) * 16 + i16];
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -829,11 +834,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           sr[r] = s_slot[(2 * m + th) * 16 + 4 * g + r];
-          sc[r] = 0.f;
-          if ((unsigned)sr[r] < (unsigned)n_slots) {
-            sc[r] = p.topk_w[sr[r]];
-            if constexpr (FP8) sc[r] *= static_cast<const float*>(p.act_scale)[sr[r]];
-          }
+          sc[r] = s_fac[(2 * m + th) * 16 + 4 * g + r];
         }
         const int s_a = odd ? sr[2] : sr[0], s_b = odd ? sr[3] : sr[1];
 #pragma unroll
@@ -858,8 +859,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
         for (int r = 0; r < 4; ++r) {
           const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
           if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
-          float sc = p.topk_w[s];
-          if constexpr (FP8) sc *= static_cast<const float*>(p.act_scale)[s];
+          const float sc = s_fac[(2 * m + th) * 16 + 4 * g + r];
           float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / p.k) * D + row0 + i16;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -888,6 +888,7 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
   constexpr bool G1 = MODE == PF_G1;
   __shared__ __align__(16) uint8_t ring[kPfRingBytes];
   __shared__ int s_slot[kPfMaxRows];
+  __shared__ float s_fac[kPfMaxRows];
   if (zero_y)
     for (int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 512)
       zero_y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -912,14 +913,27 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
   if (before % kPfMaxBlocks != 0) return;
   int nb = 1;
   while (nb < kPfMaxBlocks && mb + nb < nvb && expert_ids[mb + nb] == e) ++nb;
-  for (int i = threadIdx.x; i < kPfRows * nb; i += 512) s_slot[i] = sorted_ids[mb * kPfRows + i];
-  __syncthreads();  // s_slot
+  for (int i = threadIdx.x; i < kPfRows * nb; i += 512) {
+    const int s = sorted_ids[mb * kPfRows + i];
+    float f = 0.f;
+    if ((unsigned)s < (unsigned)(T * k)) {
+      if constexpr (G1) {
+        f = DT == DT_FP8 ? static_cast<const float*>(act_scale)[s / k] : 1.f;
+      } else {
+        f = topk_w[s];
+        if constexpr (DT == DT_FP8) f *= static_cast<const float*>(act_scale)[s];
+      }
+    }
+    s_slot[i] = s;
+    s_fac[i] = f;
+  }
+  __syncthreads();  // s_slot, s_fac
   const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out};
   switch (nb) {
-    case 1: prefill_tile<DT, MODE, 1>(p, s_slot, ring); break;
-    case 2: prefill_tile<DT, MODE, 2>(p, s_slot, ring); break;
-    case 3: prefill_tile<DT, MODE, 3>(p, s_slot, ring); break;
-    default: prefill_tile<DT, MODE, 4>(p, s_slot, ring); break;
+    case 1: prefill_tile<DT, MODE, 1>(p, s_slot, s_fac, ring); break;
+    case 2: prefill_tile<DT, MODE, 2>(p, s_slot, s_fac, ring); break;
+    case 3: prefill_tile<DT, MODE, 3>(p, s_slot, s_fac, ring); break;
+    default: prefill_tile<DT, MODE, 4>(p, s_slot, s_fac, ring); break;
   }
 }
 

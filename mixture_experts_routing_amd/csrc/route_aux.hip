@@ -33,7 +33,10 @@ __device__ __forceinline__ float exp_diff(float a, float b) {
   return expf(hi) * (1.0f + lo);
 }
 
-__device__ __forceinline__ float sigmoid_f(float l) { return 1.0f / (1.0f + expf(-l)); }
+// 1 / (1 + exp(-l)) with the hardware reciprocal (1 ulp); an underflowing result flushes to 0
+__device__ __forceinline__ float sigmoid_f(float l) {
+  return __builtin_amdgcn_rcpf(1.0f + expf(-l));
+}
 
 // y = the unnormalised scores of the row (exp(l - max) or the sigmoid; 0 in empty slots)
 // and inv_sum = 1 / sum y, so that y * inv_sum is the token's distribution.
@@ -136,15 +139,15 @@ __global__ void __launch_bounds__(256) aux_scores_backward_kernel(
     for (int i = 0; i < NV; ++i)
       if (lane + 64 * i < E) __builtin_nontemporal_store(y[i] * rinv * (g[i] - d), out + lane + 64 * i);
   } else {
-    // u = exp(-l): s = 1 / (1 + u) and s (1 - s) = 1 / (2 + u + 1/u), both accurate for
-    // every l (the second form has the right limit 0 at u = 0 and u = inf)
+    // u = exp(-l): s = 1 / (1 + u) and s (1 - s) = u s^2, both accurate for every l (no
+    // cancellation in 1 - s); u = inf (l below about -88) has s = 0 and s (1 - s) = 0
     double ssum = 0.0, dot = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       if (lane + 64 * i < E) {
         const float u = expf(-x[i]);
-        const float sv = 1.0f / (1.0f + u);
-        y[i] = 1.0f / (2.0f + u + 1.0f / u);
+        const float sv = __builtin_amdgcn_rcpf(1.0f + u);
+        y[i] = u < __builtin_inff() ? u * sv * sv : 0.0f;
         ssum += (double)sv;
         dot += (double)sv * (double)g[i];
       }
