@@ -12,7 +12,8 @@ stream it runs on), the CPU oracle's time on a bounded sample, and (unless
 --headline-only) secondary lines: GPT-OSS decode/prefill and Kimi fp8 layer times
 with per-GEMM TFLOPS, the DeepSeek and Kimi layers again with packed bf16 atomics into
 the output, the Kimi shape in mxfp4 (a4w4), the Kimi prefill with the reduce-mode combine
-(per-slot rows summed by the finalize kernel) instead of atomics, router-only GB/s at T=8192 (forward and
+(per-slot rows summed by the finalize kernel) instead of atomics, decode lines with the weights
+in fragment order (moe_preshuffle_weights), router-only GB/s at T=8192 (forward and
 backward), the group-limited router at the DeepSeek-V3 routing shape, and the auxiliary-loss
 scores forward and backward at T=8192.
 """
@@ -109,15 +110,22 @@ def algorithmic(wl, T, n_act, num_valid):
             "gemm1_flops": 2 * T * k * 2 * I * D, "gemm2_flops": 2 * T * k * D * I}
 
 
-def measure_layer(env, wl, T, steps, warmup, rotate, mode=None):
+def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=False):
     """Times moe_forward and, separately, each stage; returns a result dict.  mode overrides
-    the workload's output mode (atomic_bf16: packed bf16 atomics straight into out)."""
+    the workload's output mode (atomic_bf16: packed bf16 atomics straight into out);
+    preshuffled puts the weights in fragment order first (a one-time step, not timed)."""
     m, torch, np, synth, dev = env
     k, B, dtype = wl.topk, wl.block_m, wl.dtype
     mode = mode or wl.mode
     E, D, I = wl.E, wl.D, wl.I
-    log(f"{wl.name} T={T} E={E} k={k} D={D} I={I} B={B} {dtype} {mode}: generating inputs")
+    log(f"{wl.name} T={T} E={E} k={k} D={D} I={I} B={B} {dtype} {mode}"
+        f"{' preshuffled' if preshuffled else ''}: generating inputs")
     base = synth.layer_inputs(wl, 1, seed=0, device=dev)
+    if preshuffled:
+        for key in ("w1", "w2"):
+            base[key] = m.moe_preshuffle_weights(dtype, base[key])
+        torch.cuda.synchronize()
+    pre = dict(preshuffled=True) if preshuffled else {}
     sets = []
     for r in range(rotate):
         s = {"logits": synth.logits(T, E, seed=100 + r).to(dev)}
@@ -132,7 +140,7 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None):
         s = sets[i % len(sets)]
         m.moe_forward(dtype, s["logits"], s["x"], base["w1"], base["w2"], k, B, mode,
                       x_scale=s.get("x_scale"), w1_scale=base.get("w1_scale"),
-                      w2_scale=base.get("w2_scale"), workspace=ws, out=out, stream=st)
+                      w2_scale=base.get("w2_scale"), workspace=ws, out=out, stream=st, **pre)
 
     for i in range(warmup):
         layer_call(i, stream)
@@ -161,12 +169,13 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None):
     def gemm1_call(i, st):
         j = i % len(sets)
         m.moe_gemm1_gateup(dtype, sets[j]["x"], base["w1"], routes[j], k, B, x_scale=sets[j].get("x_scale"),
-                           w1_scale=base.get("w1_scale"), a=a, a_scale=a_scale, workspace=g1ws, stream=st)
+                           w1_scale=base.get("w1_scale"), a=a, a_scale=a_scale, workspace=g1ws, stream=st,
+                           **pre)
 
     def gemm2_call(i, st):
         j = i % len(sets)
         m.moe_gemm2_down(dtype, a, base["w2"], routes[j], T, k, B, mode, a_scale=a_scale,
-                         w2_scale=base.get("w2_scale"), y=y, stream=st)
+                         w2_scale=base.get("w2_scale"), y=y, stream=st, **pre)
 
     def fin_call(i, st):
         m.moe_finalize(mode, y, T, k, D, out=out, stream=st)
@@ -204,7 +213,8 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None):
         gemm["gemm2"]["atomic_floor_us"] = round(adds / ATOMIC_ADDS_PER_S * 1e6, 1)
         gemm["gemm2"]["frac_of_atomic_floor"] = round(adds / ATOMIC_ADDS_PER_S / (stage_ms["gemm2"] / 1e3), 4)
     res = {
-        "workload": wl.name, "T": T, "dtype": dtype, "mode": mode, "us_per_call": round(ms_per_call * 1e3, 2),
+        "workload": wl.name, "T": T, "dtype": dtype, "mode": mode,
+        "weights": "fragment order" if preshuffled else "natural", "us_per_call": round(ms_per_call * 1e3, 2),
         "timing": how,
         "layer_alg_bytes": int(layer_bytes), "layer_hbm_floor_us": round(layer_bytes / HBM_PEAK_GBS / 1e3, 1),
         "frac_of_layer_hbm_floor": round(layer_bytes / HBM_PEAK_GBS / 1e3 / (ms_per_call * 1e3), 4),
@@ -514,6 +524,15 @@ def main():
                               ("kimi_mxfp4", 16384, None), ("kimi", 4096, "reduce"),
                               ("kimi", 16384, "reduce"), ("kimi_mxfp4", 16384, "reduce")):
             r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2, mode)
+            del kp
+            torch.cuda.empty_cache()
+            secondary.append(r)
+        # weights in fragment order (prepared once, outside the timed region)
+        for name, T in (("deepseek", 16), ("kimi", 64), ("kimi_mxfp4", 64), ("gptoss", 16)):
+            # input sets rotated as in the natural-layout line of the same workload
+            rot = args.rotate if name == "deepseek" else 2
+            r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, rot, None,
+                                  preshuffled=True)
             del kp
             torch.cuda.empty_cache()
             secondary.append(r)

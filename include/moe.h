@@ -59,6 +59,13 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_dtype { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_MXFP4 = 2 };
 enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1, MOE_OUT_ATOMIC_BF16 = 2 };
 
+/* OR-ed into the dtype of moe_gemm1_gateup, moe_gemm2_down and moe_forward (and accepted,
+ * and ignored, by the workspace-size functions): w1 and w2 are in fragment order, as written
+ * by moe_preshuffle_weights.  Needs rows of whole 128-byte K chunks (fp8: D and I multiples
+ * of 128; mxfp4: of 256), else MOE_EUNSUPPORTED.  Results are bit-identical to the natural
+ * layout's. */
+#define MOE_PRESHUFFLED 0x100
+
 /* Largest E accepted ([P3] "Hardening": the radix top-k path's 8160-expert bound). */
 #define MOE_MAX_EXPERTS 8160
 
@@ -200,6 +207,23 @@ int moe_aux_loss_scores(const float* logits, int T, int E, int topk, int score, 
  * fp32 arithmetic with fp64 sums.  Validation as for moe_aux_loss_scores. */
 int moe_aux_loss_scores_backward(const float* logits, const float* grad_scores, int T, int E,
                                  int score, float* grad_logits, void* stream);
+
+/* ---------------------------------------------------------------- weight preshuffle
+ * [P2] the gate-up helper commit ("make_gateup_weight_view": a preshuffle of the weights into
+ * the order the MFMA consumes them) and the stage-2 decode profile (the gap is memory-latency
+ * bound, led by the weight loads).  A one-time layout change of a weight tensor: for each
+ * group of 16 consecutive rows and each 128-byte chunk of K, 2 KB holding, for half h (0, 1)
+ * and lane l = i + 16 g (i < 16, g < 4), the 16 bytes [128 c + 64 h + 16 g, + 16) of row
+ * 16 R + i.  Each 1 KB is then what one wave's 16-byte load brings in for one operand
+ * register, contiguous in memory.  Scales (fp8 per-row scales, mxfp4 E8M0 blocks) keep their
+ * natural layout.
+ *   w      [rows, K] in the dtype's storage (bf16: 2K bytes per row, fp8: K, mxfp4: K/2);
+ *          an expert tensor [E, N, K] is rows = E*N
+ *   w_out  the same size; must not overlap w
+ * rows must be a multiple of 16 and a row a whole number of 128-byte chunks
+ * (MOE_EUNSUPPORTED otherwise); dtype without flags. */
+int moe_preshuffle_weights(int dtype, const void* w, int64_t rows, int K, void* w_out,
+                           void* stream);
 
 /* ---------------------------------------------------------------- stage 1
  * [P2] gate-up helper and stage-1 commits ("silu(gate)*up with optional fp8

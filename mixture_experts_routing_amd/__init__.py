@@ -30,6 +30,7 @@ __all__ = [
     "moe_topk_softmax_sort_grouped",
     "moe_aux_loss_scores",
     "moe_aux_loss_scores_backward",
+    "moe_preshuffle_weights",
     "moe_forward",
     "SCORE",
     "DTYPE",
@@ -41,6 +42,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 SCORE = {"softmax": 0, "sigmoid": 1}
 DTYPE = {"bf16": 0, "fp8": 1, "mxfp4": 2}
+PRESHUFFLED = 0x100  # dtype flag: weights in fragment order (moe_preshuffle_weights)
 MODE = {"atomic": 0, "reduce": 1, "atomic_bf16": 2}
 WS_FIELDS = ("topk_weights", "topk_ids", "sorted_token_ids", "expert_ids", "num_valid",
              "route_scratch", "a", "a_scale", "gemm1_scratch", "y")
@@ -72,6 +74,7 @@ _SIGS = {
                                            _SZ, _P]),
     "moe_aux_loss_scores": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_aux_loss_scores_backward": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "moe_preshuffle_weights": (_I, [_I, _P, _I64, _I, _P, _P]),
     "moe_gemm2_down": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_finalize": (_I, [_I, _P, _I, _I, _I, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P, _P]),
@@ -223,7 +226,7 @@ def moe_topk_softmax_backward(logits, topk_ids, topk_weights, grad_topk_weights,
 
 
 def moe_gemm1_gateup(dtype: str, x, w1, route: dict, topk: int, block_m: int, x_scale=None,
-                     w1_scale=None, a=None, a_scale=None, workspace=None, stream=None):
+                     w1_scale=None, a=None, a_scale=None, workspace=None, stream=None, preshuffled: bool = False):
     """Stage 1: returns (a, a_scale); a is bf16 [T*k, I] (fp8: uint8 e4m3 codes + fp32 scales;
     mxfp4: packed uint8 [T*k, I/2] + E8M0 uint8 [T*k, I/32])."""
     T, D = x.shape
@@ -244,14 +247,14 @@ def moe_gemm1_gateup(dtype: str, x, w1, route: dict, topk: int, block_m: int, x_
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sid = route["sorted_token_ids"]
     _check(load_library().moe_gemm1_gateup(
-        DTYPE[dtype], _ptr(x), _ptr(x_scale), _ptr(w1), _ptr(w1_scale), _ptr(sid),
+        DTYPE[dtype] | (PRESHUFFLED if preshuffled else 0), _ptr(x), _ptr(x_scale), _ptr(w1), _ptr(w1_scale), _ptr(sid),
         _ptr(route["expert_ids"]), _ptr(route["num_valid"]), sid.numel(), T, E, topk, D, I, block_m,
         _ptr(a), _ptr(a_scale), _ptr(workspace), ws_bytes, _stream(stream)), "moe_gemm1_gateup")
     return a, a_scale
 
 
 def moe_gemm2_down(dtype: str, a, w2, route: dict, T: int, topk: int, block_m: int, mode: str,
-                   a_scale=None, w2_scale=None, y=None, stream=None):
+                   a_scale=None, w2_scale=None, y=None, stream=None, preshuffled: bool = False):
     """Stage 2: returns y (ATOMIC: fp32 [T, D] accumulated into; REDUCE: fp32 [T*k, D];
     ATOMIC_BF16: bf16 [T, D] accumulated into)."""
     E, D, I = w2.shape
@@ -266,7 +269,7 @@ def moe_gemm2_down(dtype: str, a, w2, route: dict, T: int, topk: int, block_m: i
             y = torch.zeros(rows, D, dtype=torch.float32, device=dev)
     sid = route["sorted_token_ids"]
     _check(load_library().moe_gemm2_down(
-        DTYPE[dtype], _ptr(a), _ptr(a_scale), _ptr(w2), _ptr(w2_scale), _ptr(route["topk_weights"]),
+        DTYPE[dtype] | (PRESHUFFLED if preshuffled else 0), _ptr(a), _ptr(a_scale), _ptr(w2), _ptr(w2_scale), _ptr(route["topk_weights"]),
         _ptr(sid), _ptr(route["expert_ids"]), _ptr(route["num_valid"]), sid.numel(), T, E, topk, D, I,
         block_m, MODE[mode], _ptr(y), _stream(stream)), "moe_gemm2_down")
     return y
@@ -283,8 +286,9 @@ def moe_finalize(mode: str, y, T: int, topk: int, D: int, out=None, stream=None)
 
 def moe_forward(dtype: str, logits, x, w1, w2, topk: int, block_m: int, mode: str = "atomic",
                 score: str = "softmax", renorm: bool = True, x_scale=None, w1_scale=None,
-                w2_scale=None, workspace=None, out=None, stream=None):
-    """Whole layer; returns (out bf16 [T, D], workspace uint8, {field: view into workspace})."""
+                w2_scale=None, workspace=None, out=None, stream=None, preshuffled: bool = False):
+    """Whole layer; returns (out bf16 [T, D], workspace uint8, {field: view into workspace}).
+    preshuffled: w1 and w2 come from moe_preshuffle_weights."""
     T, D = x.shape
     E, twoI, _ = w1.shape
     I = twoI // 2
@@ -297,10 +301,22 @@ def moe_forward(dtype: str, logits, x, w1, w2, topk: int, block_m: int, mode: st
     if out is None:
         out = torch.empty(T, D, dtype=torch.bfloat16, device=dev)
     _check(load_library().moe_forward(
-        DTYPE[dtype], SCORE[score], int(renorm), MODE[mode], _ptr(logits), _ptr(x), _ptr(x_scale),
+        DTYPE[dtype] | (PRESHUFFLED if preshuffled else 0), SCORE[score], int(renorm), MODE[mode], _ptr(logits), _ptr(x), _ptr(x_scale),
         _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), T, E, topk, D, I, block_m, _ptr(workspace),
         workspace.numel(), _ptr(out), _stream(stream)), "moe_forward")
     return out, workspace, offs
+
+
+def moe_preshuffle_weights(dtype: str, w, out=None, stream=None):
+    """Weights [E, N, row storage] (bf16, or uint8 for fp8 / packed mxfp4) into fragment order,
+    same shape and dtype (scales are not touched)."""
+    rows = w.numel() // w.shape[-1]
+    K = w.shape[-1] * 2 if dtype == "mxfp4" else w.shape[-1]
+    if out is None:
+        out = torch.empty_like(w)
+    _check(load_library().moe_preshuffle_weights(DTYPE[dtype], _ptr(w), rows, K, _ptr(out), _stream(stream)),
+           "moe_preshuffle_weights")
+    return out
 
 
 def workspace_views(workspace, offs: dict, dtype: str, mode: str, T: int, E: int, topk: int, D: int,

@@ -28,6 +28,16 @@ int check_route_dims(int T, int E, int topk, int block_m) {
 
 bool quantised(int dtype) { return dtype == MOE_FP8_E4M3 || dtype == MOE_MXFP4; }
 
+// Bytes of a weight row of K elements.
+int64_t row_bytes(int dtype, int64_t K) {
+  return dtype == MOE_BF16 ? 2 * K : dtype == MOE_FP8_E4M3 ? K : K / 2;
+}
+// Splits the MOE_PRESHUFFLED flag off dtype.
+int base_dtype(int dtype, int* pre) {
+  if (pre) *pre = (dtype & MOE_PRESHUFFLED) != 0;
+  return dtype & ~MOE_PRESHUFFLED;
+}
+
 int check_layer_dims(int dtype, int T, int E, int topk, int D, int I, int block_m) {
   if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3 && dtype != MOE_MXFP4) return MOE_EINVAL;
   int st = check_route_dims(T, E, topk, block_m);
@@ -116,6 +126,7 @@ int64_t moe_route_workspace_bytes(int T, int E, int topk, int block_m) {
 }
 
 int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I) {
+  dtype = base_dtype(dtype, nullptr);
   if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3 && dtype != MOE_MXFP4) return MOE_EINVAL;
   if (T < 0 || topk < 1 || I < 64 || I % 64) return MOE_EINVAL;
   if (dtype == MOE_BF16) return 0;
@@ -124,6 +135,7 @@ int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I) {
 
 int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
                                      int block_m, int64_t* offsets) {
+  dtype = base_dtype(dtype, nullptr);
   if (!ok_mode(mode)) return MOE_EINVAL;
   const int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
   if (st) return st;
@@ -253,9 +265,12 @@ int moe_gemm1_gateup(int dtype, const void* x, const void* x_scale, const void* 
                      const int32_t* expert_ids, const int32_t* num_valid, int64_t sorted_cap,
                      int T, int E, int topk, int D, int I, int block_m, void* a, void* a_scale,
                      void* workspace, size_t ws_bytes, void* stream) {
+  int pre;
+  dtype = base_dtype(dtype, &pre);
   int st = check_gemm_common(dtype, T, E, topk, D, I, block_m, sorted_cap, sorted_token_ids,
                              expert_ids, num_valid);
   if (st) return st;
+  if (pre && row_bytes(dtype, D) % 128) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(a)) return MOE_EINVAL;
   if (quantised(dtype)) {
@@ -264,7 +279,7 @@ int moe_gemm1_gateup(int dtype, const void* x, const void* x_scale, const void* 
     if (!ok_ptr(workspace)) return MOE_EINVAL;
   }
   const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
-  return launch_status(moe::launch_gemm1(dtype, x, x_scale, w1, w1_scale, sorted_token_ids,
+  return launch_status(moe::launch_gemm1(dtype, pre, x, x_scale, w1, w1_scale, sorted_token_ids,
                                          expert_ids, num_valid, cap, T, E, topk, D, I, block_m, a,
                                          a_scale, workspace, nullptr, 0, (hipStream_t)stream));
 }
@@ -274,15 +289,18 @@ int moe_gemm2_down(int dtype, const void* a, const void* a_scale, const void* w2
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
                    const int32_t* num_valid, int64_t sorted_cap, int T, int E, int topk, int D,
                    int I, int block_m, int mode, void* y, void* stream) {
+  int pre;
+  dtype = base_dtype(dtype, &pre);
   if (!ok_mode(mode)) return MOE_EINVAL;
   int st = check_gemm_common(dtype, T, E, topk, D, I, block_m, sorted_cap, sorted_token_ids,
                              expert_ids, num_valid);
   if (st) return st;
+  if (pre && row_bytes(dtype, I) % 128) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(a) || !ok_ptr(w2) || !ok_ptr(topk_weights) || !ok_ptr(y)) return MOE_EINVAL;
   if (quantised(dtype) && (!ok_ptr(a_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
   const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
-  return launch_status(moe::launch_gemm2(dtype, a, a_scale, w2, w2_scale, topk_weights,
+  return launch_status(moe::launch_gemm2(dtype, pre, a, a_scale, w2, w2_scale, topk_weights,
                                          sorted_token_ids, expert_ids, num_valid, cap, T, E, topk,
                                          D, I, block_m, mode, y, (hipStream_t)stream));
 }
@@ -300,11 +318,14 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
                 const void* x_scale, const void* w1, const void* w1_scale, const void* w2,
                 const void* w2_scale, int T, int E, int topk, int D, int I, int block_m,
                 void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+  int pre;
+  dtype = base_dtype(dtype, &pre);
   if (!ok_mode(mode)) return MOE_EINVAL;
   if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_EINVAL;
   if (renorm != 0 && renorm != 1) return MOE_EINVAL;
   int st = check_layer_dims(dtype, T, E, topk, D, I, block_m);
   if (st) return st;
+  if (pre && (row_bytes(dtype, D) % 128 || row_bytes(dtype, I) % 128)) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(w2) || !ok_ptr(out) ||
       !ok_ptr(workspace))
@@ -336,13 +357,25 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   hipError_t e = moe::launch_route(logits, T, E, topk, score, renorm, 1, 1, block_m, topk_w, topk_ids,
                                    sorted, cap, eids, nvalid, rws, s);
   if (e == hipSuccess)
-    e = moe::launch_gemm1(dtype, x, x_scale, w1, w1_scale, sorted, eids, nvalid, cap, T, E, topk,
+    e = moe::launch_gemm1(dtype, pre, x, x_scale, w1, w1_scale, sorted, eids, nvalid, cap, T, E, topk,
                           D, I, block_m, a, a_scale, g1ws, zero, zero_n, s);
   if (e == hipSuccess)
-    e = moe::launch_gemm2(dtype, a, a_scale, w2, w2_scale, topk_w, sorted, eids, nvalid, cap, T,
+    e = moe::launch_gemm2(dtype, pre, a, a_scale, w2, w2_scale, topk_w, sorted, eids, nvalid, cap, T,
                           E, topk, D, I, block_m, mode, y2, s);
   if (e == hipSuccess) e = moe::launch_finalize(mode, y, T, topk, D, out, s);
   return launch_status(e);
+}
+
+int moe_preshuffle_weights(int dtype, const void* w, int64_t rows, int K, void* w_out,
+                           void* stream) {
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3 && dtype != MOE_MXFP4) return MOE_EINVAL;
+  if (rows < 0 || K < 1) return MOE_EINVAL;
+  if (rows % 16 || row_bytes(dtype, K) % 128 || (dtype == MOE_MXFP4 && K % 2)) return MOE_EUNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(w) || !ok_ptr(w_out) || w == w_out) return MOE_EINVAL;
+  const int64_t rb = row_bytes(dtype, K);
+  if (rb > INT_MAX) return MOE_ERANGE;
+  return launch_status(moe::launch_preshuffle(w, rows, (int)rb, w_out, (hipStream_t)stream));
 }
 
 }  // extern "C"

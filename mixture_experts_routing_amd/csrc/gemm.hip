@@ -147,12 +147,17 @@ __device__ __forceinline__ void mfma_fp4(f32x4_t& acc, const i32x4_t (&a)[2], co
 // scales of blocks g and 4 + g of each chunk (a padding row takes 2^0), with one 8-byte load
 // per row and chunk when the scale rows are 8-byte aligned (K % 256 == 0), else two 4-byte
 // loads.
+// Weight rows: wrow[ng] already holds this lane's part of the address.  Natural layout
+// (wshift 0, whalf 64): chunk kb of the lane's row at wrow + kb, its second half 64 bytes on.
+// Fragment-order layout (wshift 4, whalf 1024): the 16-row group's chunk kb at wrow + 16 kb,
+// second half 1024 bytes on (see preshuffle_kernel).
 template <int DT, int NG, int NT, int U>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
                                          const uint8_t* const (&xrow)[NT],
                                          const uint8_t* const (&wsc)[NG],
                                          const uint8_t* const (&xsc)[NT], int kb0, int kb1,
-                                         int kbytes, f32x4_t (&acc)[NG][NT]) {
+                                         int kbytes, int wshift, int whalf,
+                                         f32x4_t (&acc)[NG][NT]) {
   constexpr bool FP4 = DT == DT_FP4;
   const int g = lane_id() >> 4, g16 = g * 16;
   const i32x4_t zero = {0, 0, 0, 0};
@@ -179,10 +184,11 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int off = kb + 128 * u + g16;
+      const int woff = (kb + 128 * u) << wshift;
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng) {
-        wa[u][ng][0] = ld16(wrow[ng] + off);
-        wa[u][ng][1] = ld16(wrow[ng] + off + 64);
+        wa[u][ng][0] = ld16(wrow[ng] + woff);
+        wa[u][ng][1] = ld16(wrow[ng] + woff + whalf);
         if constexpr (FP4) wsa[u][ng] = scales(wsc[ng], kb + 128 * u, true);
       }
 #pragma unroll
@@ -211,13 +217,14 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
   }
   for (; kb < kb1 && kb < kbytes; kb += 128) {
     const int off = kb + g16;
+    const int woff = kb << wshift;
     const bool in1 = kb + 64 < kbytes;
     i32x4_t wa[NG][2], xb[NT][2];
     uint2 wsa[NG], xsa[NT];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
-      wa[ng][0] = ld16(wrow[ng] + off);
-      wa[ng][1] = in1 ? ld16(wrow[ng] + off + 64) : zero;
+      wa[ng][0] = ld16(wrow[ng] + woff);
+      wa[ng][1] = in1 ? ld16(wrow[ng] + woff + whalf) : zero;
       if constexpr (FP4) wsa[ng] = scales(wsc[ng], kb, in1);
     }
 #pragma unroll
@@ -290,7 +297,7 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
     const uint8_t* __restrict__ w1, const void* __restrict__ w1_scale_v,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ expert_ids,
     const int32_t* __restrict__ num_valid, int T, int E, int k, int D, int I, int mbs,
-    uint16_t* __restrict__ a_out, float4* __restrict__ zero_y, int64_t zero_n4) {
+    uint16_t* __restrict__ a_out, float4* __restrict__ zero_y, int64_t zero_n4, int pre) {
   constexpr int NT = BM / 16;
   constexpr int RG = 4 / KS;
   constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
@@ -312,8 +319,10 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
   const int n_slots = T * k;
   const int rowb = DT == DT_BF16 ? D * 2 : DT == DT_FP8 ? D : D / 2;
   const int rows_s = D / 32;  // FP4: E8M0 scales per row
-  const uint8_t* wrow[2] = {w1 + ((size_t)e * 2 * I + n_w + i16) * rowb,
-                            w1 + ((size_t)e * 2 * I + I + n_w + i16) * rowb};
+  // weight rows n_w.. (gate) and I + n_w.. (up) of expert e: 16-row groups
+  const size_t lane_w = pre ? (size_t)lane * 16 : (size_t)i16 * rowb + 16 * g;
+  const uint8_t* wrow[2] = {w1 + ((size_t)e * 2 * I + n_w) * rowb + lane_w,
+                            w1 + ((size_t)e * 2 * I + I + n_w) * rowb + lane_w};
   const uint8_t* wsc[2] = {nullptr, nullptr};
   if constexpr (FP4) {
     const uint8_t* ws8 = static_cast<const uint8_t*>(w1_scale_v);
@@ -338,7 +347,7 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
     for (int tt = 0; tt < NT; ++tt) acc[a][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, pre ? 4 : 0, pre ? 1024 : 64, acc);
   if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
 
   const int n0 = n_w + 4 * g;  // this lane's 4 channels
@@ -467,7 +476,7 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     const uint8_t* __restrict__ w2, const void* __restrict__ w2_scale_v,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
-    int k, int D, int I, int mbs, void* __restrict__ y) {
+    int k, int D, int I, int mbs, void* __restrict__ y, int pre) {
   constexpr int NT = BM / 16;
   constexpr int RG = 4 / KS;
   constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
@@ -489,8 +498,9 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   const int n_slots = T * k;
   const int rowb = DT == DT_BF16 ? I * 2 : DT == DT_FP8 ? I : I / 2;
   const int rows_s = I / 32;  // FP4: E8M0 scales per row
-  const uint8_t* wrow[2] = {w2 + ((size_t)e * D + d_w + i16) * rowb,
-                            w2 + ((size_t)e * D + d_w + 16 + i16) * rowb};
+  const size_t lane_w = pre ? (size_t)lane * 16 : (size_t)i16 * rowb + 16 * g;
+  const uint8_t* wrow[2] = {w2 + ((size_t)e * D + d_w) * rowb + lane_w,
+                            w2 + ((size_t)e * D + d_w + 16) * rowb + lane_w};
   const uint8_t* wsc[2] = {nullptr, nullptr};
   if constexpr (FP4) {
     const uint8_t* ws8 = static_cast<const uint8_t*>(w2_scale_v);
@@ -515,7 +525,7 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     for (int tt = 0; tt < NT; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, pre ? 4 : 0, pre ? 1024 : 64, acc);
   if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
 
   float ws[2][4];
@@ -584,6 +594,7 @@ struct PfArgs {
   const float* topk_w;
   int T, k, N, K, e, nt;
   void* out;
+  int pre;  // weights in fragment order (preshuffle_kernel)
 };
 
 // One tile of NB sorted blocks (64 NB slot rows) x the block's 256 weight rows, 8 waves.
@@ -638,10 +649,14 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
   // weight rows: instruction jw = wave + 8 u covers block rows 8 jw .. 8 jw + 7, i.e. group
   // q = (br / 16) % 4 of wave group br / 64.  Rows past N read row 0 (results not stored).
   const uint8_t* wexp = G1 ? p.w + (size_t)p.e * 2 * N * rowb : p.w + (size_t)p.e * N * rowb;
+  // Fragment-order weights: instruction jw = wave + 8 u copies half jw % 2 (1 KB, already in
+  // MFMA lane order) of the chunk of block row group jw / 2 (rows 16 (jw / 2) .. + 15).
   uint32_t woff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int br = 8 * (wave + 8 * u) + rsub, wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
+    const int jw = wave + 8 * u;
+    const int br = p.pre ? 16 * (jw >> 1) : 8 * jw + rsub;
+    const int wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
     int row, ch;
     if constexpr (G1) {
       ch = p.nt * 128 + 32 * wg + 16 * (q & 1) + i;
@@ -651,6 +666,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
       row = ch;
     }
     woff[u] = (uint32_t)((ch < N ? row : 0) * rowb);
+    if (p.pre) woff[u] += (uint32_t)(1024 * (jw & 1) + 16 * lane);
   }
   const int row0 = G1 ? p.nt * 128 + wr * 32 : p.nt * 256 + wr * 64;
   const bool on = row0 < N;
@@ -689,11 +705,12 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     const uint32_t bo = ring_lds + (uint32_t)((c % NBUF) * BUF);
     const uint32_t lo = (c * 128 + 64 >= rowb && ls >= 4) ? 16u * (ls & 3) : 16u * ls;
     const uint8_t* tb = p.act + (size_t)c * 128;
-    const uint8_t* wb = wexp + (size_t)c * 128;
+    const uint8_t* wb = wexp + (size_t)c * (p.pre ? 2048 : 128);
+    const uint32_t wlo = p.pre ? 0u : lo;
 #pragma unroll
     for (int v = 0; v < NB; ++v) dma16_to_lds_s(tb, toff[v] + lo, bo + (wave + 8 * v) * 1024);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma16_to_lds_s(wb, woff[u] + lo, bo + TOKB + (wave + 8 * u) * 1024);
+    for (int u = 0; u < 4; ++u) dma16_to_lds_s(wb, woff[u] + wlo, bo + TOKB + (wave + 8 * u) * 1024);
     if constexpr (FP4) {
       const uint8_t* sa = static_cast<const uint8_t*>(p.act_scale) + (size_t)c * 8;
       const uint8_t* sw = wscale + (size_t)c * 8;
@@ -712,6 +729,15 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     for (int m = 0; m < MH; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int fsw = (i16 >> 1) & 7;  // read-side swizzle of row i16 of any 16-row group
+  // weight fragment (q, h) of this lane, relative to the buffer's weight rows: natural rows
+  // swizzled as the slot rows, or fragment order (group 4 wr + q, half h, 16 bytes per lane)
+  int wofs[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      wofs[q][h] = p.pre ? ((4 * wr + q) * 2 + h) * 1024 + 16 * lane
+                         : (64 * wr + 16 * q + i16) * 128 + 16 * ((4 * h + g) ^ fsw);
   issue(0);
   if (NBUF == 3 && nch > 1) issue(1);
   if (NBUF == 3 && nch > 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
@@ -721,7 +747,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     const bool more = c + NBUF - 1 < nch;
     if (more) issue(c + NBUF - 1);
     const uint8_t* tb = ring + (c % NBUF) * BUF;
-    const uint8_t* wbuf = tb + TOKB + (64 * wr) * 128;
+    const uint8_t* wbuf = tb + TOKB;
     // mxfp4: this lane's scale bytes (blocks g and 4 + g of the chunk) of its weight rows
     int wsc0[4] = {127, 127, 127, 127}, wsc1[4] = {127, 127, 127, 127};
     if constexpr (FP4) {
@@ -737,7 +763,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        wf[q][h] = *reinterpret_cast<const i32x4_t*>(&wbuf[(16 * q + i16) * 128 + 16 * ((4 * h + g) ^ fsw)]);
+        wf[q][h] = *reinterpret_cast<const i32x4_t*>(&wbuf[wofs[q][h]]);
     if (c * 128 + 64 >= rowb) {  // half last chunk
       const i32x4_t zero = {0, 0, 0, 0};
 #pragma unroll
@@ -884,7 +910,7 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
     int k, int N, int K, int mbs, void* __restrict__ out, float4* __restrict__ zero_y,
-    int64_t zero_n4) {
+    int64_t zero_n4, int pre) {
   constexpr bool G1 = MODE == PF_G1;
   __shared__ __align__(16) uint8_t ring[kPfRingBytes];
   __shared__ int s_slot[kPfMaxRows];
@@ -928,7 +954,7 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
     s_fac[i] = f;
   }
   __syncthreads();  // s_slot, s_fac
-  const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out};
+  const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out, pre};
   switch (nb) {
     case 1: prefill_tile<DT, MODE, 1>(p, s_slot, s_fac, ring); break;
     case 2: prefill_tile<DT, MODE, 2>(p, s_slot, s_fac, ring); break;
@@ -984,6 +1010,25 @@ __global__ void __launch_bounds__(256) zero_f32_kernel(float4* __restrict__ p, i
 }
 
 // ----------------------------------------------------------------------------- host side
+// ----------------------------------------------------------------------------- weight layout
+// Fragment order: for each group of 16 consecutive rows (rows R*16 .. R*16+15 of rowb bytes)
+// and each 128-byte K chunk c, 2 KB = [half h][lane l = i + 16 g][16 bytes] holding bytes
+// [c*128 + 64 h + 16 g, + 16) of row 16 R + i -- the 16 bytes lane l loads for its h-th
+// operand register of the chunk.  One 16-byte piece per thread; the stores are contiguous.
+__global__ void __launch_bounds__(256) preshuffle_kernel(const uint8_t* __restrict__ w, int64_t n16,
+                                                         int rowb, uint8_t* __restrict__ out) {
+  const int nch = rowb >> 7;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n16; t += (int64_t)gridDim.x * 256) {
+    const int l = (int)(t & 63), h = (int)((t >> 6) & 1);
+    const int64_t cr = t >> 7;  // chunk index within the whole matrix: R * nch + c
+    const int64_t R = cr / nch;
+    const int c = (int)(cr - R * nch);
+    const int64_t row = R * 16 + (l & 15);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(w + row * rowb + c * 128 + 64 * h + 16 * (l >> 4));
+    *reinterpret_cast<u32x4*>(out + t * 16) = v;
+  }
+}
+
 static int grid_1d(int64_t n, int cap_blocks = 4096) {
   int64_t b = (n + 255) / 256;
   if (b < 1) b = 1;
@@ -994,6 +1039,14 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st) {
   const int64_t n4 = n / 4;  // callers pass multiples of 4 (D % 64 == 0)
   if (n4 == 0) return hipSuccess;
   zero_f32_kernel<<<grid_1d(n4), 256, 0, st>>>(reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_preshuffle(const void* w, int64_t rows, int rowb, void* out, hipStream_t st) {
+  const int64_t n16 = rows * (rowb / 16);
+  if (n16 == 0) return hipSuccess;
+  preshuffle_kernel<<<grid_1d(n16), 256, 0, st>>>(static_cast<const uint8_t*>(w), n16, rowb,
+                                                 static_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 
@@ -1021,26 +1074,26 @@ template <int BM, int DT, int KS>
 static void gemm1_go(const void* x, const void* x_scale, const void* w1, const void* w1_scale,
                      const int32_t* sorted_ids, const int32_t* expert_ids,
                      const int32_t* num_valid, int mbs, int T, int E, int k, int D, int I,
-                     uint16_t* a_bf16, float* zero_y, int64_t zero_n, hipStream_t st) {
+                     uint16_t* a_bf16, float* zero_y, int64_t zero_n, int pre, hipStream_t st) {
   constexpr int U = BM == 64 ? 2 : 4;
   constexpr int RG = 4 / KS;
   const dim3 grid(xcd_grid(mbs, I / (16 * RG)));
   gemm1_kernel<BM, DT, U, KS><<<grid, 256, 0, st>>>(
       (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale, sorted_ids, expert_ids, num_valid,
-      T, E, k, D, I, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4);
+      T, E, k, D, I, mbs, a_bf16, reinterpret_cast<float4*>(zero_y), zero_n / 4, pre);
 }
 
 template <int BM, int DT>
 static void gemm1_ks(int ks, const void* x, const void* x_scale, const void* w1,
                      const void* w1_scale, const int32_t* sorted_ids, const int32_t* expert_ids,
                      const int32_t* num_valid, int mbs, int T, int E, int k, int D, int I,
-                     uint16_t* a_bf16, float* zero_y, int64_t zero_n, hipStream_t st) {
+                     uint16_t* a_bf16, float* zero_y, int64_t zero_n, int pre, hipStream_t st) {
   if (ks == 4)
-    gemm1_go<BM, DT, 4>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+    gemm1_go<BM, DT, 4>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, pre, st);
   else if (ks == 2)
-    gemm1_go<BM, DT, 2>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+    gemm1_go<BM, DT, 2>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, pre, st);
   else
-    gemm1_go<BM, DT, 1>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st);
+    gemm1_go<BM, DT, 1>(x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, pre, st);
 }
 
 // The quantised types write bf16 rows to the workspace, then requantise them into a.
@@ -1058,7 +1111,7 @@ static hipError_t requant(int dt, const uint16_t* a_bf16, int T, int k, int I, v
   return hipGetLastError();
 }
 
-hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* w1,
+hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, const void* w1,
                         const void* w1_scale, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
                         int E, int k, int D, int I, int B, void* a, void* a_scale, void* ws,
@@ -1072,7 +1125,7 @@ hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* 
   gemm_prefill_kernel<DTV, PF_G1><<<grid, 512, 0, st>>>((const uint8_t*)x, x_scale, (const uint8_t*)w1, \
                                                        w1_scale, nullptr, sorted_ids, expert_ids,       \
                                                        num_valid, T, E, k, I, D, mbs, a_bf16,           \
-                                                       reinterpret_cast<float4*>(zero_y), zero_n / 4)
+                                                       reinterpret_cast<float4*>(zero_y), zero_n / 4, pre)
     if (dt == DT_FP8)
       MOE_PF1(DT_FP8);
     else if (dt == DT_FP4)
@@ -1087,7 +1140,7 @@ hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* 
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int ks = pick_ks(n_act * (I / 16));  // a block covers 16*(4/ks) channels; I % 64 == 0
 #define MOE_G1_DT(BMV, DTV) \
-  gemm1_ks<BMV, DTV>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, st)
+  gemm1_ks<BMV, DTV>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, pre, st)
 #define MOE_G1(BMV)                          \
   if (dt == DT_FP8) MOE_G1_DT(BMV, DT_FP8);   \
   else if (dt == DT_FP4) MOE_G1_DT(BMV, DT_FP4); \
@@ -1110,29 +1163,29 @@ template <int BM, int DT, int OM, int KS>
 static void gemm2_go(int mbs, const void* a, const void* a_scale, const void* w2,
                      const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
-                     int D, int I, void* y, hipStream_t st) {
+                     int D, int I, void* y, int pre, hipStream_t st) {
   constexpr int U = BM == 64 ? 2 : 4;
   constexpr int RG = 4 / KS;
   const dim3 grid(xcd_grid(mbs, (D + 32 * RG - 1) / (32 * RG)));
   gemm2_kernel<BM, DT, U, OM, KS><<<grid, 256, 0, st>>>(
       (const uint8_t*)a, a_scale, (const uint8_t*)w2, w2_scale, topk_w, sorted_ids, expert_ids,
-      num_valid, T, E, k, D, I, mbs, y);
+      num_valid, T, E, k, D, I, mbs, y, pre);
 }
 
 template <int BM, int DT, int OM>
 static void gemm2_ks(int ks, int mbs, const void* a, const void* a_scale, const void* w2,
                      const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
-                     int D, int I, void* y, hipStream_t st) {
+                     int D, int I, void* y, int pre, hipStream_t st) {
   if (ks == 4)
-    gemm2_go<BM, DT, OM, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, DT, OM, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
   else if (ks == 2)
-    gemm2_go<BM, DT, OM, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, DT, OM, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
   else
-    gemm2_go<BM, DT, OM, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st);
+    gemm2_go<BM, DT, OM, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
 }
 
-hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* w2,
+hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, const void* w2,
                         const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
                         int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st) {
@@ -1143,7 +1196,7 @@ hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* 
 #define MOE_PF2(DTV, MD)                                                                                \
   gemm_prefill_kernel<DTV, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,    \
                                                     w2_scale, topk_w, sorted_ids, expert_ids, num_valid, \
-                                                    T, E, k, D, I, mbs, y, nullptr, 0)
+                                                    T, E, k, D, I, mbs, y, nullptr, 0, pre)
 #define MOE_PF2_MODES(F8)                                   \
   if (mode == OM_REDUCE) MOE_PF2(F8, PF_G2_REDUCE);         \
   else if (mode == OM_ATOMIC) MOE_PF2(F8, PF_G2_ATOMIC);    \
@@ -1162,7 +1215,7 @@ hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* 
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int ks = pick_ks(n_act * (D / 32));  // ks >= 2 needs D % 64 == 0, which always holds
 #define MOE_G2_OM(BMV, DTV, OMV) \
-  gemm2_ks<BMV, DTV, OMV>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, st)
+  gemm2_ks<BMV, DTV, OMV>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st)
 #define MOE_G2_DT(BMV, DTV)                                  \
   if (mode == OM_REDUCE) MOE_G2_OM(BMV, DTV, OM_REDUCE);      \
   else if (mode == OM_ATOMIC) MOE_G2_OM(BMV, DTV, OM_ATOMIC); \

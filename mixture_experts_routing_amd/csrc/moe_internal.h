@@ -41,13 +41,15 @@ hipError_t launch_aux_scores(const float* logits, int T, int E, int k, int score
 hipError_t launch_aux_scores_backward(const float* logits, const float* grad_scores, int T, int E,
                                       int score, float* grad_logits, hipStream_t st);
 
-hipError_t launch_gemm1(int dt, const void* x, const void* x_scale, const void* w1,
+// pre: weights in fragment order (launch_preshuffle), which needs rows of whole 128-byte
+// chunks and 16-row groups.
+hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, const void* w1,
                         const void* w1_scale, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
                         int E, int k, int D, int I, int B, void* a, void* a_scale, void* ws,
                         float* zero_y, int64_t zero_n, hipStream_t st);
 
-hipError_t launch_gemm2(int dt, const void* a, const void* a_scale, const void* w2,
+hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, const void* w2,
                         const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
                         int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st);
@@ -60,5 +62,8 @@ hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16
                            hipStream_t st);
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
+
+// Weight rows (rows a multiple of 16, rowb a multiple of 128 bytes) into fragment order.
+hipError_t launch_preshuffle(const void* w, int64_t rows, int rowb, void* out, hipStream_t st);
 
 }  // namespace moe

@@ -258,6 +258,28 @@ def test_aux_scores_validation(lib):
         assert bwd(**{key: None}) == EINVAL and bwd(**{key: BAD_ALIGN}) == EINVAL
 
 
+def test_preshuffle_validation(lib):
+    PRE = 0x100
+
+    def ps(dtype=0, rows=32, K=128, w=GOOD, o=0x20000):
+        return lib.moe_preshuffle_weights(dtype, w, rows, K, o, None)
+
+    assert ps(dtype=3) == EINVAL and ps(dtype=PRE) == EINVAL   # flags are not a dtype here
+    assert ps(rows=-16) == EINVAL and ps(K=0) == EINVAL
+    assert ps(rows=24) == EUNSUP                                  # not whole 16-row groups
+    assert ps(dtype=0, K=96) == EUNSUP                            # bf16 rows of 192 bytes
+    assert ps(dtype=1, K=192) == EUNSUP                           # fp8 rows of 192 bytes
+    assert ps(dtype=2, K=384) == EUNSUP                           # mxfp4 rows of 192 bytes
+    assert ps(rows=0, w=None, o=None) == OK
+    assert ps(w=None) == EINVAL and ps(o=BAD_ALIGN) == EINVAL and ps(o=GOOD) == EINVAL  # w == out
+    # the flag on the GEMM calls: fp8 rows must be whole 128-byte chunks (D = 192 is not)
+    assert gemm1_call(lib, dtype=1 | PRE, D=192, I=128) == EUNSUP
+    assert gemm2_call(lib, dtype=1 | PRE, D=128, I=192) == EUNSUP
+    assert gemm1_call(lib, dtype=3 | PRE) == EINVAL
+    # and is ignored by the workspace functions
+    assert lib.moe_gemm1_workspace_bytes(1 | PRE, 4, 2, 128) == lib.moe_gemm1_workspace_bytes(1, 4, 2, 128)
+
+
 def test_strerror(lib):
     import mixture_experts_routing_amd as m
     texts = {m.moe_strerror(s) for s in (OK, EINVAL, ERANGE, ENOSPC, EUNSUP, ELAUNCH)}
