@@ -57,7 +57,8 @@ def log(msg):
 
 def graph_ms_per_call(torch, calls, n, reps=5):
     """ms per call of `calls(i, stream)` for i in range(n), captured back to back in one HIP
-    graph and replayed (median over `reps` replays).  Host launch cost is excluded, as in the
+    graph and replayed (median over `reps` timed replays, after a quarter second of untimed
+    ones).  Host launch cost is excluded, as in the
     graph-replay measurement of the mxfp4 page ("Measurement").  Falls back to eager launches
     if the capture fails."""
     stream = torch.cuda.current_stream()
@@ -72,6 +73,12 @@ def graph_ms_per_call(torch, calls, n, reps=5):
                 calls(i, cs)
         g.replay()
         torch.cuda.synchronize()
+        # untimed replays for about a quarter second first, so that the timed replays do not
+        # start while the GPU clocks are still coming up from the idle host-side set-up
+        t_end = time.perf_counter() + 0.25
+        while time.perf_counter() < t_end:
+            g.replay()
+            torch.cuda.synchronize()
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
