@@ -6,14 +6,17 @@ Headline: MoE-layer microseconds per call at T=16 decode on the DeepSeek-R1 shap
 moe_forward call -- routing (top-k softmax + sort), gate-up GEMM with SiLU-mul, down
 GEMM with the routed weight, combine -- on inputs already resident in HBM.  Eight
 input sets (logits and activations) rotate so the active experts change call to call.
+The expert weights are put in MFMA fragment order once before timing
+(moe_preshuffle_weights, the one-time weight preparation a serving process does at load);
+--natural-weights times them in their [E, N, K] layout, which is also a secondary line.
 
 The JSON line also carries the roofline of the dominant kernel (HIP events on the
 stream it runs on), the CPU oracle's time on a bounded sample, and (unless
 --headline-only) secondary lines: GPT-OSS decode/prefill and Kimi fp8 layer times
 with per-GEMM TFLOPS, the DeepSeek and Kimi layers again with packed bf16 atomics into
 the output, the Kimi shape in mxfp4 (a4w4), the Kimi prefill with the reduce-mode combine
-(per-slot rows summed by the finalize kernel) instead of atomics, decode lines with the weights
-in fragment order (moe_preshuffle_weights), router-only GB/s at T=8192 (forward and
+(per-slot rows summed by the finalize kernel) instead of atomics, the headline in the other
+weight layout and the other decode lines with the weights in fragment order, router-only GB/s at T=8192 (forward and
 backward), the group-limited router at the DeepSeek-V3 routing shape, and the auxiliary-loss
 scores forward and backward at T=8192.
 """
@@ -46,6 +49,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary lines")
+    ap.add_argument("--natural-weights", action="store_true",
+                    help="headline with the weights in their natural [E, N, K] layout instead of "
+                         "fragment order (moe_preshuffle_weights, applied once before timing)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -55,9 +61,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def graph_ms_per_call(torch, calls, n, reps=5):
+def graph_ms_per_call(torch, calls, n, reps=5, warm_s=0.25):
     """ms per call of `calls(i, stream)` for i in range(n), captured back to back in one HIP
-    graph and replayed (median over `reps` timed replays, after a quarter second of untimed
+    graph and replayed (median over `reps` timed replays, after `warm_s` seconds of untimed
     ones).  Host launch cost is excluded, as in the
     graph-replay measurement of the mxfp4 page ("Measurement").  Falls back to eager launches
     if the capture fails."""
@@ -73,9 +79,9 @@ def graph_ms_per_call(torch, calls, n, reps=5):
                 calls(i, cs)
         g.replay()
         torch.cuda.synchronize()
-        # untimed replays for about a quarter second first, so that the timed replays do not
-        # start while the GPU clocks are still coming up from the idle host-side set-up
-        t_end = time.perf_counter() + 0.25
+        # untimed replays first, so that the timed replays do not start while the GPU clocks
+        # are still coming up from the idle host-side set-up
+        t_end = time.perf_counter() + warm_s
         while time.perf_counter() < t_end:
             g.replay()
             torch.cuda.synchronize()
@@ -128,9 +134,11 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
     log(f"{wl.name} T={T} E={E} k={k} D={D} I={I} B={B} {dtype} {mode}"
         f"{' preshuffled' if preshuffled else ''}: generating inputs")
     base = synth.layer_inputs(wl, 1, seed=0, device=dev)
+    # the weights the GPU calls read (base keeps the natural layout for the CPU oracle)
+    gw = {key: base[key] for key in ("w1", "w2")}
     if preshuffled:
         for key in ("w1", "w2"):
-            base[key] = m.moe_preshuffle_weights(dtype, base[key])
+            gw[key] = m.moe_preshuffle_weights(dtype, base[key])
         torch.cuda.synchronize()
     pre = dict(preshuffled=True) if preshuffled else {}
     sets = []
@@ -145,7 +153,7 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
 
     def layer_call(i, st):
         s = sets[i % len(sets)]
-        m.moe_forward(dtype, s["logits"], s["x"], base["w1"], base["w2"], k, B, mode,
+        m.moe_forward(dtype, s["logits"], s["x"], gw["w1"], gw["w2"], k, B, mode,
                       x_scale=s.get("x_scale"), w1_scale=base.get("w1_scale"),
                       w2_scale=base.get("w2_scale"), workspace=ws, out=out, stream=st, **pre)
 
@@ -153,7 +161,9 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
         layer_call(i, stream)
     torch.cuda.synchronize()
     log(f"timing {steps} moe_forward calls (graph replay)")
-    ms_per_call, how = graph_ms_per_call(torch, layer_call, steps)
+    # a full second of untimed replays: the whole-layer graph is the first GPU work after the
+    # host-side input set-up, and a quarter second left it reading up to 3% slow
+    ms_per_call, how = graph_ms_per_call(torch, layer_call, steps, warm_s=1.0)
 
     # per-stage durations: each stage alone, `steps` calls per graph, on per-set routing
     views = m.workspace_views(ws, offs, dtype, mode, T, E, k, D, I, B)
@@ -175,13 +185,13 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
 
     def gemm1_call(i, st):
         j = i % len(sets)
-        m.moe_gemm1_gateup(dtype, sets[j]["x"], base["w1"], routes[j], k, B, x_scale=sets[j].get("x_scale"),
+        m.moe_gemm1_gateup(dtype, sets[j]["x"], gw["w1"], routes[j], k, B, x_scale=sets[j].get("x_scale"),
                            w1_scale=base.get("w1_scale"), a=a, a_scale=a_scale, workspace=g1ws, stream=st,
                            **pre)
 
     def gemm2_call(i, st):
         j = i % len(sets)
-        m.moe_gemm2_down(dtype, a, base["w2"], routes[j], T, k, B, mode, a_scale=a_scale,
+        m.moe_gemm2_down(dtype, a, gw["w2"], routes[j], T, k, B, mode, a_scale=a_scale,
                          w2_scale=base.get("w2_scale"), y=y, stream=st, **pre)
 
     def fin_call(i, st):
@@ -499,7 +509,8 @@ def main():
         del src, dst
 
     wl = synth.WORKLOADS[args.workload]
-    head, keep = measure_layer(env, wl, args.T, args.steps, args.warmup, args.rotate)
+    head, keep = measure_layer(env, wl, args.T, args.steps, args.warmup, args.rotate,
+                               preshuffled=not args.natural_weights)
     g1 = head["gemm"]["gemm1"]
     g2 = head["gemm"]["gemm2"]
     dom_name, dom = max((("gemm1", g1), ("gemm2", g2)), key=lambda kv: kv[1]["us"])
@@ -534,12 +545,14 @@ def main():
             del kp
             torch.cuda.empty_cache()
             secondary.append(r)
-        # weights in fragment order (prepared once, outside the timed region)
-        for name, T in (("deepseek", 16), ("kimi", 64), ("kimi_mxfp4", 64), ("gptoss", 16)):
+        # the headline with the other weight layout, and the decode lines in fragment order
+        # (prepared once, outside the timed region)
+        for name, T, pre in ((args.workload, args.T, args.natural_weights), ("kimi", 64, True),
+                             ("kimi_mxfp4", 64, True), ("gptoss", 16, True)):
             # input sets rotated as in the natural-layout line of the same workload
-            rot = args.rotate if name == "deepseek" else 2
+            rot = args.rotate if name == args.workload else 2
             r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, rot, None,
-                                  preshuffled=True)
+                                  preshuffled=pre)
             del kp
             torch.cuda.empty_cache()
             secondary.append(r)
@@ -570,7 +583,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}-shaped MoE layer forward, T={args.T}", "T": args.T, "E": wl.E,
                    "topk": wl.topk, "D": wl.D, "I": wl.I, "block_m": wl.block_m, "mode": wl.mode,
-                   "score": "softmax", "renorm": True, "rotating_input_sets": args.rotate},
+                   "score": "softmax", "renorm": True, "rotating_input_sets": args.rotate,
+                   "weights": head["weights"] + (" (moe_preshuffle_weights, once, before timing)"
+                                                 if not args.natural_weights else "")},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "layer": head,

@@ -35,6 +35,11 @@ struct alignas(16) u32x4 {
 __device__ __forceinline__ i32x4_t ld16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4_t*>(p);
 }
+// The same for bytes read exactly once per call (decode weight rows): non-temporal, so the
+// caches keep the rows that are reused (gathered activations, sorted lists).
+__device__ __forceinline__ i32x4_t ld16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(p));
+}
 
 // Output modes of stage 2 (moe_mode): fp32 atomic accumulation, fp32 slot rows, or packed
 // bf16 atomic accumulation straight into the bf16 output.
@@ -148,17 +153,21 @@ __device__ __forceinline__ void mfma_fp4(f32x4_t& acc, const i32x4_t (&a)[2], co
 // per row and chunk when the scale rows are 8-byte aligned (K % 256 == 0), else two 4-byte
 // loads.
 // Weight rows: wrow[ng] already holds this lane's part of the address.  Natural layout
-// (wshift 0, whalf 64): chunk kb of the lane's row at wrow + kb, its second half 64 bytes on.
-// Fragment-order layout (wshift 4, whalf 1024): the 16-row group's chunk kb at wrow + 16 kb,
-// second half 1024 bytes on (see preshuffle_kernel).
-template <int DT, int NG, int NT, int U>
+// (PRE false): chunk kb of the lane's row at wrow + kb, its second half 64 bytes on.
+// Fragment-order layout (PRE true): the 16-row group's chunk kb at wrow + 16 kb, second half
+// 1024 bytes on (see preshuffle_kernel).
+template <int DT, int NG, int NT, int U, bool PRE>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
                                          const uint8_t* const (&xrow)[NT],
                                          const uint8_t* const (&wsc)[NG],
                                          const uint8_t* const (&xsc)[NT], int kb0, int kb1,
-                                         int kbytes, int wshift, int whalf,
-                                         f32x4_t (&acc)[NG][NT]) {
+                                         int kbytes, f32x4_t (&acc)[NG][NT]) {
   constexpr bool FP4 = DT == DT_FP4;
+  constexpr int wshift = PRE ? 4 : 0, whalf = PRE ? 1024 : 64;
+  // fragment order: each weight load covers 1 KB of whole lines, read once per call, so it
+  // is non-temporal; the natural layout reads each line in two halves by two loads, and the
+  // line must stay cached between them
+  auto wld = [](const uint8_t* q) { return PRE ? ld16_stream(q) : ld16(q); };
   const int g = lane_id() >> 4, g16 = g * 16;
   const i32x4_t zero = {0, 0, 0, 0};
   const bool pair8 = (kbytes & 127) == 0;  // scale rows of kbytes / 16 bytes, a multiple of 8
@@ -187,8 +196,8 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
       const int woff = (kb + 128 * u) << wshift;
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng) {
-        wa[u][ng][0] = ld16(wrow[ng] + woff);
-        wa[u][ng][1] = ld16(wrow[ng] + woff + whalf);
+        wa[u][ng][0] = wld(wrow[ng] + woff);
+        wa[u][ng][1] = wld(wrow[ng] + woff + whalf);
         if constexpr (FP4) wsa[u][ng] = scales(wsc[ng], kb + 128 * u, true);
       }
 #pragma unroll
@@ -223,8 +232,8 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
     uint2 wsa[NG], xsa[NT];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
-      wa[ng][0] = ld16(wrow[ng] + woff);
-      wa[ng][1] = in1 ? ld16(wrow[ng] + woff + whalf) : zero;
+      wa[ng][0] = wld(wrow[ng] + woff);
+      wa[ng][1] = in1 ? wld(wrow[ng] + woff + whalf) : zero;
       if constexpr (FP4) wsa[ng] = scales(wsc[ng], kb, in1);
     }
 #pragma unroll
@@ -347,7 +356,8 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
     for (int tt = 0; tt < NT; ++tt) acc[a][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, pre ? 4 : 0, pre ? 1024 : 64, acc);
+  if (pre) mainloop<DT, 2, NT, U, true>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  else mainloop<DT, 2, NT, U, false>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
   if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
 
   const int n0 = n_w + 4 * g;  // this lane's 4 channels
@@ -525,7 +535,8 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     for (int tt = 0; tt < NT; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  mainloop<DT, 2, NT, U>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, pre ? 4 : 0, pre ? 1024 : 64, acc);
+  if (pre) mainloop<DT, 2, NT, U, true>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  else mainloop<DT, 2, NT, U, false>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
   if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
 
   float ws[2][4];
