@@ -120,3 +120,34 @@ def test_preshuffled_deepseek_decode_full_size():
                              preshuffled=True)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1)
+
+
+@pytest.mark.parametrize("name,T,tokens", [
+    ("deepseek", 16, [0, 9, 15]),
+    ("gptoss", 16, [0, 7, 15]),
+    ("kimi", 64, [0, 33, 63]),
+    ("kimi_mxfp4", 64, [0, 33, 63]),
+])
+def test_preshuffled_full_size_sampled(name, T, tokens):
+    """The decode workloads in the configuration the benchmark times them in: weights in
+    fragment order (non-temporal weight loads), the workload's own output mode, moe_forward;
+    sampled tokens against the oracle."""
+    import mixture_experts_routing_amd as m
+    wl = synth.WORKLOADS[name]
+    g = synth.layer_inputs(wl, 1, seed=0, device="cuda")
+    g["logits"] = synth.logits(T, wl.E, seed=T).cuda()
+    g.update({kk: v.cuda() for kk, v in synth.activations(T, wl.D, wl.dtype, seed=T, x_std=wl.x_std).items()})
+    w1p = m.moe_preshuffle_weights(wl.dtype, g["w1"])
+    w2p = m.moe_preshuffle_weights(wl.dtype, g["w2"])
+    out, _, _ = m.moe_forward(wl.dtype, g["logits"], g["x"], w1p, w2p, wl.topk, wl.block_m, wl.mode,
+                              x_scale=g.get("x_scale"), w1_scale=g.get("w1_scale"),
+                              w2_scale=g.get("w2_scale"), preshuffled=True)
+    torch.cuda.synchronize()
+    del w1p, w2p
+    ref = oracle_layer(g, oracle_route(g["logits"], wl.topk, wl.block_m), wl.dtype, tokens=tokens)
+    if wl.dtype == "bf16":
+        compare_out(out, ref.out, np.array(tokens), BF16_TOL, BF16_COS)
+    else:
+        compare_out(out, ref.out, np.array(tokens), FP8_TOL, None)
+    del g
+    torch.cuda.empty_cache()
