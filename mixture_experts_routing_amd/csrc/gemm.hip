@@ -478,9 +478,10 @@ __global__ void __launch_bounds__(256) requant_mx_kernel(const uint16_t* __restr
 }
 
 // ----------------------------------------------------------------------------- stage 2
-// Block = 4 waves = RG = 4/KS row groups x KS parts of K; a row group is 32
-// model_dim rows.  grid: ceil(D/(32*RG)) channel tiles x cap/BM row blocks.
-template <int BM, int DT, int U, int OM, int KS>
+// Block = 4 waves = RG = 4/KS row groups x KS parts of K; a row group is 16*NG
+// model_dim rows (NG = 2, or 4 for short rows without a K split: see gemm2_ks).
+// grid: ceil(D/(16*NG*RG)) channel tiles x cap/BM row blocks.
+template <int BM, int DT, int U, int OM, int KS, int NG>
 __global__ void __launch_bounds__(256) gemm2_kernel(
     const uint8_t* __restrict__ a, const void* __restrict__ a_scale_v,
     const uint8_t* __restrict__ w2, const void* __restrict__ w2_scale_v,
@@ -492,15 +493,16 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
   const float* a_scale = static_cast<const float*>(a_scale_v);
   const float* w2_scale = static_cast<const float*>(w2_scale_v);
-  __shared__ f32x4_t red[KS > 1 ? (KS - 1) * RG * 2 * NT * 64 : 1];
+  __shared__ f32x4_t red[KS > 1 ? (KS - 1) * RG * NG * NT * 64 : 1];
   int mb, nt;
-  if (!block_tile(mbs, (D + 32 * RG - 1) / (32 * RG), mb, nt)) return;
+  if (!block_tile(mbs, (D + 16 * NG * RG - 1) / (16 * NG * RG), mb, nt)) return;
   if (mb * BM >= *num_valid) return;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int rg = wave / KS, kp = wave % KS;
-  const int d_w = nt * 32 * RG + rg * 32;
+  const int d_w = nt * 16 * NG * RG + rg * 16 * NG;
   // a partial last tile only happens with KS == 1 (the host keeps D % (32*RG) == 0
-  // otherwise), so leaving here never skips a barrier
+  // otherwise, with NG == 2), so leaving here never skips a barrier; D % 64 == 0 keeps a
+  // wave's 16*NG rows inside D once d_w < D
   if (KS == 1 && d_w >= D) return;
   const int e = expert_ids[mb];
   if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
@@ -509,13 +511,14 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   const int rowb = DT == DT_BF16 ? I * 2 : DT == DT_FP8 ? I : I / 2;
   const int rows_s = I / 32;  // FP4: E8M0 scales per row
   const size_t lane_w = pre ? (size_t)lane * 16 : (size_t)i16 * rowb + 16 * g;
-  const uint8_t* wrow[2] = {w2 + ((size_t)e * D + d_w) * rowb + lane_w,
-                            w2 + ((size_t)e * D + d_w + 16) * rowb + lane_w};
-  const uint8_t* wsc[2] = {nullptr, nullptr};
-  if constexpr (FP4) {
-    const uint8_t* ws8 = static_cast<const uint8_t*>(w2_scale_v);
-    wsc[0] = ws8 + ((size_t)e * D + d_w + i16) * rows_s;
-    wsc[1] = ws8 + ((size_t)e * D + d_w + 16 + i16) * rows_s;
+  const uint8_t* wrow[NG];
+  const uint8_t* wsc[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    wrow[q] = w2 + ((size_t)e * D + d_w + 16 * q) * rowb + lane_w;
+    wsc[q] = nullptr;
+    if constexpr (FP4)
+      wsc[q] = static_cast<const uint8_t*>(w2_scale_v) + ((size_t)e * D + d_w + 16 * q + i16) * rows_s;
   }
   const uint8_t* xrow[NT];
   const uint8_t* xsc[NT];
@@ -528,25 +531,25 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     xrow[tt] = real ? a + (size_t)s * rowb : nullptr;
     xsc[tt] = FP4 && real ? static_cast<const uint8_t*>(a_scale_v) + (size_t)s * rows_s : nullptr;
   }
-  f32x4_t acc[2][NT];
+  f32x4_t acc[NG][NT];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < NG; ++q)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  if (pre) mainloop<DT, 2, NT, U, true>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
-  else mainloop<DT, 2, NT, U, false>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
-  if (!reduce_k_split<KS, RG, 2, NT>(acc, rg, kp, red)) return;
+  if (pre) mainloop<DT, NG, NT, U, true>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  else mainloop<DT, NG, NT, U, false>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  if (!reduce_k_split<KS, RG, NG, NT>(acc, rg, kp, red)) return;
 
-  float ws[2][4];
+  float ws[NG][4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < NG; ++q)
 #pragma unroll
     for (int r = 0; r < 4; ++r) ws[q][r] = 1.f;
   if constexpr (FP8) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < NG; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) ws[q][r] = w2_scale[(size_t)e * D + d_w + 16 * q + 4 * g + r];
   }
@@ -557,7 +560,7 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     float sc = topk_w[s];
     if constexpr (FP8) sc *= a_scale[s];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NG; ++q) {
       const int d0 = d_w + 16 * q + 4 * g;
       float c[4];
 #pragma unroll
@@ -1170,15 +1173,15 @@ hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, con
   return requant(dt, a_bf16, T, k, I, a, a_scale, st);
 }
 
-template <int BM, int DT, int OM, int KS>
+template <int BM, int DT, int OM, int KS, int NG = 2>
 static void gemm2_go(int mbs, const void* a, const void* a_scale, const void* w2,
                      const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
                      int D, int I, void* y, int pre, hipStream_t st) {
   constexpr int U = BM == 64 ? 2 : 4;
   constexpr int RG = 4 / KS;
-  const dim3 grid(xcd_grid(mbs, (D + 32 * RG - 1) / (32 * RG)));
-  gemm2_kernel<BM, DT, U, OM, KS><<<grid, 256, 0, st>>>(
+  const dim3 grid(xcd_grid(mbs, (D + 16 * NG * RG - 1) / (16 * NG * RG)));
+  gemm2_kernel<BM, DT, U, OM, KS, NG><<<grid, 256, 0, st>>>(
       (const uint8_t*)a, a_scale, (const uint8_t*)w2, w2_scale, topk_w, sorted_ids, expert_ids,
       num_valid, T, E, k, D, I, mbs, y, pre);
 }
@@ -1192,6 +1195,12 @@ static void gemm2_ks(int ks, int mbs, const void* a, const void* a_scale, const 
     gemm2_go<BM, DT, OM, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
   else if (ks == 2)
     gemm2_go<BM, DT, OM, 2>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
+  else if (BM == 64 && DT != DT_FP4 && (DT == DT_BF16 ? 2 * I : I) <= 1024)
+    // rows of at most 1 KB without a K split (Kimi-K2.5's fp8 share: 512 bytes) leave each
+    // wave only a few chunks to stream: four 16-row groups per wave put twice the bytes in
+    // flight per wave (two waves per SIMD instead of three; gemm2 at Kimi fp8 T=64: 221 -> 191
+    // us).  mxfp4 would drop to one wave per SIMD and is slower with it.
+    gemm2_go<BM, DT, OM, 1, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
   else
     gemm2_go<BM, DT, OM, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
 }

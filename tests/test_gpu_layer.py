@@ -282,3 +282,22 @@ def test_layer_full_size_sampled(name, T, tokens, weights_cache):
         out2, _ = run_forward(inp, wl.topk, wl.block_m, wl.dtype, "atomic_bf16")
         compare_out_bf16_atomic(out2, ref.out, ref.contrib, rows, wl.topk,
                                 BF16_TOL if wl.dtype == "bf16" else FP8_TOL)
+
+
+@pytest.mark.parametrize("mode", ["reduce", "atomic"])
+def test_layer_short_rows_no_k_split(mode):
+    """Decode down projection with BLOCK_M 64, no K split (n_act * D/32 >= 256*16*12 waves) and
+    rows of at most 1 KB (bf16 I = 256): the kernel variant with four 16-row weight groups per
+    wave.  Sampled tokens against the oracle."""
+    T, E, k, D, I, B = 64, 256, 8, 7168, 256, 64
+    wl = synth.Workload("short_rows", E, k, D, I, B, "bf16", mode, 1.0, 0.02)
+    inp = synth.layer_inputs(wl, T, seed=11, device="cuda")
+    ref_route = oracle_route(inp["logits"], k, B)
+    # the library sizes the K split from min(T*k, E) experts (before routing is known)
+    assert min(T * k, E) * (D // 32) >= 256 * 16 * 12 and 2 * I <= 1024 and T * k < 32 * E
+    out, views = run_forward(inp, k, B, "bf16", mode)
+    tokens = [0, 31, 63]
+    ref = oracle_layer(inp, ref_route, "bf16", tokens=tokens)
+    compare_out(out, ref.out, np.array(tokens), BF16_TOL, BF16_COS)
+    del inp
+    torch.cuda.empty_cache()
