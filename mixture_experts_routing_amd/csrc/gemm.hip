@@ -1076,13 +1076,17 @@ hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16
 }
 
 // K-split choice: enough waves for ~12 rounds of the 256 CUs x 16 wave slots, since
-// every tile of a call does the same work and the last round runs part-empty.
-static int pick_ks(int64_t waves_ks1) {
+// every tile of a call does the same work and the last round runs part-empty, but no wave's
+// share of a row below 1 KB: shorter shares spend more of each wave on its start-up than on
+// streaming (mxfp4 gate-up at the Kimi-K2.5 shape, 3.5 KB rows: 258 us split four ways, 245
+// two ways, 242 unsplit; the GPT-OSS gate-up, 5.6 KB rows, is 3% faster four ways than two).
+static int pick_ks(int64_t waves_ks1, int rowb) {
   const int64_t target = 256LL * 16 * 12;
-  if (waves_ks1 >= target) return 1;
-  if (waves_ks1 * 2 >= target) return 2;
-  return 4;
+  int ks = waves_ks1 >= target ? 1 : waves_ks1 * 2 >= target ? 2 : 4;
+  while (ks > 1 && rowb / ks < 1024) ks >>= 1;
+  return ks;
 }
+static int row_bytes_of(int dt, int K) { return dt == DT_BF16 ? 2 * K : dt == DT_FP8 ? K : K / 2; }
 
 template <int BM, int DT, int KS>
 static void gemm1_go(const void* x, const void* x_scale, const void* w1, const void* w1_scale,
@@ -1152,7 +1156,7 @@ hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, con
     return requant(dt, a_bf16, T, k, I, a, a_scale, st);
   }
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
-  const int ks = pick_ks(n_act * (I / 16));  // a block covers 16*(4/ks) channels; I % 64 == 0
+  const int ks = pick_ks(n_act * (I / 16), row_bytes_of(dt, D));  // a block covers 16*(4/ks) channels; I % 64 == 0
 #define MOE_G1_DT(BMV, DTV) \
   gemm1_ks<BMV, DTV>(ks, x, x_scale, w1, w1_scale, sorted_ids, expert_ids, num_valid, mbs, T, E, k, D, I, a_bf16, zero_y, zero_n, pre, st)
 #define MOE_G1(BMV)                          \
@@ -1233,7 +1237,7 @@ hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, con
     return hipGetLastError();
   }
   const int64_t n_act = (int64_t)T * k < E ? (int64_t)T * k : E;
-  const int ks = pick_ks(n_act * (D / 32));  // ks >= 2 needs D % 64 == 0, which always holds
+  const int ks = pick_ks(n_act * (D / 32), row_bytes_of(dt, I));  // ks >= 2 needs D % 64 == 0, which always holds
 #define MOE_G2_OM(BMV, DTV, OMV) \
   gemm2_ks<BMV, DTV, OMV>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st)
 #define MOE_G2_DT(BMV, DTV)                                  \

@@ -95,6 +95,11 @@ SMALL_BF16 = [
     (640, 8, 4, 384, 512, 64),
     # long rows (2 KB) through the prefill kernels
     (256, 4, 2, 1024, 1088, 64),
+    # decode kernels with K split over the waves of a block (each wave's share of a row is
+    # kept at 1 KB or more): gate-up 4 ways (8 KB rows), down 4 ways, both 2 ways (3 KB rows)
+    (8, 8, 2, 4096, 64, 16),
+    (8, 8, 2, 128, 4096, 32),
+    (9, 8, 2, 1536, 1536, 16),
 ]
 # fp8: the intermediate is requantised per row from bf16 values that the GPU (fp32 MFMA
 # sums) and the oracle (fp64) may round one bf16 ulp apart; such a pair can land on
@@ -111,6 +116,8 @@ SMALL_FP8 = [
     (640, 8, 4, 384, 1024, 64),
     # long fp8 rows; 2112-byte rows end in a half 128-byte chunk
     (200, 4, 2, 2112, 2112, 64),
+    # decode gate-up with K split 4 ways (8 KB rows)
+    (8, 8, 2, 8192, 512, 16),
 ]
 # mxfp4: D and I multiples of 128; every BLOCK_M runs the decode kernels; D = 384 and
 # I = 640 end in a half 128-byte chunk (one of the two MFMAs of a chunk)
@@ -125,6 +132,9 @@ SMALL_MX = [
     (300, 8, 2, 512, 256, 64),
     (640, 8, 4, 256, 512, 64),
     (256, 4, 2, 1024, 768, 64),
+    # decode gate-up with K split 4 ways (4 KB rows of E2M1 codes) and 2 ways (2 KB rows)
+    (8, 8, 2, 8192, 256, 16),
+    (8, 8, 2, 4096, 256, 32),
 ]
 SMALL = ([(*c, "bf16") for c in SMALL_BF16] + [(*c, "fp8") for c in SMALL_FP8] +
          [(*c, "mxfp4") for c in SMALL_MX])
