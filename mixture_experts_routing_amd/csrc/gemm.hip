@@ -990,11 +990,15 @@ static bool use_prefill(int dt, int B, int64_t T, int k, int E, int64_t D, int64
 }
 
 // ----------------------------------------------------------------------------- combine
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// The combine kernels read each accumulator or slot row once and write each output once:
+// both go through non-temporal accesses, so they do not displace cached data.
 __global__ void __launch_bounds__(256) finalize_atomic_kernel(const float* __restrict__ y, int64_t n4,
                                                               uint16_t* __restrict__ out) {
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    const float4 v = reinterpret_cast<const float4*>(y)[i];
-    reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y) + i);
+    const u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(out) + i);
   }
 }
 
@@ -1006,15 +1010,25 @@ __global__ void __launch_bounds__(256) finalize_reduce_kernel(const float* __res
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
     const int64_t t = i / d4;
     const int c = (int)(i - t * d4);
-    float4 s = reinterpret_cast<const float4*>(y + (size_t)t * k * D)[c];
-    for (int j = 1; j < k; ++j) {
-      const float4 v = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * D)[c];
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+    // slots j = 0, 1, ... added in order; the loads of 8 slots are issued before their adds
+    const f32x4_t* row = reinterpret_cast<const f32x4_t*>(y + (size_t)t * k * D) + c;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) v[u] = __builtin_nontemporal_load(row + (size_t)(j0 + u) * (D / 4));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) {
+          s[0] += v[u][0];
+          s[1] += v[u][1];
+          s[2] += v[u][2];
+          s[3] += v[u][3];
+        }
     }
-    reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+    const u32x2_t o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(out) + i);
   }
 }
 
