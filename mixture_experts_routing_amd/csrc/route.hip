@@ -136,7 +136,9 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
                                     });
     wave_lds_sync();
   }
-  __threadfence();  // the fill stores complete before any slot is written over them
+  // the barrier's workgroup-scope release/acquire orders the fill stores before the slot
+  // stores written over them below (all of the workgroup's waves share one CU and its L2; a
+  // device-scope fence would also write back and invalidate the L2)
   __syncthreads();
 
   const int nv = block_prefix_scan(s_hist, s_cnt, s_off, s_wsum, E, B);
