@@ -135,10 +135,13 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
         f"{' preshuffled' if preshuffled else ''}: generating inputs")
     base = synth.layer_inputs(wl, 1, seed=0, device=dev)
     # the weights the GPU calls read (base keeps the natural layout for the CPU oracle)
-    gw = {key: base[key] for key in ("w1", "w2")}
+    gw = {key: base.get(key) for key in ("w1", "w2", "w1_scale", "w2_scale")}
     if preshuffled:
         for key in ("w1", "w2"):
             gw[key] = m.moe_preshuffle_weights(dtype, base[key])
+        if dtype == "mxfp4":  # the E8M0 block scales go into fragment order with their weights
+            for key in ("w1_scale", "w2_scale"):
+                gw[key] = m.moe_preshuffle_scales(base[key])
         torch.cuda.synchronize()
     pre = dict(preshuffled=True) if preshuffled else {}
     sets = []
@@ -154,8 +157,8 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
     def layer_call(i, st):
         s = sets[i % len(sets)]
         m.moe_forward(dtype, s["logits"], s["x"], gw["w1"], gw["w2"], k, B, mode,
-                      x_scale=s.get("x_scale"), w1_scale=base.get("w1_scale"),
-                      w2_scale=base.get("w2_scale"), workspace=ws, out=out, stream=st, **pre)
+                      x_scale=s.get("x_scale"), w1_scale=gw["w1_scale"],
+                      w2_scale=gw["w2_scale"], workspace=ws, out=out, stream=st, **pre)
 
     for i in range(warmup):
         layer_call(i, stream)
@@ -186,13 +189,13 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
     def gemm1_call(i, st):
         j = i % len(sets)
         m.moe_gemm1_gateup(dtype, sets[j]["x"], gw["w1"], routes[j], k, B, x_scale=sets[j].get("x_scale"),
-                           w1_scale=base.get("w1_scale"), a=a, a_scale=a_scale, workspace=g1ws, stream=st,
+                           w1_scale=gw["w1_scale"], a=a, a_scale=a_scale, workspace=g1ws, stream=st,
                            **pre)
 
     def gemm2_call(i, st):
         j = i % len(sets)
         m.moe_gemm2_down(dtype, a, gw["w2"], routes[j], T, k, B, mode, a_scale=a_scale,
-                         w2_scale=base.get("w2_scale"), y=y, stream=st, **pre)
+                         w2_scale=gw["w2_scale"], y=y, stream=st, **pre)
 
     def fin_call(i, st):
         m.moe_finalize(mode, y, T, k, D, out=out, stream=st)

@@ -61,9 +61,10 @@ enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1, MOE_OUT_ATOMIC_BF16 = 2 
 
 /* OR-ed into the dtype of moe_gemm1_gateup, moe_gemm2_down and moe_forward (and accepted,
  * and ignored, by the workspace-size functions): w1 and w2 are in fragment order, as written
- * by moe_preshuffle_weights.  Needs rows of whole 128-byte K chunks (fp8: D and I multiples
- * of 128; mxfp4: of 256), else MOE_EUNSUPPORTED.  Results are bit-identical to the natural
- * layout's. */
+ * by moe_preshuffle_weights, and for mxfp4 so are w1_scale and w2_scale, as written by
+ * moe_preshuffle_scales (fp8 per-row scales keep their layout).  Needs rows of whole
+ * 128-byte K chunks (fp8: D and I multiples of 128; mxfp4: of 256), else MOE_EUNSUPPORTED.
+ * Results are bit-identical to the natural layout's. */
 #define MOE_PRESHUFFLED 0x100
 
 /* Largest E accepted ([P3] "Hardening": the radix top-k path's 8160-expert bound). */
@@ -215,8 +216,8 @@ int moe_aux_loss_scores_backward(const float* logits, const float* grad_scores, 
  * group of 16 consecutive rows and each 128-byte chunk of K, 2 KB holding, for half h (0, 1)
  * and lane l = i + 16 g (i < 16, g < 4), the 16 bytes [128 c + 64 h + 16 g, + 16) of row
  * 16 R + i.  Each 1 KB is then what one wave's 16-byte load brings in for one operand
- * register, contiguous in memory.  Scales (fp8 per-row scales, mxfp4 E8M0 blocks) keep their
- * natural layout.
+ * register, contiguous in memory.  Scales are not touched: fp8 per-row scales keep their
+ * layout, mxfp4 E8M0 blocks go through moe_preshuffle_scales.
  *   w      [rows, K] in the dtype's storage (bf16: 2K bytes per row, fp8: K, mxfp4: K/2);
  *          an expert tensor [E, N, K] is rows = E*N
  *   w_out  the same size; must not overlap w
@@ -224,6 +225,18 @@ int moe_aux_loss_scores_backward(const float* logits, const float* grad_scores, 
  * (MOE_EUNSUPPORTED otherwise); dtype without flags. */
 int moe_preshuffle_weights(int dtype, const void* w, int64_t rows, int K, void* w_out,
                            void* stream);
+
+/* The E8M0 block scales of an mxfp4 weight tensor into fragment order, the companion of
+ * moe_preshuffle_weights for MOE_PRESHUFFLED mxfp4 calls ([P4] "Summary": a4w4 with one
+ * E8M0 scale per 32 elements along K; the same one-time layout change as for the weights).
+ * For each group of 16 consecutive rows and each 256-element chunk c of K (one 128-byte chunk
+ * of E2M1 codes), 128 bytes holding, for row i < 16, the 8 scale bytes [8 c, 8 c + 8) of row
+ * 16 R + i: the scales a wave reads for one chunk of 16 weight rows are one line.
+ *   s      uint8 [rows, K/32] (an expert tensor [E, N, K/32] is rows = E*N)
+ *   s_out  the same size; must not overlap s
+ * rows must be a multiple of 16 and K of 256 (MOE_EUNSUPPORTED otherwise); null or
+ * mis-aligned pointers, rows < 0 or K < 1 give MOE_EINVAL. */
+int moe_preshuffle_scales(const uint8_t* s, int64_t rows, int K, uint8_t* s_out, void* stream);
 
 /* ---------------------------------------------------------------- stage 1
  * [P2] gate-up helper and stage-1 commits ("silu(gate)*up with optional fp8

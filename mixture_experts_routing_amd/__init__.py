@@ -75,6 +75,7 @@ _SIGS = {
     "moe_aux_loss_scores": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_aux_loss_scores_backward": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "moe_preshuffle_weights": (_I, [_I, _P, _I64, _I, _P, _P]),
+    "moe_preshuffle_scales": (_I, [_P, _I64, _I, _P, _P]),
     "moe_gemm2_down": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_finalize": (_I, [_I, _P, _I, _I, _I, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P, _P]),
@@ -309,13 +310,25 @@ def moe_forward(dtype: str, logits, x, w1, w2, topk: int, block_m: int, mode: st
 
 def moe_preshuffle_weights(dtype: str, w, out=None, stream=None):
     """Weights [E, N, row storage] (bf16, or uint8 for fp8 / packed mxfp4) into fragment order,
-    same shape and dtype (scales are not touched)."""
+    same shape and dtype (scales are not touched; mxfp4 scales: moe_preshuffle_scales)."""
     rows = w.numel() // w.shape[-1]
     K = w.shape[-1] * 2 if dtype == "mxfp4" else w.shape[-1]
     if out is None:
         out = torch.empty_like(w)
     _check(load_library().moe_preshuffle_weights(DTYPE[dtype], _ptr(w), rows, K, _ptr(out), _stream(stream)),
            "moe_preshuffle_weights")
+    return out
+
+
+def moe_preshuffle_scales(s, out=None, stream=None):
+    """mxfp4 E8M0 weight scales uint8 [E, N, K/32] into fragment order (same shape), for calls
+    with preshuffled=True."""
+    rows = s.numel() // s.shape[-1]
+    K = s.shape[-1] * 32
+    if out is None:
+        out = torch.empty_like(s)
+    _check(load_library().moe_preshuffle_scales(_ptr(s), rows, K, _ptr(out), _stream(stream)),
+           "moe_preshuffle_scales")
     return out
 
 

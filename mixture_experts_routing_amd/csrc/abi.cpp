@@ -378,4 +378,12 @@ int moe_preshuffle_weights(int dtype, const void* w, int64_t rows, int K, void* 
   return launch_status(moe::launch_preshuffle(w, rows, (int)rb, w_out, (hipStream_t)stream));
 }
 
+int moe_preshuffle_scales(const uint8_t* s, int64_t rows, int K, uint8_t* s_out, void* stream) {
+  if (rows < 0 || K < 1) return MOE_EINVAL;
+  if (rows % 16 || K % 256) return MOE_EUNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!ok_ptr(s) || !ok_ptr(s_out) || s == s_out) return MOE_EINVAL;
+  return launch_status(moe::launch_preshuffle_scales(s, rows, K / 32, s_out, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -155,7 +155,8 @@ __device__ __forceinline__ void mfma_fp4(f32x4_t& acc, const i32x4_t (&a)[2], co
 // Weight rows: wrow[ng] already holds this lane's part of the address.  Natural layout
 // (PRE false): chunk kb of the lane's row at wrow + kb, its second half 64 bytes on.
 // Fragment-order layout (PRE true): the 16-row group's chunk kb at wrow + 16 kb, second half
-// 1024 bytes on (see preshuffle_kernel).
+// 1024 bytes on (see preshuffle_kernel); mxfp4 scales in fragment order too
+// (preshuffle_scales_kernel).
 template <int DT, int NG, int NT, int U, bool PRE>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
                                          const uint8_t* const (&xrow)[NT],
@@ -185,6 +186,12 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
     return make_uint2(lo, in1 ? *reinterpret_cast<const uint32_t*>(r + kb / 16 + 4) : 0x7F7F7F7Fu);
   };
   auto byte_g = [&](uint32_t w) { return (int)((w >> (8 * g)) & 0xFFu); };
+  // weight scales: in fragment order (PRE; wsc points at the lane's 8 bytes of the group's
+  // first chunk, whole chunks only) chunk kb's line is kb bytes on; else the natural rows
+  auto wscales = [&](const uint8_t* r, int kbb, bool in1) -> uint2 {
+    if constexpr (PRE) return *reinterpret_cast<const uint2*>(r + kbb);
+    return scales(r, kbb, in1);
+  };
   int kb = kb0;
   const int kend_full = kb1 < (kbytes & ~127) ? kb1 : (kbytes & ~127);
   for (; kb + 128 * U <= kend_full; kb += 128 * U) {
@@ -198,7 +205,7 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
       for (int ng = 0; ng < NG; ++ng) {
         wa[u][ng][0] = wld(wrow[ng] + woff);
         wa[u][ng][1] = wld(wrow[ng] + woff + whalf);
-        if constexpr (FP4) wsa[u][ng] = scales(wsc[ng], kb + 128 * u, true);
+        if constexpr (FP4) wsa[u][ng] = wscales(wsc[ng], kb + 128 * u, true);
       }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
@@ -234,7 +241,7 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&wrow)[NG],
     for (int ng = 0; ng < NG; ++ng) {
       wa[ng][0] = wld(wrow[ng] + woff);
       wa[ng][1] = in1 ? wld(wrow[ng] + woff + whalf) : zero;
-      if constexpr (FP4) wsa[ng] = scales(wsc[ng], kb, in1);
+      if constexpr (FP4) wsa[ng] = wscales(wsc[ng], kb, in1);
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
@@ -335,8 +342,10 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
   const uint8_t* wsc[2] = {nullptr, nullptr};
   if constexpr (FP4) {
     const uint8_t* ws8 = static_cast<const uint8_t*>(w1_scale_v);
-    wsc[0] = ws8 + ((size_t)e * 2 * I + n_w + i16) * rows_s;
-    wsc[1] = ws8 + ((size_t)e * 2 * I + I + n_w + i16) * rows_s;
+    // fragment order: group base (rows n_w, I + n_w are multiples of 16) + this row's 8 bytes
+    wsc[0] = pre ? ws8 + ((size_t)e * 2 * I + n_w) * rows_s + i16 * 8 : ws8 + ((size_t)e * 2 * I + n_w + i16) * rows_s;
+    wsc[1] = pre ? ws8 + ((size_t)e * 2 * I + I + n_w) * rows_s + i16 * 8
+                 : ws8 + ((size_t)e * 2 * I + I + n_w + i16) * rows_s;
   }
   const uint8_t* xrow[NT];
   const uint8_t* xsc[NT];
@@ -518,7 +527,8 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     wrow[q] = w2 + ((size_t)e * D + d_w + 16 * q) * rowb + lane_w;
     wsc[q] = nullptr;
     if constexpr (FP4)
-      wsc[q] = static_cast<const uint8_t*>(w2_scale_v) + ((size_t)e * D + d_w + 16 * q + i16) * rows_s;
+      wsc[q] = static_cast<const uint8_t*>(w2_scale_v) +
+               (pre ? ((size_t)e * D + d_w + 16 * q) * rows_s + i16 * 8 : ((size_t)e * D + d_w + 16 * q + i16) * rows_s);
   }
   const uint8_t* xrow[NT];
   const uint8_t* xsc[NT];
@@ -707,7 +717,9 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
         const int br = 32 * (j - 2 * NB) + r, wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
         const int ch = G1 ? p.nt * 128 + 32 * wg + 16 * (q & 1) + i : p.nt * 256 + br;
         const int row = G1 && q >= 2 ? N + ch : ch;
-        soff[x] = (uint32_t)((ch < N ? row : 0) * srow) + 4u * (lane & 1);
+        const int rr = ch < N ? row : 0;
+        // fragment order: [16-row group][chunk][row in group][8 bytes]; chunk c is 128 bytes on
+        soff[x] = (uint32_t)(p.pre ? (rr >> 4) * (srow >> 3) * 128 + (rr & 15) * 8 : rr * srow) + 4u * (lane & 1);
         sdst[x] = (uint32_t)(DATB + kPfRows * NB * 8 + 256 * (j - 2 * NB));
       }
     }
@@ -727,7 +739,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     for (int u = 0; u < 4; ++u) dma16_to_lds_s(wb, woff[u] + wlo, bo + TOKB + (wave + 8 * u) * 1024);
     if constexpr (FP4) {
       const uint8_t* sa = static_cast<const uint8_t*>(p.act_scale) + (size_t)c * 8;
-      const uint8_t* sw = wscale + (size_t)c * 8;
+      const uint8_t* sw = wscale + (size_t)c * (p.pre ? 128 : 8);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const bool tokrow = sdst[x] < (uint32_t)(DATB + kPfRows * NB * 8);
@@ -1057,6 +1069,23 @@ __global__ void __launch_bounds__(256) preshuffle_kernel(const uint8_t* __restri
   }
 }
 
+// E8M0 block scales of mxfp4 weights in fragment order: for each group of 16 consecutive rows
+// (nsb = K/32 scale bytes per row) and each 256-element chunk c, 128 bytes = [row i][8 bytes]
+// holding scale bytes [8 c, 8 c + 8) of row 16 R + i: the 8 bytes each lane of a decode wave
+// loads for its row of the chunk, all 16 rows in one line.  One 8-byte piece per thread.
+__global__ void __launch_bounds__(256) preshuffle_scales_kernel(const uint8_t* __restrict__ s, int64_t n8,
+                                                                int nsb, uint8_t* __restrict__ out) {
+  const int nch = nsb >> 3;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n8; t += (int64_t)gridDim.x * 256) {
+    const int i = (int)(t & 15);
+    const int64_t cr = t >> 4;  // R * nch + c
+    const int64_t R = cr / nch;
+    const int c = (int)(cr - R * nch);
+    const uint2 v = *reinterpret_cast<const uint2*>(s + (R * 16 + i) * nsb + c * 8);
+    *reinterpret_cast<uint2*>(out + t * 8) = v;
+  }
+}
+
 static int grid_1d(int64_t n, int cap_blocks = 4096) {
   int64_t b = (n + 255) / 256;
   if (b < 1) b = 1;
@@ -1067,6 +1096,14 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st) {
   const int64_t n4 = n / 4;  // callers pass multiples of 4 (D % 64 == 0)
   if (n4 == 0) return hipSuccess;
   zero_f32_kernel<<<grid_1d(n4), 256, 0, st>>>(reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_preshuffle_scales(const void* s, int64_t rows, int nsb, void* out, hipStream_t st) {
+  const int64_t n8 = rows * (nsb / 8);
+  if (n8 == 0) return hipSuccess;
+  preshuffle_scales_kernel<<<grid_1d(n8), 256, 0, st>>>(static_cast<const uint8_t*>(s), n8, nsb,
+                                                        static_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 

@@ -42,7 +42,8 @@ hipError_t launch_aux_scores_backward(const float* logits, const float* grad_sco
                                       int score, float* grad_logits, hipStream_t st);
 
 // pre: weights in fragment order (launch_preshuffle), which needs rows of whole 128-byte
-// chunks and 16-row groups.
+// chunks and 16-row groups; mxfp4 weight scales in fragment order too
+// (launch_preshuffle_scales).
 hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, const void* w1,
                         const void* w1_scale, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_valid, int64_t cap, int T,
@@ -65,5 +66,8 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
 
 // Weight rows (rows a multiple of 16, rowb a multiple of 128 bytes) into fragment order.
 hipError_t launch_preshuffle(const void* w, int64_t rows, int rowb, void* out, hipStream_t st);
+// mxfp4 E8M0 scale rows (rows a multiple of 16, nsb scale bytes per row, a multiple of 8) into
+// fragment order.
+hipError_t launch_preshuffle_scales(const void* s, int64_t rows, int nsb, void* out, hipStream_t st);
 
 }  // namespace moe

@@ -280,6 +280,18 @@ def test_preshuffle_validation(lib):
     assert lib.moe_gemm1_workspace_bytes(1 | PRE, 4, 2, 128) == lib.moe_gemm1_workspace_bytes(1, 4, 2, 128)
 
 
+def test_preshuffle_scales_validation(lib):
+    def pss(rows=32, K=256, s=GOOD, o=0x20000):
+        return lib.moe_preshuffle_scales(s, rows, K, o, None)
+
+    assert pss(rows=-16) == EINVAL and pss(K=0) == EINVAL
+    assert pss(rows=24) == EUNSUP                                 # not whole 16-row groups
+    assert pss(K=128) == EUNSUP and pss(K=288) == EUNSUP          # not whole 256-element chunks
+    assert pss(rows=0, s=None, o=None) == OK
+    assert pss(s=None) == EINVAL and pss(o=None) == EINVAL
+    assert pss(o=BAD_ALIGN) == EINVAL and pss(o=GOOD) == EINVAL   # s == out
+
+
 def test_strerror(lib):
     import mixture_experts_routing_amd as m
     texts = {m.moe_strerror(s) for s in (OK, EINVAL, ERANGE, ENOSPC, EUNSUP, ELAUNCH)}

@@ -1,4 +1,4 @@
-"""Weights in fragment order (moe_preshuffle_weights, MOE_PRESHUFFLED).
+"""Weights in fragment order (moe_preshuffle_weights, moe_preshuffle_scales, MOE_PRESHUFFLED).
 
 The layout is a byte permutation, checked against a numpy transposition of the rows.  The
 GEMMs read the same operand bytes in the same order either way, so gate-up outputs and
@@ -46,6 +46,35 @@ def test_preshuffle_is_the_documented_permutation(dtype, K):
     assert np.array_equal(got, want)
 
 
+def scale_fragment_order(raw: np.ndarray) -> np.ndarray:
+    """raw uint8 E8M0 scales [rows, K/32] -> bytes in the documented order [R][chunk][i][8]."""
+    rows, nsb = raw.shape
+    v = raw.reshape(rows // 16, 16, nsb // 8, 8)  # R, i, c, byte
+    return v.transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("K", [256, 768, 7168])
+def test_preshuffle_scales_is_the_documented_permutation(K):
+    import mixture_experts_routing_amd as m
+    g = torch.Generator().manual_seed(K)
+    raw = torch.randint(0, 256, (3, 32, K // 32), generator=g, dtype=torch.uint8)
+    out = m.moe_preshuffle_scales(raw.cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1)
+    want = scale_fragment_order(raw.numpy().reshape(96, -1))
+    assert np.array_equal(got, want)
+
+
+def pre_weights(m, dtype, g):
+    """w1, w2 in fragment order, and for mxfp4 their E8M0 scales too (fp8 scales unchanged)."""
+    out = {"w1": m.moe_preshuffle_weights(dtype, g["w1"]), "w2": m.moe_preshuffle_weights(dtype, g["w2"]),
+           "w1_scale": g.get("w1_scale"), "w2_scale": g.get("w2_scale")}
+    if dtype == "mxfp4":
+        out["w1_scale"] = m.moe_preshuffle_scales(g["w1_scale"])
+        out["w2_scale"] = m.moe_preshuffle_scales(g["w2_scale"])
+    return out
+
+
 def _ok(D, I, dtype):
     unit = {"bf16": 64, "fp8": 128, "mxfp4": 256}[dtype]
     return D % unit == 0 and I % unit == 0
@@ -67,19 +96,19 @@ def test_preshuffled_gemms_bit_identical(T, E, k, D, I, B, dtype):
     import mixture_experts_routing_amd as m
     assert _ok(D, I, dtype)
     g = to_cuda(synth.small_layer_inputs(T, E, k, D, I, dtype, seed=3))
-    w1p = m.moe_preshuffle_weights(dtype, g["w1"])
-    w2p = m.moe_preshuffle_weights(dtype, g["w2"])
+    pw = pre_weights(m, dtype, g)
     r = m.moe_topk_softmax_sort(g["logits"], k, B)
     kw1 = dict(x_scale=g.get("x_scale"), w1_scale=g.get("w1_scale"))
     a0, s0 = m.moe_gemm1_gateup(dtype, g["x"], g["w1"], r, k, B, **kw1)
-    a1, s1 = m.moe_gemm1_gateup(dtype, g["x"], w1p, r, k, B, preshuffled=True, **kw1)
+    a1, s1 = m.moe_gemm1_gateup(dtype, g["x"], pw["w1"], r, k, B, preshuffled=True, x_scale=g.get("x_scale"),
+                                w1_scale=pw["w1_scale"])
     torch.cuda.synchronize()
     assert torch.equal(a0, a1)
     if s0 is not None:
         assert torch.equal(s0, s1)
-    kw2 = dict(a_scale=s0, w2_scale=g.get("w2_scale"))
-    y0 = m.moe_gemm2_down(dtype, a0, g["w2"], r, T, k, B, "reduce", **kw2)
-    y1 = m.moe_gemm2_down(dtype, a0, w2p, r, T, k, B, "reduce", preshuffled=True, **kw2)
+    y0 = m.moe_gemm2_down(dtype, a0, g["w2"], r, T, k, B, "reduce", a_scale=s0, w2_scale=g.get("w2_scale"))
+    y1 = m.moe_gemm2_down(dtype, a0, pw["w2"], r, T, k, B, "reduce", preshuffled=True, a_scale=s0,
+                          w2_scale=pw["w2_scale"])
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
 
@@ -95,10 +124,9 @@ def test_preshuffled_forward_against_oracle(T, E, k, D, I, B, dtype, mode):
     # there; a rare pair of requant codes one step apart can exceed it on other draws)
     cpu = synth.small_layer_inputs(T, E, k, D, I, dtype, seed=T + D, w_std=0.05)
     g = to_cuda(cpu)
-    w1p = m.moe_preshuffle_weights(dtype, g["w1"])
-    w2p = m.moe_preshuffle_weights(dtype, g["w2"])
-    out, _, _ = m.moe_forward(dtype, g["logits"], g["x"], w1p, w2p, k, B, mode, x_scale=g.get("x_scale"),
-                              w1_scale=g.get("w1_scale"), w2_scale=g.get("w2_scale"), preshuffled=True)
+    pw = pre_weights(m, dtype, g)
+    out, _, _ = m.moe_forward(dtype, g["logits"], g["x"], pw["w1"], pw["w2"], k, B, mode, x_scale=g.get("x_scale"),
+                              w1_scale=pw["w1_scale"], w2_scale=pw["w2_scale"], preshuffled=True)
     torch.cuda.synchronize()
     ref = oracle_layer(cpu, oracle_route(cpu["logits"], k, B), dtype)
     tol = BF16_TOL if dtype == "bf16" else FP8_TOL
@@ -137,13 +165,12 @@ def test_preshuffled_full_size_sampled(name, T, tokens):
     g = synth.layer_inputs(wl, 1, seed=0, device="cuda")
     g["logits"] = synth.logits(T, wl.E, seed=T).cuda()
     g.update({kk: v.cuda() for kk, v in synth.activations(T, wl.D, wl.dtype, seed=T, x_std=wl.x_std).items()})
-    w1p = m.moe_preshuffle_weights(wl.dtype, g["w1"])
-    w2p = m.moe_preshuffle_weights(wl.dtype, g["w2"])
-    out, _, _ = m.moe_forward(wl.dtype, g["logits"], g["x"], w1p, w2p, wl.topk, wl.block_m, wl.mode,
-                              x_scale=g.get("x_scale"), w1_scale=g.get("w1_scale"),
-                              w2_scale=g.get("w2_scale"), preshuffled=True)
+    pw = pre_weights(m, wl.dtype, g)
+    out, _, _ = m.moe_forward(wl.dtype, g["logits"], g["x"], pw["w1"], pw["w2"], wl.topk, wl.block_m, wl.mode,
+                              x_scale=g.get("x_scale"), w1_scale=pw["w1_scale"],
+                              w2_scale=pw["w2_scale"], preshuffled=True)
     torch.cuda.synchronize()
-    del w1p, w2p
+    del pw
     ref = oracle_layer(g, oracle_route(g["logits"], wl.topk, wl.block_m), wl.dtype, tokens=tokens)
     if wl.dtype == "bf16":
         compare_out(out, ref.out, np.array(tokens), BF16_TOL, BF16_COS)
