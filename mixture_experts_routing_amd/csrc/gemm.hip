@@ -1228,12 +1228,12 @@ hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, con
   return requant(dt, a_bf16, T, k, I, a, a_scale, st);
 }
 
-template <int BM, int DT, int OM, int KS, int NG = 2>
+template <int BM, int DT, int OM, int KS, int NG = 2, int UU = 0>
 static void gemm2_go(int mbs, const void* a, const void* a_scale, const void* w2,
                      const void* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                      const int32_t* expert_ids, const int32_t* num_valid, int T, int E, int k,
                      int D, int I, void* y, int pre, hipStream_t st) {
-  constexpr int U = BM == 64 ? 2 : 4;
+  constexpr int U = UU ? UU : BM == 64 ? 2 : 4;
   constexpr int RG = 4 / KS;
   const dim3 grid(xcd_grid(mbs, (D + 16 * NG * RG - 1) / (16 * NG * RG)));
   gemm2_kernel<BM, DT, U, OM, KS, NG><<<grid, 256, 0, st>>>(
@@ -1254,8 +1254,12 @@ static void gemm2_ks(int ks, int mbs, const void* a, const void* a_scale, const 
     // rows of at most 1 KB without a K split (Kimi-K2.5's fp8 share: 512 bytes) leave each
     // wave only a few chunks to stream: four 16-row groups per wave put twice the bytes in
     // flight per wave (two waves per SIMD instead of three; gemm2 at Kimi fp8 T=64: 221 -> 191
-    // us).  mxfp4 would drop to one wave per SIMD and is slower with it.
+    // us).  mxfp4 with two chunks per iteration would drop to one wave per SIMD; with one
+    // chunk per iteration (rows of at most 512 bytes: Kimi's mxfp4 share has 256) it keeps two
+    // (gemm2 at Kimi mxfp4 T=64: 165 -> 138 us in fragment order).
     gemm2_go<BM, DT, OM, 1, 4>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
+  else if (BM == 64 && DT == DT_FP4 && I / 2 <= 512)
+    gemm2_go<BM, DT, OM, 1, 4, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
   else
     gemm2_go<BM, DT, OM, 1>(mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st);
 }
