@@ -16,7 +16,8 @@ stream it runs on), the CPU oracle's time on a bounded sample, and (unless
 with per-GEMM TFLOPS, the DeepSeek and Kimi layers again with packed bf16 atomics into
 the output, the Kimi shape in mxfp4 (a4w4), the Kimi prefill with the reduce-mode combine
 (per-slot rows summed by the finalize kernel) instead of atomics, the headline in the other
-weight layout and the other decode lines with the weights in fragment order, router-only GB/s at T=8192 (forward and
+weight layout, the DeepSeek shape at T=1 and T=4 and the other decode lines with the weights in
+fragment order, router-only GB/s at T=8192 (forward and
 backward), the group-limited router at the DeepSeek-V3 routing shape, and the auxiliary-loss
 scores forward and backward at T=8192.
 """
@@ -550,10 +551,11 @@ def main():
             secondary.append(r)
         # the headline with the other weight layout, and the decode lines in fragment order
         # (prepared once, outside the timed region)
-        for name, T, pre in ((args.workload, args.T, args.natural_weights), ("kimi", 64, True),
-                             ("kimi_mxfp4", 64, True), ("gptoss", 16, True)):
+        for name, T, pre in ((args.workload, args.T, args.natural_weights), ("deepseek", 1, True),
+                             ("deepseek", 4, True), ("kimi", 64, True), ("kimi_mxfp4", 64, True),
+                             ("gptoss", 16, True)):
             # input sets rotated as in the natural-layout line of the same workload
-            rot = args.rotate if name == args.workload else 2
+            rot = args.rotate if name == args.workload or name == "deepseek" else 2
             r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, rot, None,
                                   preshuffled=pre)
             del kp
