@@ -75,6 +75,12 @@ def _scores_f64(l: np.ndarray, score: str) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-l))
 
 
+def _sigmoid_slope(l: np.ndarray) -> np.ndarray:
+    """The sigmoid's derivative s (1 - s) = sigma(l) sigma(-l), float64."""
+    with np.errstate(over="ignore"):
+        return (1.0 / (1.0 + np.exp(-l))) * (1.0 / (1.0 + np.exp(l)))
+
+
 def routing_weights_f64(logits: np.ndarray, ids: np.ndarray, score: str = "softmax",
                         renorm: bool = True) -> np.ndarray:
     """The routed weights in float64, unrounded (see routing_weights)."""
@@ -100,7 +106,7 @@ def routing_weights(logits: np.ndarray, ids: np.ndarray, score: str = "softmax",
 
 
 def routing_weights_backward(logits: np.ndarray, ids: np.ndarray, grad_w: np.ndarray,
-                             score: str = "softmax", renorm: bool = True) -> np.ndarray:
+                             score: str = "softmax", renorm: bool = True, magnitude: bool = False):
     """Gradient of the routed weights with respect to the logits, float64 [T, E].
 
     "[Common] Optimize fused router forward/backward kernels" (TransformerEngine #3012),
@@ -112,6 +118,10 @@ def routing_weights_backward(logits: np.ndarray, ids: np.ndarray, grad_w: np.nda
     * sigmoid, renorm: w_j = s_j / sum_{i in S} s_i, dw_j/dl_m = s_m (1 - s_m) (d_jm - w_j) / sum s;
     * softmax over all E (no renorm): dw_j/dl_m = p_j (d_{e_j m} - p_m) for every expert m;
     * sigmoid (no renorm): dw_j/dl_m = s_j (1 - s_j) d_{e_j m}.
+    With magnitude=True also returns, per element, the same contraction with every Jacobian
+    entry's two parts (the Kronecker term and the coupling term) taken in absolute value and
+    |grad_w|: the size of the terms a finite-precision evaluation adds up, against which its
+    rounding is measured.
     """
     if score not in SCORES:
         raise ValueError(f"score must be one of {SCORES}")
@@ -121,7 +131,11 @@ def routing_weights_backward(logits: np.ndarray, ids: np.ndarray, grad_w: np.nda
     T, E = l.shape
     k = ids.shape[1]
     p = _scores_f64(l, score)
+    # sigmoid slope s (1 - s), written as sigma(l) sigma(-l): the same number without the
+    # cancellation of 1 - s, which is exactly 0 in float64 for logits above about 37
+    slope = _sigmoid_slope(l) if score == "sigmoid" else None
     out = np.zeros((T, E))
+    mag = np.zeros((T, E))
     for t in range(T):
         sel = p[t, ids[t]]
         if renorm:
@@ -132,17 +146,22 @@ def routing_weights_backward(logits: np.ndarray, ids: np.ndarray, grad_w: np.nda
                     d = 1.0 if mi == j else 0.0
                     if score == "softmax":
                         jac = w[j] * (d - w[mi])
+                        size = w[j] * (d + w[mi])
                     else:
-                        jac = sel[mi] * (1.0 - sel[mi]) * (d - w[j]) / sel.sum()
+                        jac = slope[t, m] * (d - w[j]) / sel.sum()
+                        size = slope[t, m] * (d + w[j]) / sel.sum()
                     out[t, m] += g[t, j] * jac
+                    mag[t, m] += abs(g[t, j]) * size
         else:
             for j in range(k):
                 e = ids[t, j]
                 if score == "softmax":
                     out[t] += g[t, j] * p[t, e] * ((np.arange(E) == e) - p[t])
+                    mag[t] += abs(g[t, j]) * p[t, e] * ((np.arange(E) == e) + p[t])
                 else:
-                    out[t, e] += g[t, j] * sel[j] * (1.0 - sel[j])
-    return out
+                    out[t, e] += g[t, j] * slope[t, e]
+                    mag[t, e] += abs(g[t, j]) * slope[t, e]
+    return (out, mag) if magnitude else out
 
 
 def sort_slots(ids: np.ndarray, E: int, block_m: int, cap: int | None = None):
@@ -321,14 +340,16 @@ def aux_loss_scores_f64(logits: np.ndarray, score: str = "softmax") -> np.ndarra
 
 
 def aux_loss_scores_backward(logits: np.ndarray, grad_scores: np.ndarray,
-                             score: str = "softmax") -> np.ndarray:
+                             score: str = "softmax", magnitude: bool = False):
     """Gradient of aux_loss_scores' scores with respect to the logits, float64 [T, E].
 
     Written as the Jacobian of the scores contracted with grad_scores, entry by entry:
     * softmax: dp_e/dl_c = p_e (d_ec - p_c);
     * normalised sigmoid, q_e = s_e / S with S = sum_i s_i:
       dq_e/dl_c = s_c (1 - s_c) (d_ec - q_e) / S.
-    The routing map is piecewise constant and passes no gradient.
+    The routing map is piecewise constant and passes no gradient.  With magnitude=True also
+    returns the contraction of |grad_scores| with the Jacobian whose two parts (Kronecker and
+    coupling term) are taken in absolute value, as in routing_weights_backward.
     """
     if score not in SCORES:
         raise ValueError(f"score must be one of {SCORES}")
@@ -336,15 +357,20 @@ def aux_loss_scores_backward(logits: np.ndarray, grad_scores: np.ndarray,
     g = np.asarray(grad_scores, dtype=np.float64)
     T, E = l.shape
     out = np.zeros((T, E))
+    mag = np.zeros((T, E))
     eye = np.eye(E)
     for t in range(T):
         if score == "softmax":
             p = _scores_f64(l[t:t + 1], "softmax")[0]
             jac = p[:, None] * (eye - p[None, :])          # [e, c]
+            size = p[:, None] * (eye + p[None, :])
         else:
             s = 1.0 / (1.0 + np.exp(-l[t]))
             S = s.sum()
             q = s / S
-            jac = (eye - q[:, None]) * (s * (1.0 - s))[None, :] / S
+            slope = _sigmoid_slope(l[t])  # s (1 - s) without cancellation
+            jac = (eye - q[:, None]) * slope[None, :] / S
+            size = (eye + q[:, None]) * slope[None, :] / S
         out[t] = g[t] @ jac
-    return out
+        mag[t] = np.abs(g[t]) @ size
+    return (out, mag) if magnitude else out

@@ -89,6 +89,26 @@ def route_call(lib, T=4, E=8, k=2, score=0, renorm=1, B=16, cap=None, ptrs=None,
                                      p["sorted"], cap, p["eids"], p["nv"], ws, ws_bytes, None)
 
 
+def test_forward_workspace_bytes(lib):
+    """moe_forward_workspace_bytes returns the layout's total, and 0 for invalid arguments."""
+    import mixture_experts_routing_amd as m
+    for dtype in ("bf16", "fp8", "mxfp4"):
+        for mode in ("atomic", "reduce", "atomic_bf16"):
+            for (T, E, k, D, I, B) in [(4, 8, 2, 128, 128, 16), (8192, 2304, 36, 128, 128, 32),
+                                       (16, 256, 8, 7168, 2048, 16), (0, 8, 2, 128, 128, 16)]:
+                total, _ = m.moe_forward_workspace_layout(dtype, mode, T, E, k, D, I, B)
+                got = lib.moe_forward_workspace_bytes(m.DTYPE[dtype], m.MODE[mode], T, E, k, D, I, B)
+                assert got == total > 0
+                assert m.moe_forward_workspace_bytes(dtype, mode, T, E, k, D, I, B) == total
+    # invalid: bad dtype, bad mode, topk > E, D not a multiple of 64, block_m 8, T*k*D past int32
+    for args in [(7, 0, 4, 8, 2, 128, 128, 16), (0, 9, 4, 8, 2, 128, 128, 16), (0, 0, 4, 8, 9, 128, 128, 16),
+                 (0, 0, 4, 8, 2, 100, 128, 16), (0, 0, 4, 8, 2, 128, 128, 8),
+                 (0, 0, 1 << 20, 8, 8, 1 << 10, 128, 16)]:
+        assert lib.moe_forward_workspace_bytes(*args) == 0, args
+    with pytest.raises(m.MoeError):
+        m.moe_forward_workspace_bytes("bf16", "atomic", 4, 8, 9, 128, 128, 16)
+
+
 def test_route_validation(lib):
     assert route_call(lib, k=0) == EINVAL
     assert route_call(lib, k=9) == EINVAL

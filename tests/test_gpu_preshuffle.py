@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from _gpu_helpers import BF16_COS, BF16_TOL, FP8_TOL, compare_out, oracle_route
+from _gpu_helpers import BF16_COS, BF16_TOL, FP8_TOL, compare_layer, compare_out_bf16_atomic, oracle_route
 from test_gpu_layer import oracle_layer, to_cuda
 
 pytestmark = pytest.mark.gpu
@@ -113,26 +113,35 @@ def test_preshuffled_gemms_bit_identical(T, E, k, D, I, B, dtype):
     assert torch.equal(y0, y1)
 
 
-@pytest.mark.parametrize("T,E,k,D,I,B,dtype,mode", [
+FWD = [
+    # (T, E, k, D, I, B, dtype, mode): decode and prefill kernels, every output mode; the fp8
+    # and mxfp4 shapes have I >= 512, where one requant code one step apart moves an output by
+    # about 0.2/sqrt(I) of its rms, well inside the 5e-2 bound
     (37, 16, 4, 384, 192, 16, "bf16", "atomic"), (640, 8, 4, 384, 512, 64, "bf16", "atomic"),
     (200, 40, 5, 256, 640, 64, "fp8", "atomic_bf16"), (640, 8, 4, 384, 1024, 64, "fp8", "reduce"),
-    (300, 8, 2, 512, 256, 64, "mxfp4", "atomic"),
-])
-def test_preshuffled_forward_against_oracle(T, E, k, D, I, B, dtype, mode):
+    (61, 12, 3, 512, 512, 32, "fp8", "atomic"), (300, 8, 2, 512, 512, 64, "mxfp4", "atomic"),
+    (37, 16, 4, 512, 512, 16, "mxfp4", "reduce"),
+]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("T,E,k,D,I,B,dtype,mode", FWD)
+def test_preshuffled_forward_against_oracle(T, E, k, D, I, B, dtype, mode, seed):
     import mixture_experts_routing_amd as m
-    # the inputs of the natural-layout layer tests for these shapes (fp8's 5e-2 bound is met
-    # there; a rare pair of requant codes one step apart can exceed it on other draws)
-    cpu = synth.small_layer_inputs(T, E, k, D, I, dtype, seed=T + D, w_std=0.05)
+    cpu = synth.small_layer_inputs(T, E, k, D, I, dtype, seed=1000 * seed + T + D, w_std=0.05)
     g = to_cuda(cpu)
     pw = pre_weights(m, dtype, g)
-    out, _, _ = m.moe_forward(dtype, g["logits"], g["x"], pw["w1"], pw["w2"], k, B, mode, x_scale=g.get("x_scale"),
-                              w1_scale=pw["w1_scale"], w2_scale=pw["w2_scale"], preshuffled=True)
+    out, ws, offs = m.moe_forward(dtype, g["logits"], g["x"], pw["w1"], pw["w2"], k, B, mode,
+                                  x_scale=g.get("x_scale"), w1_scale=pw["w1_scale"], w2_scale=pw["w2_scale"],
+                                  preshuffled=True)
     torch.cuda.synchronize()
     ref = oracle_layer(cpu, oracle_route(cpu["logits"], k, B), dtype)
     tol = BF16_TOL if dtype == "bf16" else FP8_TOL
     if mode == "atomic_bf16":
-        tol = 2 * tol  # bf16 rounding of each contribution and of each partial sum
-    compare_out(out, ref.out, np.arange(T), tol, BF16_COS if dtype == "bf16" and mode != "atomic_bf16" else None)
+        compare_out_bf16_atomic(out, ref.out, ref.contrib, np.arange(T), k, tol, out_allow=ref.out_allow)
+    else:
+        y = m.workspace_views(ws, offs, dtype, mode, T, E, k, D, I, B)["y"]
+        compare_layer(out, y, mode, k, ref, np.arange(T), tol, BF16_COS if dtype == "bf16" else None)
 
 
 def test_preshuffled_deepseek_decode_full_size():
@@ -150,31 +159,46 @@ def test_preshuffled_deepseek_decode_full_size():
     assert torch.equal(o0, o1)
 
 
+@pytest.fixture(scope="module")
+def pre_cache():
+    cache = {}
+    yield cache
+    cache.clear()
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,T,tokens", [
+    ("deepseek", 1, [0]),
+    ("deepseek", 2, [0, 1]),
+    ("deepseek", 4, [0, 1, 2, 3]),
+    ("deepseek", 8, [0, 3, 7]),
     ("deepseek", 16, [0, 9, 15]),
     ("gptoss", 16, [0, 7, 15]),
     ("kimi", 64, [0, 33, 63]),
     ("kimi_mxfp4", 64, [0, 33, 63]),
 ])
-def test_preshuffled_full_size_sampled(name, T, tokens):
+def test_preshuffled_full_size_sampled(name, T, tokens, pre_cache):
     """The decode workloads in the configuration the benchmark times them in: weights in
     fragment order (non-temporal weight loads), the workload's own output mode, moe_forward;
     sampled tokens against the oracle."""
     import mixture_experts_routing_amd as m
     wl = synth.WORKLOADS[name]
-    g = synth.layer_inputs(wl, 1, seed=0, device="cuda")
+    if pre_cache.get("name") != name:
+        pre_cache.clear()
+        torch.cuda.empty_cache()
+        base = synth.layer_inputs(wl, 1, seed=0, device="cuda")
+        pre_cache.update(name=name, base=base, pw=pre_weights(m, wl.dtype, base))
+    g = dict(pre_cache["base"])
+    pw = pre_cache["pw"]
     g["logits"] = synth.logits(T, wl.E, seed=T).cuda()
     g.update({kk: v.cuda() for kk, v in synth.activations(T, wl.D, wl.dtype, seed=T, x_std=wl.x_std).items()})
-    pw = pre_weights(m, wl.dtype, g)
-    out, _, _ = m.moe_forward(wl.dtype, g["logits"], g["x"], pw["w1"], pw["w2"], wl.topk, wl.block_m, wl.mode,
-                              x_scale=g.get("x_scale"), w1_scale=pw["w1_scale"],
-                              w2_scale=pw["w2_scale"], preshuffled=True)
+    out, ws, offs = m.moe_forward(wl.dtype, g["logits"], g["x"], pw["w1"], pw["w2"], wl.topk, wl.block_m,
+                                  wl.mode, x_scale=g.get("x_scale"), w1_scale=pw["w1_scale"],
+                                  w2_scale=pw["w2_scale"], preshuffled=True)
     torch.cuda.synchronize()
-    del pw
     ref = oracle_layer(g, oracle_route(g["logits"], wl.topk, wl.block_m), wl.dtype, tokens=tokens)
-    if wl.dtype == "bf16":
-        compare_out(out, ref.out, np.array(tokens), BF16_TOL, BF16_COS)
-    else:
-        compare_out(out, ref.out, np.array(tokens), FP8_TOL, None)
-    del g
-    torch.cuda.empty_cache()
+    y = m.workspace_views(ws, offs, wl.dtype, wl.mode, T, wl.E, wl.topk, wl.D, wl.I, wl.block_m)["y"]
+    tol, cos = (BF16_TOL, BF16_COS) if wl.dtype == "bf16" else (FP8_TOL, None)
+    ratio, c, allow = compare_layer(out, y, wl.mode, wl.topk, ref, np.array(tokens), tol, cos)
+    sys.stderr.write(f"[parity] {name} T={T} fragment order: max|err|/rms = {ratio:.4g}, cos {c:.7f}, "
+                     f"largest rounding-decision allowance {allow:.3g} rms\n")

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import synth
-from oracle import bf16_decode, e4m3_decode, moe_layer, route
+from oracle import bf16_decode, bf16_encode_rne, e4m3_decode, moe_layer, route
 from oracle.layer import requant_rows_fp8
 
 
@@ -212,3 +212,124 @@ def test_token_subset_reads_only_needed_experts():
     part = moe_layer(npi["x"], w1, w2, r.ids, r.weights, tokens=[2, 7])
     assert np.array_equal(part.out[[2, 7]], full.out[[2, 7]])
     assert np.isnan(part.out[0]).all()
+
+
+def test_slot_subset_matches_full():
+    """slots= evaluates exactly the listed slots: their contrib and intermediate rows equal the
+    full evaluation's, and no token output is formed."""
+    T, E, k, D, I = 10, 12, 3, 16, 8
+    npi = np_inputs(synth.small_layer_inputs(T, E, k, D, I, "fp8", seed=5))
+    r = route(npi["logits"], k, 16)
+    kw = dict(x_scale=npi["x_scale"], w1_scale=npi["w1_scale"], w2_scale=npi["w2_scale"])
+    full = moe_layer(npi["x"], npi["w1"], npi["w2"], r.ids, r.weights, "fp8", **kw)
+    sl = [1, 4, 17, 29]
+    part = moe_layer(npi["x"], npi["w1"], npi["w2"], r.ids, r.weights, "fp8", slots=sl, **kw)
+    # fp64 BLAS may block a product of fewer rows differently: equal to rounding
+    assert np.allclose(part.contrib[sl], full.contrib[sl], rtol=1e-12, atol=0)
+    assert np.array_equal(part.a_codes[sl], full.a_codes[sl])
+    assert np.array_equal(part.computed, np.isin(np.arange(T * k), sl))
+    assert np.isnan(part.out).all()
+    both = moe_layer(npi["x"], npi["w1"], npi["w2"], r.ids, r.weights, "fp8", tokens=[2], slots=[0], **kw)
+    assert np.allclose(both.out[2], full.out[2], rtol=1e-12, atol=0) and np.isnan(both.out[0]).all()
+    assert np.allclose(both.contrib[0], full.contrib[0], rtol=1e-12, atol=0)
+
+
+def test_a_cond_brute_force():
+    """a_cond against a pure-Python loop: the sums of |products| of the gate and up rows, with
+    silu's derivative taken by a central difference."""
+    T, E, k, D, I = 3, 4, 2, 8, 4
+    npi = np_inputs(synth.small_layer_inputs(T, E, k, D, I, "bf16", seed=9, w_std=0.3))
+    r = route(npi["logits"], k, 16)
+    res = moe_layer(npi["x"], npi["w1"], npi["w2"], r.ids, r.weights, cond=True)
+    x = bf16_decode(npi["x"])
+    silu = lambda z: z / (1.0 + math.exp(-z))  # noqa: E731
+    for t in range(T):
+        for j in range(k):
+            e = int(r.ids[t, j])
+            W = bf16_decode(npi["w1"][e])
+            for n in range(I):
+                g = sum(float(W[n, d]) * float(x[t, d]) for d in range(D))
+                u = sum(float(W[I + n, d]) * float(x[t, d]) for d in range(D))
+                ag = sum(abs(float(W[n, d]) * float(x[t, d])) for d in range(D))
+                au = sum(abs(float(W[I + n, d]) * float(x[t, d])) for d in range(D))
+                h = 1e-5
+                ds = (silu(g + h) - silu(g - h)) / (2 * h)
+                want = abs(ds * u) * ag + abs(silu(g)) * au
+                got = float(res.a_cond[t * k + j, n])
+                assert abs(got - want) <= 1e-5 * want + 1e-30, (t, j, n, got, want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp4"])
+def test_requant_spread_covers_every_alternative(dtype):
+    """Alternative implementations: each slot's silu(g)*u moved anywhere inside the band
+    (random points and both ends), rounded to bf16 and requantised by the same rule.  Their
+    bf16 rows lie in [a_lo, a_hi], their scales in [q_lo, q_hi], their dequantised rows within
+    a_spread of the oracle's, and their slot and token outputs within contrib_allow and
+    out_allow.  A wide band (2^-9, 2^-7) makes scale and exponent changes happen too."""
+    from oracle.layer import SILU_REL, requant_rows_fp8, requant_rows_mx
+    from oracle import mx_dequantize
+    T, E, k, D, I = 24, 3, 2, 64, 128
+    band_rel = {"bf16": 2.0 ** -9, "fp8": 2.0 ** -9, "mxfp4": 2.0 ** -7}[dtype]
+    npi = np_inputs(synth.small_layer_inputs(T, E, k, D, I, dtype, seed=17, w_std=0.3))
+    r = route(npi["logits"], k, 16)
+    kw = {} if dtype == "bf16" else dict(x_scale=npi["x_scale"], w1_scale=npi["w1_scale"],
+                                         w2_scale=npi["w2_scale"])
+    res = moe_layer(npi["x"], npi["w1"], npi["w2"], r.ids, r.weights, dtype, band_rel=band_rel, **kw)
+
+    def dec(w, sc, e):
+        if dtype == "bf16":
+            return bf16_decode(w[e])
+        if dtype == "fp8":
+            return e4m3_decode(w[e]) * sc[e][:, None].astype(np.float64)
+        from oracle import fp4_unpack
+        return mx_dequantize(fp4_unpack(w[e]), sc[e])
+
+    if dtype == "bf16":
+        xh = bf16_decode(npi["x"])
+    elif dtype == "fp8":
+        xh = e4m3_decode(npi["x"]) * npi["x_scale"][:, None].astype(np.float64)
+    else:
+        from oracle import fp4_unpack
+        xh = mx_dequantize(fp4_unpack(npi["x"]), npi["x_scale"])
+    flat = r.ids.reshape(-1)
+    v = np.zeros((T * k, I))
+    for s_ in range(T * k):
+        W1 = dec(npi["w1"], npi.get("w1_scale"), flat[s_])
+        gu = W1 @ xh[s_ // k]
+        g, u = gu[:I], gu[I:]
+        v[s_] = g / (1 + np.exp(-g)) * u
+    band = band_rel * res.a_cond.astype(np.float64) + SILU_REL * np.abs(v)
+    if dtype == "fp8":
+        ah_ref = requant_rows_fp8(res.a_bits)[2]
+    elif dtype == "mxfp4":
+        ah_ref = requant_rows_mx(res.a_bits)[2]
+    else:
+        ah_ref = bf16_decode(res.a_bits)
+    rng = np.random.default_rng(0)
+    var_seen = False
+    for trial in range(40):
+        f = {0: -1.0, 1: 1.0}.get(trial, None)
+        shift = f * band if f is not None else rng.uniform(-1, 1, band.shape) * band
+        alt_bits = bf16_encode_rne(v + shift)
+        alt = bf16_decode(alt_bits)
+        assert np.all(alt >= res.a_lo) and np.all(alt <= res.a_hi)
+        if dtype == "fp8":
+            _, sc, ah = requant_rows_fp8(alt_bits)
+            assert np.all(sc >= res.q_lo) and np.all(sc <= res.q_hi)
+        elif dtype == "mxfp4":
+            _, sc, ah = requant_rows_mx(alt_bits)
+            assert np.all(sc >= res.q_lo) and np.all(sc <= res.q_hi)
+        else:
+            ah = alt
+        assert np.all(np.abs(ah - ah_ref) <= res.a_spread.astype(np.float64) * (1 + 1e-6) + 1e-30)
+        out = np.zeros((T, D))
+        for s_ in range(T * k):
+            W2 = dec(npi["w2"], npi.get("w2_scale"), flat[s_])
+            c = float(r.weights.reshape(-1)[s_]) * (W2 @ ah[s_])
+            assert np.all(np.abs(c - res.contrib[s_]) <= res.contrib_allow[s_] * (1 + 1e-9) + 1e-12)
+            out[s_ // k] += c
+        assert np.all(np.abs(out - res.out) <= res.out_allow * (1 + 1e-9) + 1e-12)
+    if dtype != "bf16":
+        var_seen = bool(np.any(res.q_lo != res.q_hi))
+        assert var_seen, "the band never moved a scale: the wide-band branch went untested"
+    assert (res.a_spread > 0).any()

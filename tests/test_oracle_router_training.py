@@ -166,3 +166,20 @@ def test_aux_backward_special_cases():
     # softmax is shift-invariant, so each token's gradient sums to zero
     gr = aux_loss_scores_backward(l, rng.standard_normal((4, 12)), "softmax")
     assert np.allclose(gr.sum(axis=1), 0.0, atol=1e-15)
+
+
+def test_aux_backward_magnitude():
+    """The magnitude output: closed form for softmax, p_c (|g_c| + sum_e p_e |g_e|), on a
+    uniform row; |gradient| <= magnitude on random rows."""
+    E = 5
+    g = np.array([[1.0, -2.0, 0.5, 0.0, 3.0]])
+    out, mag = aux_loss_scores_backward(np.zeros((1, E)), g, "softmax", magnitude=True)
+    p = 1.0 / E
+    assert np.allclose(mag[0], p * (np.abs(g[0]) + p * np.abs(g[0]).sum()), rtol=1e-14, atol=0)
+    rng = np.random.default_rng(6)
+    l = rng.standard_normal((4, 9))
+    gr = rng.standard_normal((4, 9))
+    for score in ("softmax", "sigmoid"):
+        o, m_ = aux_loss_scores_backward(l, gr, score, magnitude=True)
+        assert np.array_equal(o, aux_loss_scores_backward(l, gr, score))
+        assert np.all(np.abs(o) <= m_ * (1 + 1e-12))

@@ -226,3 +226,35 @@ def test_backward_special_cases():
     np.put_along_axis(mask, ids3, True, axis=1)
     for score, renorm in (("softmax", True), ("sigmoid", True), ("sigmoid", False)):
         assert not routing_weights_backward(l, ids3, np.ones((4, 3)) * 0.7, score, renorm)[~mask].any()
+
+
+def test_backward_magnitude():
+    """The magnitude output: a hand-worked case (two picks, softmax renormalised: weights 3/4
+    and 1/4, gradient (1, -2)), and |gradient| <= magnitude on random data for every mode."""
+    l = np.array([[0.0, np.log(3.0)]])
+    ids = np.array([[1, 0]])
+    out, mag = routing_weights_backward(l, ids, np.array([[1.0, -2.0]]), "softmax", True, magnitude=True)
+    # (the logits pass through fp32, which moves ln 3 by about 1e-8)
+    assert np.allclose(out[0], [-0.5625, 0.5625], atol=0, rtol=1e-7)
+    assert np.allclose(mag[0], [0.8125, 1.6875], atol=0, rtol=1e-7)
+    rng = np.random.default_rng(5)
+    lr = rng.standard_normal((6, 20))
+    ids4 = select_topk(lr.astype(np.float32), 4)
+    gw = rng.standard_normal((6, 4))
+    for score in ("softmax", "sigmoid"):
+        for renorm in (True, False):
+            o, m_ = routing_weights_backward(lr, ids4, gw, score, renorm, magnitude=True)
+            assert np.array_equal(o, routing_weights_backward(lr, ids4, gw, score, renorm))
+            assert np.all(np.abs(o) <= m_ * (1 + 1e-12) + 1e-300)
+            assert np.all((m_ > 0) >= (o != 0))
+
+
+def test_sigmoid_backward_large_logits():
+    """The sigmoid's slope at large logits, where 1 - sigmoid(l) is 0 in float64: sigma(l)
+    sigma(-l) = e^{-l} / (1 + e^{-l})^2 (about 4.25e-18 at l = 40, 0 only past exp's range)."""
+    l = np.array([[40.0, -3.0, 90.0, 0.0]])
+    ids = np.array([[2, 0]])
+    out = routing_weights_backward(l, ids, np.array([[2.0, 0.5]]), "sigmoid", False)
+    assert np.isclose(out[0, 0], 0.5 * np.exp(-40.0) / (1 + np.exp(-40.0)) ** 2, rtol=1e-14, atol=0)
+    assert np.isclose(out[0, 2], 2.0 * np.exp(-90.0), rtol=1e-14, atol=0)
+    assert out[0, 1] == 0 and out[0, 3] == 0
