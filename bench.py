@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--natural-weights", action="store_true",
                     help="headline with the weights in their natural [E, N, K] layout instead of "
                          "fragment order (moe_preshuffle_weights, applied once before timing)")
+    ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
+                    help="file for the full per-line results (the stdout line carries the headline, "
+                         "its roofline, the CPU baseline and a summary); empty to skip")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -202,7 +205,10 @@ def measure_layer(env, wl, T, steps, warmup, rotate, mode=None, preshuffled=Fals
         m.moe_finalize(mode, y, T, k, D, out=out, stream=st)
 
     stage_ms = {}
-    for name, fn in (("route", route_call), ("gemm1", gemm1_call), ("gemm2", gemm2_call), ("finalize", fin_call)):
+    stages = [("route", route_call), ("gemm1", gemm1_call), ("gemm2", gemm2_call)]
+    if mode != "atomic_bf16":  # packed bf16 atomics: stage 2 wrote out, no combine launch
+        stages.append(("finalize", fin_call))
+    for name, fn in stages:
         stage_ms[name], _ = graph_ms_per_call(torch, fn, steps)
     acc = {"route": 0, "gemm1": 0, "gemm2": 0, "gemm1_flops": 0, "gemm2_flops": 0}
     n_acts = []
@@ -545,6 +551,11 @@ def main():
     peaks = achievable_peaks(torch, dev)
 
     secondary = []
+
+    def emit(r):
+        secondary.append(r)
+        log(brief(r))
+
     if not args.headline_only:
         for name, T, mode in (("gptoss", 16, None), ("gptoss", 4096, None), ("kimi", 64, None),
                               ("kimi", 4096, None), ("kimi", 16384, None), ("deepseek", 16, "atomic_bf16"),
@@ -555,11 +566,12 @@ def main():
             r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2, mode)
             del kp
             torch.cuda.empty_cache()
-            secondary.append(r)
+            emit(r)
         # the headline with the other weight layout, and the decode lines in fragment order
         # (prepared once, outside the timed region)
         for name, T, pre in ((args.workload, args.T, args.natural_weights), ("deepseek", 1, True),
-                             ("deepseek", 4, True), ("kimi", 64, True), ("kimi_mxfp4", 64, True),
+                             ("deepseek", 2, True), ("deepseek", 4, True), ("deepseek", 8, True), ("kimi", 64, True),
+                             ("kimi_mxfp4", 64, True),
                              ("gptoss", 16, True)):
             # input sets rotated as in the natural-layout line of the same workload
             rot = args.rotate if name == args.workload or name == "deepseek" else 2
@@ -567,18 +579,31 @@ def main():
                                   preshuffled=pre)
             del kp
             torch.cuda.empty_cache()
-            secondary.append(r)
+            emit(r)
         for (E, k) in synth.ROUTER_CASES:
             for score in ("softmax", "sigmoid"):
-                secondary.append(measure_router(env, E, k, score, args.steps, 3))
+                emit(measure_router(env, E, k, score, args.steps, 3))
         torch.cuda.empty_cache()
         for T, B in ((16, 16), (synth.ROUTER_T, synth.ROUTER_BLOCK_M)):
-            secondary.append(measure_router_grouped(env, T, 256, 8, 8, 4, "sigmoid", B, args.steps, 3))
+            emit(measure_router_grouped(env, T, 256, 8, 8, 4, "sigmoid", B, args.steps, 3))
         for (E, k) in synth.AUX_CASES:
             for score in ("softmax", "sigmoid"):
-                secondary.append(measure_aux(env, E, k, score, args.steps, 3))
+                emit(measure_aux(env, E, k, score, args.steps, 3))
         torch.cuda.empty_cache()
 
+    details = {"layer": head, "achievable_peaks": peaks, "secondary": secondary}
+    if args.details:
+        os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)
+        with open(args.details, "w") as f:
+            json.dump(details, f, indent=1)
+        log(f"full results written to {args.details}")
+    print(record_line(args, wl, head, roofline, cpu, secondary), flush=True)
+
+
+def record_line(args, wl, head, roofline, cpu, secondary):
+    """The one JSON line the run ends with (kept under 4000 characters): the headline, its
+    roofline, the CPU baseline, the headline's stage times and a summary of the secondary
+    lines.  The full per-line results go to the --details file."""
     res = {
         "metric": f"moe_layer_us_per_call_T{args.T}_decode" if args.workload == "deepseek"
         else f"moe_layer_us_per_call_{wl.name}_T{args.T}",
@@ -595,16 +620,57 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}-shaped MoE layer forward, T={args.T}", "T": args.T, "E": wl.E,
                    "topk": wl.topk, "D": wl.D, "I": wl.I, "block_m": wl.block_m, "mode": wl.mode,
-                   "score": "softmax", "renorm": True, "rotating_input_sets": args.rotate,
-                   "weights": head["weights"] + (" (moe_preshuffle_weights, once, before timing)"
-                                                 if not args.natural_weights else "")},
+                   "rotating_input_sets": args.rotate,
+                   "weights": "natural" if args.natural_weights else "fragment order (prepared once)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "layer": head,
-        "achievable_peaks": peaks,
-        "secondary": secondary,
+        "stage_us": head["stage_us"],
+        "layer_frac_of_hbm_floor": head["frac_of_layer_hbm_floor"],
+        "summary": summarize(secondary) if secondary else None,
     }
-    print(json.dumps(res))
+    line = json.dumps(res, separators=(",", ":"))
+    if len(line) > 4000:  # keep the record one short line: the summary goes first
+        res["summary"] = None
+        line = json.dumps(res, separators=(",", ":"))
+    return line
+
+
+def summarize(secondary):
+    """The other two parts of the metric, from the secondary lines: prefill GEMM TFLOPS with
+    their fraction of the dense MFMA peak (and of the binding floor), routing GB/s with their
+    fraction of HBM peak, and the other decode layer times (weights in fragment order)."""
+    import synth
+    out = {"prefill": {}, "router": {}, "decode": {}}
+    for r in secondary:
+        if "workload" in r:
+            default_mode = r["mode"] == synth.WORKLOADS[r["workload"]].mode
+            key = f"{r['workload']}_T{r['T']}" + ("" if default_mode else f"_{r['mode']}")
+            if r["T"] >= 1024:
+                g1, g2 = r["gemm"]["gemm1"], r["gemm"]["gemm2"]
+                out["prefill"][key] = {
+                    "us": r["us_per_call"],
+                    "gemm1": [g1["us"], g1["TFLOPS"], g1["mfma_frac"], g1["frac_of_binding_floor"]],
+                    "gemm2": [g2["us"], g2["TFLOPS"], g2["mfma_frac"], g2["frac_of_binding_floor"]]}
+            elif default_mode and r["weights"] == "fragment order":
+                out["decode"][key] = [r["us_per_call"], r["frac_of_layer_hbm_floor"]]
+        elif "router" in r:
+            out["router"][f"{r['router']}_{r['score']}"] = [r["us_per_call"], r["GB/s"], r["hbm_frac"]]
+    out["legend"] = {"prefill": "gemm1/gemm2: [us, TFLOPS, frac of dense MFMA peak, frac of binding floor]",
+                     "router": "[us, GB/s, frac of HBM peak], T=8192",
+                     "decode": "[us/call, frac of layer HBM floor]"}
+    return out
+
+
+def brief(r):
+    """One short line describing a secondary result (progress on stderr)."""
+    if "workload" in r:
+        return (f"{r['workload']} T={r['T']} {r['mode']} {r['weights']}: {r['us_per_call']} us "
+                f"(stages {r['stage_us']})")
+    if "router" in r:
+        return f"router {r['router']} {r['score']}: {r['us_per_call']} us, {r['GB/s']} GB/s"
+    if "router_grouped" in r:
+        return f"grouped router T={r['T']}: {r['grouped_us_per_call']} us"
+    return f"aux scores {r['aux_scores']} {r['score']}: fwd {r['forward']['us_per_call']} us"
 
 
 if __name__ == "__main__":

@@ -103,6 +103,12 @@ int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I);
 int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
                                      int block_m, int64_t* offsets);
 
+/* Total workspace bytes of moe_forward (the value moe_forward_workspace_layout returns), or 0
+ * when the arguments are invalid (a valid layout is never empty: every field takes at least
+ * 256 bytes); moe_forward_workspace_layout gives the status code of an invalid call. */
+size_t moe_forward_workspace_bytes(int dtype, int mode, int T, int E, int topk, int D, int I,
+                                   int block_m);
+
 /* Static description of a status code. */
 const char* moe_strerror(int status);
 

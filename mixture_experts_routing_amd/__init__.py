@@ -21,6 +21,7 @@ __all__ = [
     "moe_route_workspace_bytes",
     "moe_gemm1_workspace_bytes",
     "moe_forward_workspace_layout",
+    "moe_forward_workspace_bytes",
     "moe_strerror",
     "moe_topk_softmax_sort",
     "moe_gemm1_gateup",
@@ -66,6 +67,7 @@ _SIGS = {
     "moe_route_workspace_bytes": (_I64, [_I, _I, _I, _I]),
     "moe_gemm1_workspace_bytes": (_I64, [_I, _I, _I, _I]),
     "moe_forward_workspace_layout": (_I64, [_I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "moe_forward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "moe_strerror": (ctypes.c_char_p, [_I]),
     "moe_topk_softmax_sort": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "moe_gemm1_gateup": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
@@ -139,6 +141,15 @@ def moe_forward_workspace_layout(dtype: str, mode: str, T: int, E: int, topk: in
         DTYPE[dtype], MODE[mode], T, E, topk, D, I, block_m, ctypes.cast(offs, ctypes.c_void_p)),
         "moe_forward_workspace_layout")
     return total, {f: (None if offs[i] < 0 else offs[i]) for i, f in enumerate(WS_FIELDS)}
+
+
+def moe_forward_workspace_bytes(dtype: str, mode: str, T: int, E: int, topk: int, D: int, I: int,
+                                block_m: int) -> int:
+    """Total bytes of moe_forward's workspace; raises for invalid arguments (the C call returns 0)."""
+    n = load_library().moe_forward_workspace_bytes(DTYPE[dtype], MODE[mode], T, E, topk, D, I, block_m)
+    if n == 0:
+        moe_forward_workspace_layout(dtype, mode, T, E, topk, D, I, block_m)  # raises with the status
+    return n
 
 
 def _route_buffers(logits, topk, block_m, out, workspace):

@@ -145,6 +145,12 @@ int64_t moe_forward_workspace_layout(int dtype, int mode, int T, int E, int topk
   return L.total;
 }
 
+size_t moe_forward_workspace_bytes(int dtype, int mode, int T, int E, int topk, int D, int I,
+                                   int block_m) {
+  const int64_t total = moe_forward_workspace_layout(dtype, mode, T, E, topk, D, I, block_m, nullptr);
+  return total < 0 ? 0 : (size_t)total;
+}
+
 // [P3] "Hardening": topk a multiple of group_topk.  A selection over the kept groups needs
 // at least topk experts in them.
 static int check_groups(int E, int topk, int n_group, int topk_group) {

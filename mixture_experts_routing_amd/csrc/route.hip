@@ -369,9 +369,10 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(
     }
     wave_lds_sync();
   }
-  for (int e = chunk + nch * tid; e < E; e += nch * 1024) {
+  // 64-bit stride: nch * 1024 passes INT_MAX from T = 2^27 tokens on (E <= 15 allows such T)
+  for (int64_t e = chunk + (int64_t)nch * tid; e < E; e += (int64_t)nch * 1024) {
     const int c = tot[e];
-    if (c > 0) write_block_experts(e, s_goff[e >> 6] + loff[e], c, B, expert_ids);
+    if (c > 0) write_block_experts((int)e, s_goff[e >> 6] + loff[e], c, B, expert_ids);
   }
   const int nv = s_goff[128];
   if (chunk == 0 && tid == 0) *num_valid = nv;
