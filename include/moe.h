@@ -327,6 +327,27 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
                 const void* w2_scale, int T, int E, int topk, int D, int I, int block_m,
                 void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
 
+/* ---------------------------------------------------------------- no-allocation variant
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  moe_forward with the same arguments
+ * minus the workspace: the workspace lives in a static device array of
+ * moe_forward_noalloc_max_bytes() bytes (32 MiB) that every device the library runs on holds
+ * from module load until the process ends; the call allocates nothing.  The intermediates
+ * sit at the offsets moe_forward_workspace_layout reports, inside that array.
+ * Errors: those of moe_forward, and MOE_ENOSPC when moe_forward_workspace_bytes(...) exceeds
+ * the array (then nothing is enqueued; the DeepSeek-R1, GPT-OSS and Kimi-K2.5 decode shapes
+ * need at most about 3 MB); MOE_ELAUNCH if the array's device address cannot be obtained.
+ * Every call on one device uses that device's array: calls that overlap on one device (other
+ * streams, other threads) race and must be ordered by the caller.  The array keeps the last
+ * call's contents; every call rewrites what it reads. */
+int moe_forward_noalloc(int dtype, int score, int renorm, int mode, const float* logits,
+                        const void* x, const void* x_scale, const void* w1, const void* w1_scale,
+                        const void* w2, const void* w2_scale, int T, int E, int topk, int D, int I,
+                        int block_m, uint16_t* out, void* stream);
+
+/* Size in bytes of moe_forward_noalloc's static workspace. */
+int64_t moe_forward_noalloc_max_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,8 @@ __all__ = [
     "moe_aux_loss_scores_backward",
     "moe_preshuffle_weights",
     "moe_forward",
+    "moe_forward_noalloc",
+    "moe_forward_noalloc_max_bytes",
     "SCORE",
     "DTYPE",
     "MODE",
@@ -81,6 +83,8 @@ _SIGS = {
     "moe_gemm2_down": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_finalize": (_I, [_I, _P, _I, _I, _I, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P, _P]),
+    "moe_forward_noalloc": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_forward_noalloc_max_bytes": (_I64, []),
 }
 
 
@@ -317,6 +321,27 @@ def moe_forward(dtype: str, logits, x, w1, w2, topk: int, block_m: int, mode: st
         _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), T, E, topk, D, I, block_m, _ptr(workspace),
         workspace.numel(), _ptr(out), _stream(stream)), "moe_forward")
     return out, workspace, offs
+
+
+def moe_forward_noalloc(dtype: str, logits, x, w1, w2, topk: int, block_m: int, out, mode: str = "atomic",
+                        score: str = "softmax", renorm: bool = True, x_scale=None, w1_scale=None,
+                        w2_scale=None, stream=None, preshuffled: bool = False):
+    """moe_forward without a workspace argument (the library's static per-device array);
+    `out` bf16 [T, D] is the caller's.  Returns out."""
+    T, D = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    if dtype == "mxfp4":
+        D *= 2
+    _check(load_library().moe_forward_noalloc(
+        DTYPE[dtype] | (PRESHUFFLED if preshuffled else 0), SCORE[score], int(renorm), MODE[mode], _ptr(logits),
+        _ptr(x), _ptr(x_scale), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), T, E, topk, D, I, block_m,
+        _ptr(out), _stream(stream)), "moe_forward_noalloc")
+    return out
+
+
+def moe_forward_noalloc_max_bytes() -> int:
+    return load_library().moe_forward_noalloc_max_bytes()
 
 
 def moe_preshuffle_weights(dtype: str, w, out=None, stream=None):

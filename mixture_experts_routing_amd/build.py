@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "route_bwd.hip", "route_aux.hip", "gemm.hip", "abi.cpp"]
+SOURCES = ["route.hip", "route_bwd.hip", "route_aux.hip", "gemm.hip", "noalloc.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -320,10 +320,15 @@ int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out
   return launch_status(moe::launch_finalize(mode, y, T, topk, D, out, (hipStream_t)stream));
 }
 
-int moe_forward(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
-                const void* x_scale, const void* w1, const void* w1_scale, const void* w2,
-                const void* w2_scale, int T, int E, int topk, int D, int I, int block_m,
-                void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+}  // extern "C"
+
+// moe_forward's checks and launches; `workspace(total, &ws)` supplies the workspace once every
+// argument check has passed and returns MOE_OK or an error code.
+template <class GetWorkspace>
+static int forward_impl(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
+                        const void* x_scale, const void* w1, const void* w1_scale, const void* w2,
+                        const void* w2_scale, int T, int E, int topk, int D, int I, int block_m,
+                        GetWorkspace workspace, uint16_t* out, void* stream) {
   int pre;
   dtype = base_dtype(dtype, &pre);
   if (!ok_mode(mode)) return MOE_EINVAL;
@@ -333,14 +338,13 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   if (st) return st;
   if (pre && (row_bytes(dtype, D) % 128 || row_bytes(dtype, I) % 128)) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(w2) || !ok_ptr(out) ||
-      !ok_ptr(workspace))
-    return MOE_EINVAL;
+  if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(w2) || !ok_ptr(out)) return MOE_EINVAL;
   if (quantised(dtype) && (!ok_ptr(x_scale) || !ok_ptr(w1_scale) || !ok_ptr(w2_scale))) return MOE_EINVAL;
   const Layout L = forward_layout(dtype, mode, T, E, topk, D, I, block_m);
-  if ((int64_t)ws_bytes < L.total) return MOE_ENOSPC;
+  char* ws = nullptr;
+  st = workspace(L.total, &ws);
+  if (st) return st;
 
-  char* ws = static_cast<char*>(workspace);
   auto at = [&](int f) -> void* { return L.off[f] < 0 ? nullptr : ws + L.off[f]; };
   float* topk_w = static_cast<float*>(at(0));
   int32_t* topk_ids = static_cast<int32_t*>(at(1));
@@ -371,6 +375,39 @@ int moe_forward(int dtype, int score, int renorm, int mode, const float* logits,
   if (e == hipSuccess) e = moe::launch_finalize(mode, y, T, topk, D, out, s);
   return launch_status(e);
 }
+
+extern "C" {
+
+int moe_forward(int dtype, int score, int renorm, int mode, const float* logits, const void* x,
+                const void* x_scale, const void* w1, const void* w1_scale, const void* w2,
+                const void* w2_scale, int T, int E, int topk, int D, int I, int block_m,
+                void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+  auto caller_ws = [&](int64_t total, char** ws) -> int {
+    if (!ok_ptr(workspace)) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < total) return MOE_ENOSPC;
+    *ws = static_cast<char*>(workspace);
+    return MOE_OK;
+  };
+  return forward_impl(dtype, score, renorm, mode, logits, x, x_scale, w1, w1_scale, w2, w2_scale, T, E,
+                      topk, D, I, block_m, caller_ws, out, stream);
+}
+
+int moe_forward_noalloc(int dtype, int score, int renorm, int mode, const float* logits,
+                        const void* x, const void* x_scale, const void* w1, const void* w1_scale,
+                        const void* w2, const void* w2_scale, int T, int E, int topk, int D, int I,
+                        int block_m, uint16_t* out, void* stream) {
+  auto static_ws = [&](int64_t total, char** ws) -> int {
+    if (total > moe::kNoAllocScratchBytes) return MOE_ENOSPC;
+    void* p = nullptr;
+    if (moe::noalloc_scratch(&p) != hipSuccess) return MOE_ELAUNCH;
+    *ws = static_cast<char*>(p);
+    return MOE_OK;
+  };
+  return forward_impl(dtype, score, renorm, mode, logits, x, x_scale, w1, w1_scale, w2, w2_scale, T, E,
+                      topk, D, I, block_m, static_ws, out, stream);
+}
+
+int64_t moe_forward_noalloc_max_bytes(void) { return moe::kNoAllocScratchBytes; }
 
 int moe_preshuffle_weights(int dtype, const void* w, int64_t rows, int K, void* w_out,
                            void* stream) {

@@ -70,4 +70,9 @@ hipError_t launch_preshuffle(const void* w, int64_t rows, int rowb, void* out, h
 // fragment order.
 hipError_t launch_preshuffle_scales(const void* s, int64_t rows, int nsb, void* out, hipStream_t st);
 
+// moe_forward_noalloc: size of the static per-device workspace and its device address on the
+// current device (taken once per device with hipGetSymbolAddress).
+constexpr int64_t kNoAllocScratchBytes = 32LL << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace moe

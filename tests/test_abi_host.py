@@ -109,6 +109,28 @@ def test_forward_workspace_bytes(lib):
         m.moe_forward_workspace_bytes("bf16", "atomic", 4, 8, 9, 128, 128, 16)
 
 
+def test_forward_noalloc_host_checks(lib):
+    """moe_forward_noalloc: the static workspace size, and the errors returned before any HIP
+    call (a workspace need beyond the array gives MOE_ENOSPC; bad arguments as moe_forward)."""
+    import mixture_experts_routing_amd as m
+    assert lib.moe_forward_noalloc_max_bytes() == m.moe_forward_noalloc_max_bytes() == 32 << 20
+    P = GOOD
+
+    def call(dtype=0, mode=0, T=4, E=8, k=2, D=128, I=128, B=16, out=P, score=0, renorm=1):
+        return lib.moe_forward_noalloc(dtype, score, renorm, mode, P, P, P, P, P, P, P, T, E, k, D, I, B, out, None)
+
+    # the GPT-OSS prefill shape in reduce mode needs ~290 MB: rejected before any HIP call
+    assert m.moe_forward_workspace_bytes("bf16", "reduce", 4096, 128, 4, 2880, 2880, 64) > 32 << 20
+    assert call(0, 1, 4096, 128, 4, 2880, 2880, 64) == ENOSPC
+    assert call(mode=7) == EINVAL
+    assert call(score=5) == EINVAL
+    assert call(k=9) == EINVAL
+    assert call(D=100) == EUNSUP
+    assert call(out=BAD_ALIGN) == EINVAL
+    assert call(out=0) == EINVAL
+    assert call(T=0) == OK  # nothing to do
+
+
 def test_route_validation(lib):
     assert route_call(lib, k=0) == EINVAL
     assert route_call(lib, k=9) == EINVAL
