@@ -29,7 +29,16 @@
  *  - Alignment: tensors of 2-byte or wider elements and every fp8 tensor
  *    must be 16-byte aligned; otherwise MOE_EINVAL.
  *  - Calls on different streams may run concurrently if their output and
- *    workspace buffers are disjoint; the library keeps no global state.
+ *    workspace buffers are disjoint; the library keeps no global state (apart
+ *    from moe_forward_noalloc's static workspace, see there).
+ *  - Size limits of the layer calls: T*k*D and T*k*I below 2^31 (per-slot-row
+ *    offsets are 32-bit), else MOE_ERANGE; at the Kimi-K2.5 share (k=9, D=7168)
+ *    that is T <= 33288.  The LDS-tiled prefill GEMMs run when block_m = 64,
+ *    T*k >= 32*E, the bf16 intermediate rows span less than 2 GB
+ *    (T*k*max(D,I)*2 bytes) and one expert's W1 less than 2 GB (mxfp4 also
+ *    needs D and I multiples of 256); past those limits the decode kernels
+ *    (64-bit addressing) compute the same result, several times slower at
+ *    prefill sizes.
  *
  * Notation: T tokens, E experts, k = topk, D = model_dim, I = inter_dim,
  * B = block_m.  Slot s = t*k + j is token t's j-th ranked expert.  The
