@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary lines")
+    ap.add_argument("--lines", default="layers,decode,router,grouped,aux",
+                    help="secondary line groups to run (comma list of layers, decode, router, grouped, aux)")
     ap.add_argument("--natural-weights", action="store_true",
                     help="headline with the weights in their natural [E, N, K] layout instead of "
                          "fragment order (moe_preshuffle_weights, applied once before timing)")
@@ -556,7 +558,8 @@ def main():
         secondary.append(r)
         log(brief(r))
 
-    if not args.headline_only:
+    groups = set() if args.headline_only else set(args.lines.split(","))
+    if "layers" in groups:
         for name, T, mode in (("gptoss", 16, None), ("gptoss", 4096, None), ("kimi", 64, None),
                               ("kimi", 4096, None), ("kimi", 16384, None), ("deepseek", 16, "atomic_bf16"),
                               ("kimi", 4096, "atomic_bf16"), ("kimi", 16384, "atomic_bf16"),
@@ -567,6 +570,7 @@ def main():
             del kp
             torch.cuda.empty_cache()
             emit(r)
+    if "decode" in groups:
         # the headline with the other weight layout, and the decode lines in fragment order
         # (prepared once, outside the timed region)
         for name, T, pre in ((args.workload, args.T, args.natural_weights), ("deepseek", 1, True),
@@ -580,12 +584,15 @@ def main():
             del kp
             torch.cuda.empty_cache()
             emit(r)
+    if "router" in groups:
         for (E, k) in synth.ROUTER_CASES:
             for score in ("softmax", "sigmoid"):
                 emit(measure_router(env, E, k, score, args.steps, 3))
         torch.cuda.empty_cache()
+    if "grouped" in groups:
         for T, B in ((16, 16), (synth.ROUTER_T, synth.ROUTER_BLOCK_M)):
             emit(measure_router_grouped(env, T, 256, 8, 8, 4, "sigmoid", B, args.steps, 3))
+    if "aux" in groups:
         for (E, k) in synth.AUX_CASES:
             for score in ("softmax", "sigmoid"):
                 emit(measure_aux(env, E, k, score, args.steps, 3))
