@@ -34,8 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                                # MI355X HBM3E
-# fp32 atomic adds to HBM-resident memory, measured on MI355X with a plain atomic-add stream
-# (0.32-0.34 G adds/ms whatever the lane pattern or occupancy): the floor of atomic mode
+# fp32 atomic adds to HBM-resident memory on MI355X: torch's index_add_ reaches 0.28 G adds/ms
+# (--atomic-floor), this library's atomic combine 0.32 and a plain atomic-add stream 0.32-0.34
+# whatever the lane pattern or occupancy; the floor of atomic mode takes 0.33
 ATOMIC_ADDS_PER_S = 3.3e11
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}   # dense
 
@@ -58,6 +59,11 @@ def parse():
     ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
                     help="file for the full per-line results (the stdout line carries the headline, "
                          "its roofline, the CPU baseline and a summary); empty to skip")
+    ap.add_argument("--mode", default=None, choices=["atomic", "reduce", "atomic_bf16"],
+                    help="output mode of the headline layer (default: the workload's own)")
+    ap.add_argument("--atomic-floor", action="store_true",
+                    help="only measure the chip's fp32 atomic-add rate (a plain stream of atomic adds "
+                         "into a 470 MB buffer, torch's index_add_) and exit")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -427,6 +433,36 @@ def achievable_peaks(torch, dev):
     return res
 
 
+def atomic_floor(torch, dev):
+    """fp32 atomic adds per second into HBM-resident memory: torch's index_add_ adds a
+    [n, 7168] fp32 source into a [16384, 7168] destination (470 MB, the Kimi-K2.5 T=16384
+    accumulator) through rows chosen at random, one atomic add per element, timed over
+    graph-free eager launches.  Two lane patterns: whole rows (64 consecutive floats per
+    wave instruction) and the same adds with the destination rows in a random permutation."""
+    T, D = 16384, 7168
+    y = torch.zeros(T, D, device=dev)
+    n = 147456 // 4  # a quarter of the Kimi T=16384 slot rows per launch
+    src = torch.randn(n, D, device=dev)
+    res = {"destination_MB": round(T * D * 4 / 1e6, 1), "adds_per_launch": n * D}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for name, idx in (("rows_in_order", torch.arange(n, device=dev) % T),
+                      ("rows_random", torch.randint(0, T, (n,), device=dev, generator=g))):
+        for _ in range(3):
+            y.index_add_(0, idx, src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            y.index_add_(0, idx, src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms_per_launch": round(ms, 3), "G_adds_per_ms": round(n * D / ms / 1e9, 4)}
+    return res
+
+
 def kernel_source_sha256():
     """sha256 of the GEMM sources with comments and blank space removed, so that only code
     changes (which can change the kernels' traffic) invalidate stored counter readings."""
@@ -528,7 +564,10 @@ def main():
         del src, dst
 
     wl = synth.WORKLOADS[args.workload]
-    head, keep = measure_layer(env, wl, args.T, args.steps, args.warmup, args.rotate,
+    if args.atomic_floor:
+        print(json.dumps(atomic_floor(torch, dev)), flush=True)
+        return
+    head, keep = measure_layer(env, wl, args.T, args.steps, args.warmup, args.rotate, args.mode,
                                preshuffled=not args.natural_weights)
     g1 = head["gemm"]["gemm1"]
     g2 = head["gemm"]["gemm2"]
@@ -626,7 +665,7 @@ def record_line(args, wl, head, roofline, cpu, secondary):
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": f"{wl.name}-shaped MoE layer forward, T={args.T}", "T": args.T, "E": wl.E,
-                   "topk": wl.topk, "D": wl.D, "I": wl.I, "block_m": wl.block_m, "mode": wl.mode,
+                   "topk": wl.topk, "D": wl.D, "I": wl.I, "block_m": wl.block_m, "mode": head["mode"],
                    "rotating_input_sets": args.rotate,
                    "weights": "natural" if args.natural_weights else "fragment order (prepared once)"},
         "roofline": roofline,

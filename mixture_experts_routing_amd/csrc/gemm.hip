@@ -607,8 +607,9 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
 //  * stage 1 (gate-up): weight rows are the first MFMA operand, so a lane ends up with 4
 //    consecutive channels of one slot (gate and up pair in the same lane);
 //  * stage 2 (down): the operands are swapped, so a lane holds one model_dim channel of
-//    4 slots and 16 lanes cover 16 consecutive channels of one slot: each atomic (or
-//    store) instruction writes 64 contiguous bytes per row.
+//    4 slots and 16 lanes cover 16 consecutive channels of one slot: each atomic
+//    instruction adds into 64 contiguous bytes per row; the fp32 slot rows of the reduce
+//    mode are regrouped through LDS and stored 256 contiguous bytes per row.
 enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2, PF_G2_ATOMIC_BF16 = 3 };
 constexpr int kPfRows = 64;                          // rows of one sorted block
 constexpr int kPfMaxBlocks = 4;                      // sorted blocks per tile
@@ -913,6 +914,34 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
             atomic_add_bf16x2(out + (size_t)(s_b / p.k) * D + dch, odd ? rb : cv[1], odd ? cv[3] : rb);
         }
       }
+    } else if constexpr (MODE == PF_G2_REDUCE) {
+      // slot rows through LDS (the ring is free after the last chunk's barrier): each wave
+      // writes its 16 rows x 64 channels of group m, then lane l of store v takes channels
+      // 4 (l % 16) .. + 3 of row 4 v + l / 16, so each store covers 256 contiguous bytes of
+      // four rows (two full lines each) instead of 64 bytes of four rows.  Rows are padded to
+      // 68 floats: the 16 lanes i16 of each of the four rows g land in different banks.
+      float* y = reinterpret_cast<float*>(p.out);
+      float* stg = reinterpret_cast<float*>(ring + wave * (16 * 68 * 4));
+      const int j4 = lane & 15, rho0 = lane >> 4;
+#pragma unroll
+      for (int m = 0; m < MH; ++m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sc = s_fac[(2 * m + th) * 16 + 4 * g + r];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) stg[(4 * g + r) * 68 + 16 * q + i16] = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int rho = 4 * v + rho0;
+          const int s = s_slot[(2 * m + th) * 16 + rho];
+          const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&stg[rho * 68 + 4 * j4]);
+          if ((unsigned)s < (unsigned)n_slots)  // padding rows issue nothing
+            __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(y + (size_t)s * D + row0 + 4 * j4));
+        }
+        wave_lds_sync();  // the staging rows are rewritten for the next group
+      }
     } else {
       float* y = reinterpret_cast<float*>(p.out);
 #pragma unroll
@@ -922,13 +951,9 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
           const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
           if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
           const float sc = s_fac[(2 * m + th) * 16 + 4 * g + r];
-          float* dst = MODE == PF_G2_REDUCE ? y + (size_t)s * D + row0 + i16 : y + (size_t)(s / p.k) * D + row0 + i16;
+          float* dst = y + (size_t)(s / p.k) * D + row0 + i16;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float cv = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
-            if constexpr (MODE == PF_G2_REDUCE) dst[16 * q] = cv;
-            else atomicAdd(dst + 16 * q, cv);
-          }
+          for (int q = 0; q < 4; ++q) atomicAdd(dst + 16 * q, acc[q][m][r] * (FP8 ? sc * ws[q] : sc));
         }
       }
     }
