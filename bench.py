@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--atomic-floor", action="store_true",
                     help="only measure the chip's fp32 atomic-add rate (a plain stream of atomic adds "
                          "into a 470 MB buffer, torch's index_add_) and exit")
+    ap.add_argument("--sequence", default=None,
+                    help="only time these layer lines one after another in this process, weights in fragment "
+                         "order (comma list of workload:T[:rotating sets], e.g. kimi:64:2,deepseek:4:8,kimi:64:2), "
+                         "one JSON line each, and exit; a line's time can depend on what ran before it")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -566,6 +570,16 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if args.atomic_floor:
         print(json.dumps(atomic_floor(torch, dev)), flush=True)
+        return
+    if args.sequence:
+        for item in args.sequence.split(","):
+            name, T, *rot = item.split(":")
+            r, kp = measure_layer(env, synth.WORKLOADS[name], int(T), args.steps, args.warmup,
+                                  int(rot[0]) if rot else args.rotate, None, preshuffled=True)
+            del kp
+            torch.cuda.empty_cache()
+            print(json.dumps({"line": item, "us_per_call": r["us_per_call"], "stage_us": r["stage_us"],
+                              "stage_sum_us": round(sum(r["stage_us"].values()), 2)}), flush=True)
         return
     head, keep = measure_layer(env, wl, args.T, args.steps, args.warmup, args.rotate, args.mode,
                                preshuffled=not args.natural_weights)

@@ -623,13 +623,17 @@ struct PfArgs {
   const uint8_t* w;
   const void* w_scale;    // fp8: fp32 per row; mxfp4: E8M0 bytes [E, rows, K/32]
   const float* topk_w;
-  int T, k, N, K, e, nt;
+  int T, k, N, K, e;
+  int nt0, nt1;  // the run of channel tiles [nt0, nt1) this workgroup computes
   void* out;
   int pre;  // weights in fragment order (preshuffle_kernel)
   int wnt;  // the tile covers all of its expert's blocks: no other tile reads its weight chunks
 };
 
-// One tile of NB sorted blocks (64 NB slot rows) x the block's 256 weight rows, 8 waves.
+// One tile of NB sorted blocks (64 NB slot rows) x 256 weight rows, 8 waves, for each channel
+// tile of a run [nt0, nt1).  The chunks of the run's channel tiles form one stream through the
+// LDS ring: the first chunks of the next channel tile are in flight while the current one's
+// epilogue runs, and the slot ids, factors and slot-row offsets are set up once per run.
 // Wave w computes weight rows 64 (w % 4) .. + 63 against the slot-row groups tt with
 // tt % 2 == w / 4.  Both operands are staged by direct-to-LDS loads, one 128-byte K chunk
 // at a time, double buffered.  A load instruction fills 1 KB = 8 rows x 128 B; lane l takes
@@ -684,24 +688,24 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
   // Fragment-order weights: instruction jw = wave + 8 u copies half jw % 2 (1 KB, already in
   // MFMA lane order) of the chunk of block row group jw / 2 (rows 16 (jw / 2) .. + 15).
   uint32_t woff[4];
+  auto set_woff = [&](int nt) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jw = wave + 8 * u;
-    const int br = p.pre ? 16 * (jw >> 1) : 8 * jw + rsub;
-    const int wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
-    int row, ch;
-    if constexpr (G1) {
-      ch = p.nt * 128 + 32 * wg + 16 * (q & 1) + i;
-      row = (q >= 2 ? N : 0) + ch;
-    } else {
-      ch = p.nt * 256 + br;
-      row = ch;
+    for (int u = 0; u < 4; ++u) {
+      const int jw = wave + 8 * u;
+      const int br = p.pre ? 16 * (jw >> 1) : 8 * jw + rsub;
+      const int wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
+      int row, ch;
+      if constexpr (G1) {
+        ch = nt * 128 + 32 * wg + 16 * (q & 1) + i;
+        row = (q >= 2 ? N : 0) + ch;
+      } else {
+        ch = nt * 256 + br;
+        row = ch;
+      }
+      woff[u] = (uint32_t)((ch < N ? row : 0) * rowb);
+      if (p.pre) woff[u] += (uint32_t)(1024 * (jw & 1) + 16 * lane);
     }
-    woff[u] = (uint32_t)((ch < N ? row : 0) * rowb);
-    if (p.pre) woff[u] += (uint32_t)(1024 * (jw & 1) + 16 * lane);
-  }
-  const int row0 = G1 ? p.nt * 128 + wr * 32 : p.nt * 256 + wr * 64;
-  const bool on = row0 < N;
+  };
   const int nch = (rowb + 127) >> 7;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   // mxfp4 scale loads: instruction j < 2 NB covers slot rows 32 j .. + 31, the others weight
@@ -709,34 +713,36 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
   const int srow = p.K / 32;  // scale bytes per row
   uint32_t soff[2] = {0u, 0u}, sdst[2] = {0u, 0u};
   const uint8_t* wscale = nullptr;
-  if constexpr (FP4) {
-    wscale = static_cast<const uint8_t*>(p.w_scale) + (size_t)p.e * (G1 ? 2 * N : N) * srow;
+  auto set_soff = [&](int nt) {
+    if constexpr (FP4) {
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      int j = wave + 8 * x;
-      if (j >= 2 * NB + 8) j = wave;  // repeat the wave's first load
-      const int r = lane >> 1;
-      if (j < 2 * NB) {
-        const int s = s_slot[32 * j + r];
-        const bool ok = (unsigned)s < (unsigned)n_slots;
-        soff[x] = (uint32_t)((ok ? (G1 ? s / p.k : s) : 0) * srow) + 4u * (lane & 1);
-        sdst[x] = (uint32_t)(DATB + 256 * j);
-      } else {
-        const int br = 32 * (j - 2 * NB) + r, wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
-        const int ch = G1 ? p.nt * 128 + 32 * wg + 16 * (q & 1) + i : p.nt * 256 + br;
-        const int row = G1 && q >= 2 ? N + ch : ch;
-        const int rr = ch < N ? row : 0;
-        // fragment order: [16-row group][chunk][row in group][8 bytes]; chunk c is 128 bytes on
-        soff[x] = (uint32_t)(p.pre ? (rr >> 4) * (srow >> 3) * 128 + (rr & 15) * 8 : rr * srow) + 4u * (lane & 1);
-        sdst[x] = (uint32_t)(DATB + kPfRows * NB * 8 + 256 * (j - 2 * NB));
+      for (int x = 0; x < 2; ++x) {
+        int j = wave + 8 * x;
+        if (j >= 2 * NB + 8) j = wave;  // repeat the wave's first load
+        const int r = lane >> 1;
+        if (j < 2 * NB) {
+          const int s = s_slot[32 * j + r];
+          const bool ok = (unsigned)s < (unsigned)n_slots;
+          soff[x] = (uint32_t)((ok ? (G1 ? s / p.k : s) : 0) * srow) + 4u * (lane & 1);
+          sdst[x] = (uint32_t)(DATB + 256 * j);
+        } else {
+          const int br = 32 * (j - 2 * NB) + r, wg = br >> 6, q = (br >> 4) & 3, i = br & 15;
+          const int ch = G1 ? nt * 128 + 32 * wg + 16 * (q & 1) + i : nt * 256 + br;
+          const int row = G1 && q >= 2 ? N + ch : ch;
+          const int rr = ch < N ? row : 0;
+          // fragment order: [16-row group][chunk][row in group][8 bytes]; chunk c is 128 bytes on
+          soff[x] = (uint32_t)(p.pre ? (rr >> 4) * (srow >> 3) * 128 + (rr & 15) * 8 : rr * srow) + 4u * (lane & 1);
+          sdst[x] = (uint32_t)(DATB + kPfRows * NB * 8 + 256 * (j - 2 * NB));
+        }
       }
     }
-  }
-  // chunk c's loads into buffer c % NBUF.  In a half last chunk (fp8, K % 128 == 64) the
-  // lanes of the missing half read the present half again; their weight operand bytes are
-  // zeroed.
-  auto issue = [&](int c) {
-    const uint32_t bo = ring_lds + (uint32_t)((c % NBUF) * BUF);
+  };
+  if constexpr (FP4) wscale = static_cast<const uint8_t*>(p.w_scale) + (size_t)p.e * (G1 ? 2 * N : N) * srow;
+  // chunk c of the next channel tile to load into buffer b.  In a half last chunk (fp8,
+  // K % 128 == 64) the lanes of the missing half read the present half again; their weight
+  // operand bytes are zeroed.
+  auto issue = [&](int c, int b) {
+    const uint32_t bo = ring_lds + (uint32_t)(b * BUF);
     const uint32_t lo = (c * 128 + 64 >= rowb && ls >= 4) ? 16u * (ls & 3) : 16u * ls;
     const uint8_t* tb = p.act + (size_t)c * 128;
     const uint8_t* wb = wexp + (size_t)c * (p.pre ? 2048 : 128);
@@ -759,12 +765,6 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     }
   };
 
-  f32x4_t acc[4][MH];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int m = 0; m < MH; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   const int fsw = (i16 >> 1) & 7;  // read-side swizzle of row i16 of any 16-row group
   // weight fragment (q, h) of this lane, relative to the buffer's weight rows: natural rows
   // swizzled as the slot rows, or fragment order (group 4 wr + q, half h, 16 bytes per lane)
@@ -775,202 +775,246 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     for (int h = 0; h < 2; ++h)
       wofs[q][h] = p.pre ? ((4 * wr + q) * 2 + h) * 1024 + 16 * lane
                          : (64 * wr + 16 * q + i16) * 128 + 16 * ((4 * h + g) ^ fsw);
-  issue(0);
-  if (NBUF == 3 && nch > 1) issue(1);
-  if (NBUF == 3 && nch > 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int c = 0; c < nch; ++c) {
-    // buffer (c + NBUF - 1) % NBUF was last read in chunk c - 1, before the last barrier
-    const bool more = c + NBUF - 1 < nch;
-    if (more) issue(c + NBUF - 1);
-    const uint8_t* tb = ring + (c % NBUF) * BUF;
-    const uint8_t* wbuf = tb + TOKB;
-    // mxfp4: this lane's scale bytes (blocks g and 4 + g of the chunk) of its weight rows
-    int wsc0[4] = {127, 127, 127, 127}, wsc1[4] = {127, 127, 127, 127};
-    if constexpr (FP4) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint2 v = *reinterpret_cast<const uint2*>(tb + DATB + kPfRows * NB * 8 + (64 * wr + 16 * q + i16) * 8);
-        wsc0[q] = (int)((v.x >> (8 * g)) & 0xFFu);
-        wsc1[q] = (int)((v.y >> (8 * g)) & 0xFFu);
+  // the chunk stream: chunk ic of channel tile int_ is the next to load, into buffer ib
+  const int gtot = (p.nt1 - p.nt0) * nch;
+  int ic = 0, int_ = p.nt0, ib = 0;
+  auto issue_next = [&]() {
+    issue(ic, ib);
+    ib = ib + 1 == NBUF ? 0 : ib + 1;
+    if (++ic == nch) {
+      ic = 0;
+      if (++int_ < p.nt1) {
+        set_woff(int_);
+        set_soff(int_);
       }
     }
-    i32x4_t wf[4][2];
+  };
+  set_woff(p.nt0);
+  set_soff(p.nt0);
+  issue_next();
+  if (NBUF == 3 && gtot > 1) issue_next();
+  if (NBUF == 3 && gtot > 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  int cb = 0;  // buffer of the chunk being computed
+  for (int nt = p.nt0; nt < p.nt1; ++nt) {
+    f32x4_t acc[4][MH];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        wf[q][h] = *reinterpret_cast<const i32x4_t*>(&wbuf[wofs[q][h]]);
-    if (c * 128 + 64 >= rowb) {  // half last chunk
-      const i32x4_t zero = {0, 0, 0, 0};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wf[q][1] = zero;
-    }
-    // slot-row fragments: a ring of 4, read 3 groups ahead of the MFMAs that use them
-    i32x4_t tf[4][2];
-    int tsc0[4], tsc1[4];
-    auto rd = [&](int m) {
-      const int tt = 2 * m + th;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        tf[m & 3][h] = *reinterpret_cast<const i32x4_t*>(&tb[(tt * 16 + i16) * 128 + 16 * ((4 * h + g) ^ fsw)]);
+      for (int m = 0; m < MH; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint8_t* tb = ring;
+    for (int c = 0; c < nch; ++c) {
+      // the buffer of chunk gc + NBUF - 1 was last read in chunk gc - 1, before the last barrier
+      const int gc = (nt - p.nt0) * nch + c;
+      const bool more = gc + NBUF - 1 < gtot;
+      if (more) issue_next();
+      tb = ring + cb * BUF;
+      const uint8_t* wbuf = tb + TOKB;
+      // mxfp4: this lane's scale bytes (blocks g and 4 + g of the chunk) of its weight rows
+      int wsc0[4] = {127, 127, 127, 127}, wsc1[4] = {127, 127, 127, 127};
       if constexpr (FP4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(tb + DATB + (tt * 16 + i16) * 8);
-        tsc0[m & 3] = (int)((v.x >> (8 * g)) & 0xFFu);
-        tsc1[m & 3] = (int)((v.y >> (8 * g)) & 0xFFu);
-      }
-    };
-#pragma unroll
-    for (int m = 0; m < 3 && m < MH; ++m) rd(m);
-#pragma unroll
-    for (int m = 0; m < MH; ++m) {
-      if (m + 3 < MH) rd(m + 3);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (FP4) {
-          if constexpr (G1) mfma_fp4(acc[q][m], wf[q], tf[m & 3], wsc0[q], wsc1[q], tsc0[m & 3], tsc1[m & 3]);
-          else mfma_fp4(acc[q][m], tf[m & 3], wf[q], tsc0[m & 3], tsc1[m & 3], wsc0[q], wsc1[q]);
-        } else {
-          if constexpr (G1) mfma_chunk<FP8>(acc[q][m], wf[q], tf[m & 3]);
-          else mfma_chunk<FP8>(acc[q][m], tf[m & 3], wf[q]);
-        }
-      }
-    }
-    // chunk c + 1 has landed (only the loads issued in this chunk may still be in flight)
-    // and every wave is done with buffer c % NBUF
-    if (NBUF == 3 && more) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NDMA) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-  if (!on) return;
-
-  if constexpr (G1) {
-    // acc[q][m][r]: channel row0 + 16*(q&1) + 4g + r (q<2 gate, q>=2 up), slot column i16
-    // of group tt = 2 m + th
-    const int I = N;
-    uint16_t* a_out = reinterpret_cast<uint16_t*>(p.out);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n0 = row0 + 16 * h + 4 * g;
-      float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (FP8) {
-        const float* ws = static_cast<const float*>(p.w_scale) + (size_t)p.e * 2 * I;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sg[r] = ws[n0 + r];
-          su[r] = ws[I + n0 + r];
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MH; ++m) {
-        const int s = s_slot[(2 * m + th) * 16 + i16];
-        if ((unsigned)s >= (unsigned)n_slots) continue;
-        float xs = 1.f;
-        if constexpr (FP8) xs = s_fac[(2 * m + th) * 16 + i16];
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          v[r] = silu_mul(acc[h][m][r] * (sg[r] * xs), acc[2 + h][m][r] * (su[r] * xs));
-        uint2 pk;
-        pk.x = pack_bf16x2(v[0], v[1]);
-        pk.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(a_out + (size_t)s * I + n0) = pk;
-      }
-    }
-  } else {
-    // acc[q][m][r]: slot row (2 m + th)*16 + 4g + r, model_dim channel row0 + 16q + i16
-    const int D = N;
-    float ws[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (FP8) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ws[q] = static_cast<const float*>(p.w_scale)[(size_t)p.e * D + row0 + 16 * q + i16];
-    }
-    if constexpr (MODE == PF_G2_ATOMIC_BF16) {
-      // channel pairs (2c, 2c+1) sit in lanes i16 = 2c and 2c+1: the even lane adds the pairs
-      // of slot rows r = 0, 1, the odd lane those of r = 2, 3, after one exchange of two
-      // values between the two lanes
-      uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
-      const bool odd = (i16 & 1) != 0;
-#pragma unroll
-      for (int m = 0; m < MH; ++m) {
-        int sr[4];
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sr[r] = s_slot[(2 * m + th) * 16 + 4 * g + r];
-          sc[r] = s_fac[(2 * m + th) * 16 + 4 * g + r];
-        }
-        const int s_a = odd ? sr[2] : sr[0], s_b = odd ? sr[3] : sr[1];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float cv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) cv[r] = acc[q][m][r] * (FP8 ? sc[r] * ws[q] : sc[r]);
-          const float ra = __uint_as_float(xor_lane<1>(__float_as_uint(odd ? cv[0] : cv[2])));
-          const float rb = __uint_as_float(xor_lane<1>(__float_as_uint(odd ? cv[1] : cv[3])));
-          const int dch = row0 + 16 * q + (i16 & ~1);
-          if ((unsigned)s_a < (unsigned)n_slots)  // padding rows issue nothing
-            atomic_add_bf16x2(out + (size_t)(s_a / p.k) * D + dch, odd ? ra : cv[0], odd ? cv[2] : ra);
-          if ((unsigned)s_b < (unsigned)n_slots)
-            atomic_add_bf16x2(out + (size_t)(s_b / p.k) * D + dch, odd ? rb : cv[1], odd ? cv[3] : rb);
+          const uint2 v = *reinterpret_cast<const uint2*>(tb + DATB + kPfRows * NB * 8 + (64 * wr + 16 * q + i16) * 8);
+          wsc0[q] = (int)((v.x >> (8 * g)) & 0xFFu);
+          wsc1[q] = (int)((v.y >> (8 * g)) & 0xFFu);
         }
       }
-    } else if constexpr (MODE == PF_G2_REDUCE) {
-      // slot rows through LDS (the ring is free after the last chunk's barrier): each wave
-      // writes its 16 rows x 64 channels of group m, then lane l of store v takes channels
-      // 4 (l % 16) .. + 3 of row 4 v + l / 16, so each store covers 256 contiguous bytes of
-      // four rows (two full lines each) instead of 64 bytes of four rows.  Rows are padded to
-      // 68 floats: the 16 lanes i16 of each of the four rows g land in different banks.
-      float* y = reinterpret_cast<float*>(p.out);
-      float* stg = reinterpret_cast<float*>(ring + wave * (16 * 68 * 4));
-      const int j4 = lane & 15, rho0 = lane >> 4;
+      i32x4_t wf[4][2];
 #pragma unroll
-      for (int m = 0; m < MH; ++m) {
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float sc = s_fac[(2 * m + th) * 16 + 4 * g + r];
+        for (int h = 0; h < 2; ++h)
+          wf[q][h] = *reinterpret_cast<const i32x4_t*>(&wbuf[wofs[q][h]]);
+      if (c * 128 + 64 >= rowb) {  // half last chunk
+        const i32x4_t zero = {0, 0, 0, 0};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) stg[(4 * g + r) * 68 + 16 * q + i16] = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rho = 4 * v + rho0;
-          const int s = s_slot[(2 * m + th) * 16 + rho];
-          const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&stg[rho * 68 + 4 * j4]);
-          if ((unsigned)s < (unsigned)n_slots)  // padding rows issue nothing
-            __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(y + (size_t)s * D + row0 + 4 * j4));
-        }
-        wave_lds_sync();  // the staging rows are rewritten for the next group
+        for (int q = 0; q < 4; ++q) wf[q][1] = zero;
       }
-    } else {
-      float* y = reinterpret_cast<float*>(p.out);
+      // slot-row fragments: a ring of 4, read 3 groups ahead of the MFMAs that use them
+      i32x4_t tf[4][2];
+      int tsc0[4], tsc1[4];
+      auto rd = [&](int m) {
+        const int tt = 2 * m + th;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          tf[m & 3][h] = *reinterpret_cast<const i32x4_t*>(&tb[(tt * 16 + i16) * 128 + 16 * ((4 * h + g) ^ fsw)]);
+        if constexpr (FP4) {
+          const uint2 v = *reinterpret_cast<const uint2*>(tb + DATB + (tt * 16 + i16) * 8);
+          tsc0[m & 3] = (int)((v.x >> (8 * g)) & 0xFFu);
+          tsc1[m & 3] = (int)((v.y >> (8 * g)) & 0xFFu);
+        }
+      };
+#pragma unroll
+      for (int m = 0; m < 3 && m < MH; ++m) rd(m);
 #pragma unroll
       for (int m = 0; m < MH; ++m) {
+        if (m + 3 < MH) rd(m + 3);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
-          if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
-          const float sc = s_fac[(2 * m + th) * 16 + 4 * g + r];
-          float* dst = y + (size_t)(s / p.k) * D + row0 + i16;
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (FP4) {
+            if constexpr (G1) mfma_fp4(acc[q][m], wf[q], tf[m & 3], wsc0[q], wsc1[q], tsc0[m & 3], tsc1[m & 3]);
+            else mfma_fp4(acc[q][m], tf[m & 3], wf[q], tsc0[m & 3], tsc1[m & 3], wsc0[q], wsc1[q]);
+          } else {
+            if constexpr (G1) mfma_chunk<FP8>(acc[q][m], wf[q], tf[m & 3]);
+            else mfma_chunk<FP8>(acc[q][m], tf[m & 3], wf[q]);
+          }
+        }
+      }
+      cb = cb + 1 == NBUF ? 0 : cb + 1;
+      // chunk gc + 1 has landed (only the loads issued in this chunk may still be in flight)
+      // and every wave is done with this chunk's buffer; after a tile's last chunk the
+      // epilogue first runs while the next tile's first chunks load
+      if (c + 1 == nch) break;
+      if (NBUF == 3 && more) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    // the reduce epilogue stages slot rows through the last chunk's buffer, once every wave
+    // has read its fragments
+    if (MODE == PF_G2_REDUCE) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    uint8_t* const stage = tb;
+    const int row0 = G1 ? nt * 128 + wr * 32 : nt * 256 + wr * 64;
+    if (row0 < N) {
+      if constexpr (G1) {
+        // acc[q][m][r]: channel row0 + 16*(q&1) + 4g + r (q<2 gate, q>=2 up), slot column i16
+        // of group tt = 2 m + th
+        const int I = N;
+        uint16_t* a_out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) atomicAdd(dst + 16 * q, acc[q][m][r] * (FP8 ? sc * ws[q] : sc));
+        for (int h = 0; h < 2; ++h) {
+          const int n0 = row0 + 16 * h + 4 * g;
+          float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (FP8) {
+            const float* ws = static_cast<const float*>(p.w_scale) + (size_t)p.e * 2 * I;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              sg[r] = ws[n0 + r];
+              su[r] = ws[I + n0 + r];
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < MH; ++m) {
+            const int s = s_slot[(2 * m + th) * 16 + i16];
+            if ((unsigned)s >= (unsigned)n_slots) continue;
+            float xs = 1.f;
+            if constexpr (FP8) xs = s_fac[(2 * m + th) * 16 + i16];
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              v[r] = silu_mul(acc[h][m][r] * (sg[r] * xs), acc[2 + h][m][r] * (su[r] * xs));
+            uint2 pk;
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(a_out + (size_t)s * I + n0) = pk;
+          }
+        }
+      } else {
+        // acc[q][m][r]: slot row (2 m + th)*16 + 4g + r, model_dim channel row0 + 16q + i16
+        const int D = N;
+        float ws[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (FP8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ws[q] = static_cast<const float*>(p.w_scale)[(size_t)p.e * D + row0 + 16 * q + i16];
+        }
+        if constexpr (MODE == PF_G2_ATOMIC_BF16) {
+          // channel pairs (2c, 2c+1) sit in lanes i16 = 2c and 2c+1: the even lane adds the pairs
+          // of slot rows r = 0, 1, the odd lane those of r = 2, 3, after one exchange of two
+          // values between the two lanes
+          uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+          const bool odd = (i16 & 1) != 0;
+#pragma unroll
+          for (int m = 0; m < MH; ++m) {
+            int sr[4];
+            float sc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              sr[r] = s_slot[(2 * m + th) * 16 + 4 * g + r];
+              sc[r] = s_fac[(2 * m + th) * 16 + 4 * g + r];
+            }
+            const int s_a = odd ? sr[2] : sr[0], s_b = odd ? sr[3] : sr[1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float cv[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) cv[r] = acc[q][m][r] * (FP8 ? sc[r] * ws[q] : sc[r]);
+              const float ra = __uint_as_float(xor_lane<1>(__float_as_uint(odd ? cv[0] : cv[2])));
+              const float rb = __uint_as_float(xor_lane<1>(__float_as_uint(odd ? cv[1] : cv[3])));
+              const int dch = row0 + 16 * q + (i16 & ~1);
+              if ((unsigned)s_a < (unsigned)n_slots)  // padding rows issue nothing
+                atomic_add_bf16x2(out + (size_t)(s_a / p.k) * D + dch, odd ? ra : cv[0], odd ? cv[2] : ra);
+              if ((unsigned)s_b < (unsigned)n_slots)
+                atomic_add_bf16x2(out + (size_t)(s_b / p.k) * D + dch, odd ? rb : cv[1], odd ? cv[3] : rb);
+            }
+          }
+        } else if constexpr (MODE == PF_G2_REDUCE) {
+          // slot rows through LDS (a ring buffer no wave reads any more): each wave
+          // writes its 16 rows x 64 channels of group m, then lane l of store v takes channels
+          // 4 (l % 16) .. + 3 of row 4 v + l / 16, so each store covers 256 contiguous bytes of
+          // four rows (two full lines each) instead of 64 bytes of four rows.  Rows are padded to
+          // 68 floats: the 16 lanes i16 of each of the four rows g land in different banks.
+          float* y = reinterpret_cast<float*>(p.out);
+          float* stg = reinterpret_cast<float*>(stage + wave * (16 * 68 * 4));
+          const int j4 = lane & 15, rho0 = lane >> 4;
+#pragma unroll
+          for (int m = 0; m < MH; ++m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float sc = s_fac[(2 * m + th) * 16 + 4 * g + r];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) stg[(4 * g + r) * 68 + 16 * q + i16] = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int rho = 4 * v + rho0;
+              const int s = s_slot[(2 * m + th) * 16 + rho];
+              const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&stg[rho * 68 + 4 * j4]);
+              if ((unsigned)s < (unsigned)n_slots)  // padding rows issue nothing
+                __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(y + (size_t)s * D + row0 + 4 * j4));
+            }
+            wave_lds_sync();  // the staging rows are rewritten for the next group
+          }
+        } else {
+          float* y = reinterpret_cast<float*>(p.out);
+#pragma unroll
+          for (int m = 0; m < MH; ++m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int s = s_slot[(2 * m + th) * 16 + 4 * g + r];
+              if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue nothing
+              const float sc = s_fac[(2 * m + th) * 16 + 4 * g + r];
+              float* dst = y + (size_t)(s / p.k) * D + row0 + i16;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) atomicAdd(dst + 16 * q, acc[q][m][r] * (FP8 ? sc * ws[q] : sc));
+            }
+          }
         }
       }
     }
+    // only the reduce mode runs several channel tiles per workgroup (the host launches the
+    // others with one): their kernels keep a single pass, whose chunk loop the compiler does
+    // not see follow an epilogue with memory operations it counts as pending
+    if (MODE != PF_G2_REDUCE || nt + 1 == p.nt1) return;
+    // the next chunk has landed, the epilogue's loads and stores are done and no wave reads
+    // the staging.  A builtin wait, which the compiler sees: after an opaque one it would
+    // assume the epilogue's memory operations still pending and wait for every load in flight
+    // before each chunk's fragment reads.
+    __builtin_amdgcn_s_waitcnt(0x70);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
   }
 }
 
 // Block = 8 waves; tile = up to kPfMaxBlocks consecutive sorted blocks of one expert, counted
-// from the expert's first block (the workgroups of the tile's other blocks exit at once) x one
-// tile of 256 weight rows (gemm1: 128 gate and the matching 128 up channels; gemm2: 256
-// model_dim rows).
+// from the expert's first block (the workgroups of the tile's other blocks exit at once) x a run
+// of ntr consecutive tiles of 256 weight rows (gemm1: 128 gate and the matching 128 up
+// channels; gemm2: 256 model_dim rows).
 template <int DT, int MODE>
 __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
     const uint8_t* __restrict__ act, const void* __restrict__ act_scale,
     const uint8_t* __restrict__ w, const void* __restrict__ w_scale,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_valid, int T, int E,
-    int k, int N, int K, int mbs, void* __restrict__ out, float4* __restrict__ zero_y,
+    int k, int N, int K, int mbs, int ntr, void* __restrict__ out, float4* __restrict__ zero_y,
     int64_t zero_n4, int pre) {
   constexpr bool G1 = MODE == PF_G1;
   __shared__ __align__(16) uint8_t ring[kPfRingBytes];
@@ -980,8 +1024,9 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
     for (int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x; i < zero_n4; i += (int64_t)gridDim.x * 512)
       zero_y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int tile_n = G1 ? 128 : 256;
-  int mb, nt;
-  if (!block_tile_rows(mbs, (N + tile_n - 1) / tile_n, mb, nt)) return;
+  const int nts = (N + tile_n - 1) / tile_n;
+  int mb, ntg;
+  if (!block_tile_rows(mbs, (nts + ntr - 1) / ntr, mb, ntg)) return;
   const int nvb = *num_valid / kPfRows;  // sorted blocks holding slots
   if (mb >= nvb) return;
   const int e = expert_ids[mb];
@@ -1020,7 +1065,8 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
   // T=4096: gate-up 614 -> 603 us, down 946 -> 874 us); where two tiles share them, the second
   // one's hits would be lost (T=16384 gate-up: 1320 -> 1454 us)
   const int solo = before == 0 && (mb + nb >= nvb || expert_ids[mb + nb] != e);
-  const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt, out, pre, solo};
+  const int nt0 = ntg * ntr, nt1 = nt0 + ntr < nts ? nt0 + ntr : nts;
+  const PfArgs p{act, act_scale, w, w_scale, topk_w, T, k, N, K, e, nt0, nt1, out, pre, solo};
   switch (nb) {
     case 1: prefill_tile<DT, MODE, 1>(p, s_slot, s_fac, ring); break;
     case 2: prefill_tile<DT, MODE, 2>(p, s_slot, s_fac, ring); break;
@@ -1034,6 +1080,20 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
 // weights must each span less than 2 GB (larger shapes run the decode kernels, which
 // address in 64 bits).
 // mxfp4 needs K % 256 == 0 on both GEMMs (whole 8-byte scale groups per chunk).
+// Channel tiles per prefill workgroup.  In the reduce mode the epilogue of each tile (its
+// slot-row stores) then overlaps the loads of the next one's first chunks, which pays where K
+// is short and the stores are a large share of a tile: runs of up to 8 equal lengths for at
+// most 8 chunks of K (Kimi-K2.5 fp8 down projection, 4 chunks, 28 channel tiles: 1546 ->
+// 1285 us at T=16384 with runs of 7; runs of 4 1465 us, of 10 1534 us, of 14 1653 us), one
+// tile otherwise (GPT-OSS, 45 chunks: 538 us alone, 587 us in runs of 2).  The other modes
+// compute one channel tile per workgroup.
+static int prefill_ntr(int mode, int nts, int nch) {
+  if (mode != PF_G2_REDUCE || nch > 8) return 1;
+  for (int r = nts < 8 ? nts : 8; r > 1; --r)
+    if (nts % r == 0) return r;
+  return nts < 4 ? nts : 4;
+}
+
 static bool use_prefill(int dt, int B, int64_t T, int k, int E, int64_t D, int64_t I) {
   const int64_t kMax = (int64_t)1 << 31;
   if (dt == DT_FP4 && (D % 256 || I % 256)) return false;
@@ -1231,11 +1291,12 @@ hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, con
   uint16_t* a_bf16 = dt != DT_BF16 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
   const int mbs = (int)(cap / B);
   if (use_prefill(dt, B, T, k, E, D, I)) {
-    const dim3 grid(xcd_grid(mbs, (I + 127) / 128));
+    const int ntr = prefill_ntr(PF_G1, (I + 127) / 128, 0);
+    const dim3 grid(xcd_grid(mbs, ((I + 127) / 128 + ntr - 1) / ntr));
 #define MOE_PF1(DTV)                                                                                   \
   gemm_prefill_kernel<DTV, PF_G1><<<grid, 512, 0, st>>>((const uint8_t*)x, x_scale, (const uint8_t*)w1, \
                                                        w1_scale, nullptr, sorted_ids, expert_ids,       \
-                                                       num_valid, T, E, k, I, D, mbs, a_bf16,           \
+                                                       num_valid, T, E, k, I, D, mbs, ntr, a_bf16,      \
                                                        reinterpret_cast<float4*>(zero_y), zero_n / 4, pre)
     if (dt == DT_FP8)
       MOE_PF1(DT_FP8);
@@ -1313,11 +1374,13 @@ hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, con
   if (T == 0) return hipSuccess;
   const int mbs = (int)(cap / B);
   if (use_prefill(dt, B, T, k, E, D, I)) {
-    const dim3 grid(xcd_grid(mbs, (D + 255) / 256));
+    const int ntr = prefill_ntr(mode == OM_REDUCE ? PF_G2_REDUCE : PF_G2_ATOMIC, (D + 255) / 256,
+                                (row_bytes_of(dt, I) + 127) / 128);
+    const dim3 grid(xcd_grid(mbs, ((D + 255) / 256 + ntr - 1) / ntr));
 #define MOE_PF2(DTV, MD)                                                                                \
   gemm_prefill_kernel<DTV, MD><<<grid, 512, 0, st>>>((const uint8_t*)a, a_scale, (const uint8_t*)w2,    \
                                                     w2_scale, topk_w, sorted_ids, expert_ids, num_valid, \
-                                                    T, E, k, D, I, mbs, y, nullptr, 0, pre)
+                                                    T, E, k, D, I, mbs, ntr, y, nullptr, 0, pre)
 #define MOE_PF2_MODES(F8)                                   \
   if (mode == OM_REDUCE) MOE_PF2(F8, PF_G2_REDUCE);         \
   else if (mode == OM_ATOMIC) MOE_PF2(F8, PF_G2_ATOMIC);    \
