@@ -406,7 +406,10 @@ __global__ void __launch_bounds__(256) gemm1_kernel(
 }
 
 // fp8: per slot row, scale = amax/448 (1 for a zero row), codes = e4m3(a/scale).
-// One wave per row.
+// One wave per row; rows of at most 512 NQ values are read once into registers (8 values per
+// lane and 512-value group), so the conversion does not read the row again after the
+// amax reduction; longer rows (NQ = 0) read it twice.
+template <int NQ>
 __global__ void __launch_bounds__(256) requant_rows_kernel(const uint16_t* __restrict__ a_bf16,
                                                            int rows, int I,
                                                            uint8_t* __restrict__ a_codes,
@@ -415,18 +418,7 @@ __global__ void __launch_bounds__(256) requant_rows_kernel(const uint16_t* __res
   if (row >= rows) return;
   const int lane = lane_id();
   const uint16_t* src = a_bf16 + (size_t)row * I;
-  float amax = 0.f;
-  for (int c = lane * 8; c < I; c += 512) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[q] >> 16))));
-  }
-  amax = wave_max_f32(amax);
-  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-  for (int c = lane * 8; c < I; c += 512) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
+  auto convert = [&](const u32x4& v, int c, float scale) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t out[2];
 #pragma unroll
@@ -438,8 +430,37 @@ __global__ void __launch_bounds__(256) requant_rows_kernel(const uint16_t* __res
       out[q] = lo | (hi << 16);
     }
     *reinterpret_cast<uint2*>(a_codes + (size_t)row * I + c) = make_uint2(out[0], out[1]);
+  };
+  auto vmax = [](float m, const u32x4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[q] >> 16))));
+    return m;
+  };
+  float amax = 0.f;
+  if constexpr (NQ > 0) {
+    u32x4 v[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int c = lane * 8 + 512 * q;
+      v[q] = c < I ? *reinterpret_cast<const u32x4*>(src + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) amax = vmax(amax, v[q]);
+    amax = wave_max_f32(amax);
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (lane * 8 + 512 * q < I) convert(v[q], lane * 8 + 512 * q, scale);
+    if (lane == 0) a_scale[row] = scale;
+  } else {
+    for (int c = lane * 8; c < I; c += 512) amax = vmax(amax, *reinterpret_cast<const u32x4*>(src + c));
+    amax = wave_max_f32(amax);
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    for (int c = lane * 8; c < I; c += 512) convert(*reinterpret_cast<const u32x4*>(src + c), c, scale);
+    if (lane == 0) a_scale[row] = scale;
   }
-  if (lane == 0) a_scale[row] = scale;
 }
 
 // MXFP4: each block of 32 consecutive bf16 values of a slot row becomes one E8M0 scale
@@ -1272,8 +1293,13 @@ static hipError_t requant(int dt, const uint16_t* a_bf16, int T, int k, int I, v
                           hipStream_t st) {
   const int rows = T * k;
   if (dt == DT_FP8) {
-    requant_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>(a_bf16, rows, I, reinterpret_cast<uint8_t*>(a),
-                                                         static_cast<float*>(a_scale));
+    const unsigned g = (unsigned)((rows + 3) / 4);
+    uint8_t* codes = reinterpret_cast<uint8_t*>(a);
+    float* sc = static_cast<float*>(a_scale);
+    if (I <= 512) requant_rows_kernel<1><<<g, 256, 0, st>>>(a_bf16, rows, I, codes, sc);
+    else if (I <= 1024) requant_rows_kernel<2><<<g, 256, 0, st>>>(a_bf16, rows, I, codes, sc);
+    else if (I <= 2048) requant_rows_kernel<4><<<g, 256, 0, st>>>(a_bf16, rows, I, codes, sc);
+    else requant_rows_kernel<0><<<g, 256, 0, st>>>(a_bf16, rows, I, codes, sc);
   } else {
     const int64_t nblocks = (int64_t)rows * (I / 32);
     requant_mx_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, st>>>(
