@@ -28,6 +28,7 @@ import argparse
 import json
 import os
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -56,7 +57,7 @@ def parse():
     ap.add_argument("--natural-weights", action="store_true",
                     help="headline with the weights in their natural [E, N, K] layout instead of "
                          "fragment order (moe_preshuffle_weights, applied once before timing)")
-    ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
+    ap.add_argument("--details", default=os.path.join(tempfile.gettempdir(), "moe_bench_details.json"),
                     help="file for the full per-line results (the stdout line carries the headline, "
                          "its roofline, the CPU baseline and a summary); empty to skip")
     ap.add_argument("--mode", default=None, choices=["atomic", "reduce", "atomic_bf16"],
@@ -396,7 +397,7 @@ KERNEL_SOURCES = ("mixture_experts_routing_amd/csrc/gemm.hip", "mixture_experts_
 
 
 def achievable_peaks(torch, dev):
-    """What PyTorch's own kernels reach on this machine, reported beside the spec-sheet peaks as
+    """What PyTorch's own kernels reach on this GPU, reported beside the spec-sheet peaks as
     context (not as a ceiling: the layer's gemm1 streams faster than torch's sum reads): a
     streaming read (sum over 4 GiB), a device copy (1 GiB each way, both directions counted),
     and dense 8192^3 matmuls (bf16, and fp8 e4m3 with unit scales when torch supports it)."""
@@ -546,7 +547,7 @@ def cpu_baseline(env, wl, T, keep, n_calls=3):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no multi-GPU "
               "path", file=sys.stderr)
         sys.exit(2)
     import numpy as np
