@@ -34,11 +34,13 @@
  *  - Size limits of the layer calls: T*k*D and T*k*I below 2^31 (per-slot-row
  *    offsets are 32-bit), else MOE_ERANGE; at the Kimi-K2.5 share (k=9, D=7168)
  *    that is T <= 33288.  The LDS-tiled prefill GEMMs run when block_m = 64,
- *    T*k >= 32*E, the bf16 intermediate rows span less than 2 GB
- *    (T*k*max(D,I)*2 bytes) and one expert's W1 less than 2 GB (mxfp4 also
- *    needs D and I multiples of 256); past those limits the decode kernels
- *    (64-bit addressing) compute the same result, several times slower at
- *    prefill sizes.
+ *    T*k >= 32*E and the rows they gather and one expert's weights each span
+ *    less than 2 GB: T rows of D elements and 2*I rows of D for the gate-up,
+ *    T*k rows of I elements and D rows of I for the down projection, in bytes
+ *    of the dtype (mxfp4 also needs D and I multiples of 256).  Past those
+ *    limits the decode kernels (64-bit addressing) compute the same result,
+ *    several times slower at prefill sizes; at the Kimi-K2.5 share every T
+ *    the layer calls accept stays on the prefill GEMMs.
  *
  * Notation: T tokens, E experts, k = topk, D = model_dim, I = inter_dim,
  * B = block_m.  Slot s = t*k + j is token t's j-th ranked expert.  The

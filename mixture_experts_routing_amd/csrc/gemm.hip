@@ -1097,9 +1097,9 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
 }
 
 // The tiled kernel pays off once the experts carry several 64-row blocks on average.  Its
-// direct-to-LDS loads take 32-bit byte offsets: the activation rows and one expert's
-// weights must each span less than 2 GB (larger shapes run the decode kernels, which
-// address in 64 bits).
+// direct-to-LDS loads take 32-bit byte offsets: the rows it gathers (x for the gate-up, the
+// intermediate a for the down projection) and one expert's weights must each span less than
+// 2 GB (larger shapes run the decode kernels, which address in 64 bits).
 // mxfp4 needs K % 256 == 0 on both GEMMs (whole 8-byte scale groups per chunk).
 // Channel tiles per prefill workgroup.  In the reduce mode the epilogue of each tile (its
 // slot-row stores) then overlaps the loads of the next one's first chunks, which pays where K
@@ -1115,11 +1115,15 @@ static int prefill_ntr(int mode, int nts, int nch) {
   return nts < 4 ? nts : 4;
 }
 
-static bool use_prefill(int dt, int B, int64_t T, int k, int E, int64_t D, int64_t I) {
+static bool use_prefill(int stage, int dt, int B, int64_t T, int k, int E, int64_t D, int64_t I) {
   const int64_t kMax = (int64_t)1 << 31;
   if (dt == DT_FP4 && (D % 256 || I % 256)) return false;
-  return B == kPfRows && T * k >= 32LL * E && T * k * (D > I ? D : I) * 2 < kMax &&
-         2 * I * D * 2 < kMax;
+  if (B != kPfRows || T * k < 32LL * E) return false;
+  // the byte offsets of the gathered rows (token rows of x for the gate-up, slot rows of a
+  // for the down projection) and of one expert's weight rows
+  const int64_t rD = dt == DT_BF16 ? 2 * D : dt == DT_FP8 ? D : D / 2;
+  const int64_t rI = dt == DT_BF16 ? 2 * I : dt == DT_FP8 ? I : I / 2;
+  return stage == 1 ? T * rD < kMax && 2 * I * rD < kMax : T * k * rI < kMax && D * rI < kMax;
 }
 
 // ----------------------------------------------------------------------------- combine
@@ -1316,7 +1320,7 @@ hipError_t launch_gemm1(int dt, int pre, const void* x, const void* x_scale, con
   if (T == 0) return hipSuccess;
   uint16_t* a_bf16 = dt != DT_BF16 ? reinterpret_cast<uint16_t*>(ws) : reinterpret_cast<uint16_t*>(a);
   const int mbs = (int)(cap / B);
-  if (use_prefill(dt, B, T, k, E, D, I)) {
+  if (use_prefill(1, dt, B, T, k, E, D, I)) {
     const int ntr = prefill_ntr(PF_G1, (I + 127) / 128, 0);
     const dim3 grid(xcd_grid(mbs, ((I + 127) / 128 + ntr - 1) / ntr));
 #define MOE_PF1(DTV)                                                                                   \
@@ -1399,7 +1403,7 @@ hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, con
                         int E, int k, int D, int I, int B, int mode, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int mbs = (int)(cap / B);
-  if (use_prefill(dt, B, T, k, E, D, I)) {
+  if (use_prefill(2, dt, B, T, k, E, D, I)) {
     const int ntr = prefill_ntr(mode == OM_REDUCE ? PF_G2_REDUCE : PF_G2_ATOMIC, (D + 255) / 256,
                                 (row_bytes_of(dt, I) + 127) / 128);
     const dim3 grid(xcd_grid(mbs, ((D + 255) / 256 + ntr - 1) / ntr));

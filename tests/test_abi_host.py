@@ -185,6 +185,10 @@ def test_gemm1_validation(lib):
         assert gemm1_call(lib, dtype=1, ptrs={key: None}) == EINVAL
     assert gemm1_call(lib, dtype=1, ws_bytes=4 * 2 * 64 * 2 - 1) == ENOSPC
     assert gemm1_call(lib, T=70000, E=8, k=2, D=16384) == ERANGE  # T*k*D > INT_MAX
+    # the Kimi-K2.5 share (k=9, D=7168): T=33288 is the largest T with T*k*D < 2^31
+    kimi = dict(dtype=1, E=385, k=9, D=7168, I=512, B=64)
+    assert 33288 * 9 * 7168 < 2**31 <= 33289 * 9 * 7168
+    assert gemm1_call(lib, T=33289, **kimi) == ERANGE
 
 
 def gemm2_call(lib, dtype=0, mode=0, T=4, E=8, k=2, D=128, I=64, B=16, cap=None, ptrs=None):

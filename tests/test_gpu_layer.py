@@ -239,6 +239,9 @@ FULL = [
     ("kimi", 64, [0, 33, 63]),
     ("kimi", 4096, spread(4096)),
     ("kimi", 16384, spread(16384)),
+    # the largest T the layer calls accept at this shape (T*k*D < 2^31): the prefill GEMMs at
+    # their largest gathered-row offsets
+    ("kimi", 33288, spread(33288)),
     ("kimi_mxfp4", 64, [0, 33, 63]),
     ("kimi_mxfp4", 4096, spread(4096)),
     ("kimi_mxfp4", 16384, spread(16384)),
