@@ -4,8 +4,8 @@ Group-limited routing: ids, sort and expert ids bit-exact, weights rel <= 1e-6, 
 plain router.  The group decisions come from fp64 sums of at most 36 terms on both sides,
 which agree to about 1e-14 (relative); the test inputs are checked to hold no pair of groups
 whose scores agree to within 1e-12 without being exactly equal, so every decision is unique.  Auxiliary-loss scores: routing map bit-exact,
-scores rel <= 1e-6 (plus the smallest normal fp32, for underflow), backward
-max|err| <= 1e-5 * max|ref| per call."""
+scores rel <= 1e-6 (plus the smallest normal fp32, for underflow), backward element by element
+|err| <= 1e-5 * the magnitude of the terms the element adds up."""
 
 import sys
 
