@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--details", default=os.path.join(tempfile.gettempdir(), "moe_bench_details.json"),
                     help="file for the full per-line results (the stdout line carries the headline, "
                          "its roofline, the CPU baseline and a summary); empty to skip")
-    ap.add_argument("--mode", default=None, choices=["atomic", "reduce", "atomic_bf16"],
+    ap.add_argument("--mode", default=None, choices=["atomic", "reduce", "atomic_bf16", "reduce_bf16"],
                     help="output mode of the headline layer (default: the workload's own)")
     ap.add_argument("--atomic-floor", action="store_true",
                     help="only measure the chip's fp32 atomic-add rate (a plain stream of atomic adds "
@@ -619,7 +619,9 @@ def main():
                               ("kimi", 4096, "atomic_bf16"), ("kimi", 16384, "atomic_bf16"),
                               ("kimi_mxfp4", 64, None), ("kimi_mxfp4", 4096, None),
                               ("kimi_mxfp4", 16384, None), ("kimi", 4096, "reduce"),
-                              ("kimi", 16384, "reduce"), ("kimi_mxfp4", 16384, "reduce")):
+                              ("kimi", 16384, "reduce"), ("kimi_mxfp4", 16384, "reduce"),
+                              ("gptoss", 4096, "reduce_bf16"), ("kimi", 4096, "reduce_bf16"),
+                              ("kimi", 16384, "reduce_bf16"), ("kimi_mxfp4", 16384, "reduce_bf16")):
             r, kp = measure_layer(env, synth.WORKLOADS[name], T, max(5, args.steps // 2), 2, 2, mode)
             del kp
             torch.cuda.empty_cache()

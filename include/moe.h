@@ -68,7 +68,7 @@ enum moe_status {
 
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_dtype { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_MXFP4 = 2 };
-enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1, MOE_OUT_ATOMIC_BF16 = 2 };
+enum moe_mode { MOE_OUT_ATOMIC = 0, MOE_OUT_REDUCE = 1, MOE_OUT_ATOMIC_BF16 = 2, MOE_OUT_REDUCE_BF16 = 3 };
 
 /* OR-ed into the dtype of moe_gemm1_gateup, moe_gemm2_down and moe_forward (and accepted,
  * and ignored, by the workspace-size functions): w1 and w2 are in fragment order, as written
@@ -107,7 +107,8 @@ int64_t moe_gemm1_workspace_bytes(int dtype, int T, int topk, int I);
  *   6 a: bf16 [T*k,I], e4m3 [T*k,I] or packed mxfp4 [T*k,I/2]
  *   7 a_scale: fp32 [T*k] (fp8), E8M0 uint8 [T*k,I/32] (mxfp4)
  *   8 gemm1 scratch (fp8, mxfp4: bf16 [T*k,I])
- *   9 y: ATOMIC fp32 [T,D] accumulator, REDUCE fp32 [T*k,D] slot rows
+ *   9 y: ATOMIC fp32 [T,D] accumulator, REDUCE fp32 [T*k,D] slot rows,
+ *        REDUCE_BF16 bf16 [T*k,D] slot rows
  *        (ATOMIC_BF16: unused, -1; the stage-2 atomics add into out itself)
  * Returns the total size in bytes, or a negative moe_status. */
 #define MOE_WS_NFIELDS 10
@@ -293,20 +294,25 @@ int moe_gemm1_gateup(int dtype, const void* x, const void* x_scale, const void* 
  * [P2] stage-2 commit: down projection with per-token(row) x per-channel
  * (model_dim) fp8 dequant, the routed weight, and two epilogue modes:
  * atomic accumulation into out[token, model_dim], or a plain store of
- * out[token*topk + slot, model_dim] for a separate reduction.  Padding rows
- * issue no store and no atomic.
+ * out[token*topk + slot, model_dim] for a separate reduction, in fp32 or in the
+ * output's 16-bit type.  Padding rows issue no store and no atomic.
  *
  * For every real slot s = t*k + j in a block of expert e:
  *   c_s[d] = topk_weights[s] * sum_n W2[e, d, n] * a[s, n]
  *            (fp8: * a_scale[s] * w2_scale[e, d])
  *   ATOMIC:      y[t, d] += c_s[d]   (y fp32 [T, D]; the caller zeroes it first)
  *   REDUCE:      y[s, d]  = c_s[d]   (y fp32 [T*k, D])
+ *   REDUCE_BF16: y[s, d]  = bf16_rne(c_s[d])   (y bf16 [T*k, D]: half the bytes of REDUCE
+ *                to write here and to read in moe_finalize; each contribution moves by at
+ *                most 2^-8 * |c_s[d]|, half a bf16 step)
  *   ATOMIC_BF16: y[t, d] += c_s[d]   (y bf16 [T, D], zeroed by the caller; [P2] "atomic
  *                scatter into out": each c_s[d] is rounded to bf16 and added to the
  *                pair (d, d+1) with one packed bf16 atomic add, which rounds the running
  *                sum to bf16 again.  Half the atomic operations of ATOMIC; the result
  *                depends on the order of the k adds, and beyond ATOMIC's rounding it may
- *                differ from the exact sum by up to (k+1) * 2^-9 * sum_j |c_{t*k+j}[d]|.)
+ *                differ from the exact sum by up to about (k+1) * 2^-8 * sum_j |c_{t*k+j}[d]|:
+ *                k + 1 roundings to bf16, each of at most half a bf16 step, 2^-8 of a value
+ *                no larger in magnitude than that sum.)
  *
  *   mxfp4: the block scales of a and W2 enter the products; no per-row factors.
  *
@@ -324,9 +330,11 @@ int moe_gemm2_down(int dtype, const void* a, const void* a_scale, const void* w2
  * [P2] stage-2 commit and summary: the reduce mode's separate reduction kernel.
  * ATOMIC: out[t, d] = bf16_rne(y[t, d]), y fp32 [T, D].
  * REDUCE: out[t, d] = bf16_rne(sum_j y[t*k + j, d]) summed in fp32, j ascending.
+ * REDUCE_BF16: the same over the bf16 slot rows (each widened to fp32 exactly).
  * ATOMIC_BF16: nothing to do (stage 2 wrote the bf16 result); y and out are not used.
+ *   y   as written by moe_gemm2_down in the same mode (fp32, or bf16 for REDUCE_BF16)
  *   out bf16 [T, D] */
-int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out, void* stream);
+int moe_finalize(int mode, const void* y, int T, int topk, int D, uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------- whole layer
  * moe_topk_softmax_sort -> (ATOMIC: zero the accumulator; ATOMIC_BF16: zero out)

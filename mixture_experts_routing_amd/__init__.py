@@ -46,7 +46,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 SCORE = {"softmax": 0, "sigmoid": 1}
 DTYPE = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 PRESHUFFLED = 0x100  # dtype flag: weights in fragment order (moe_preshuffle_weights)
-MODE = {"atomic": 0, "reduce": 1, "atomic_bf16": 2}
+MODE = {"atomic": 0, "reduce": 1, "atomic_bf16": 2, "reduce_bf16": 3}
 WS_FIELDS = ("topk_weights", "topk_ids", "sorted_token_ids", "expert_ids", "num_valid",
              "route_scratch", "a", "a_scale", "gemm1_scratch", "y")
 
@@ -272,17 +272,14 @@ def moe_gemm1_gateup(dtype: str, x, w1, route: dict, topk: int, block_m: int, x_
 def moe_gemm2_down(dtype: str, a, w2, route: dict, T: int, topk: int, block_m: int, mode: str,
                    a_scale=None, w2_scale=None, y=None, stream=None, preshuffled: bool = False):
     """Stage 2: returns y (ATOMIC: fp32 [T, D] accumulated into; REDUCE: fp32 [T*k, D];
-    ATOMIC_BF16: bf16 [T, D] accumulated into)."""
+    ATOMIC_BF16: bf16 [T, D] accumulated into; REDUCE_BF16: bf16 [T*k, D])."""
     E, D, I = w2.shape
     if dtype == "mxfp4":
         I *= 2
     dev = a.device
     if y is None:
-        if mode == "atomic_bf16":
-            y = torch.zeros(T, D, dtype=torch.bfloat16, device=dev)
-        else:
-            rows = T if mode == "atomic" else T * topk
-            y = torch.zeros(rows, D, dtype=torch.float32, device=dev)
+        rows = T if mode in ("atomic", "atomic_bf16") else T * topk
+        y = torch.zeros(rows, D, dtype=torch.bfloat16 if mode.endswith("bf16") else torch.float32, device=dev)
     sid = route["sorted_token_ids"]
     _check(load_library().moe_gemm2_down(
         DTYPE[dtype] | (PRESHUFFLED if preshuffled else 0), _ptr(a), _ptr(a_scale), _ptr(w2), _ptr(w2_scale), _ptr(route["topk_weights"]),
@@ -292,7 +289,8 @@ def moe_gemm2_down(dtype: str, a, w2, route: dict, T: int, topk: int, block_m: i
 
 
 def moe_finalize(mode: str, y, T: int, topk: int, D: int, out=None, stream=None):
-    """Combine: bf16 out [T, D] from the fp32 accumulator or slot rows (ATOMIC_BF16: no-op)."""
+    """Combine: bf16 out [T, D] from the fp32 accumulator, the fp32 or bf16 slot rows
+    (ATOMIC_BF16: no-op)."""
     if out is None:
         out = torch.empty(T, D, dtype=torch.bfloat16, device=y.device)
     _check(load_library().moe_finalize(MODE[mode], _ptr(y), T, topk, D, _ptr(out), _stream(stream)),
@@ -394,5 +392,5 @@ def workspace_views(workspace, offs: dict, dtype: str, mode: str, T: int, E: int
         "a_pre": view("gemm1_scratch", n * I, torch.bfloat16, (n, I)),
     }
     rows = T if mode == "atomic" else n
-    v["y"] = view("y", rows * D, torch.float32, (rows, D))
+    v["y"] = view("y", rows * D, torch.bfloat16 if mode == "reduce_bf16" else torch.float32, (rows, D))
     return v

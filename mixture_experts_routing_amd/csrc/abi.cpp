@@ -55,7 +55,8 @@ int check_layer_dims(int dtype, int T, int E, int topk, int D, int I, int block_
 int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 
 bool ok_mode(int mode) {
-  return mode == MOE_OUT_ATOMIC || mode == MOE_OUT_REDUCE || mode == MOE_OUT_ATOMIC_BF16;
+  return mode == MOE_OUT_ATOMIC || mode == MOE_OUT_REDUCE || mode == MOE_OUT_ATOMIC_BF16 ||
+         mode == MOE_OUT_REDUCE_BF16;
 }
 
 struct Layout {
@@ -92,7 +93,7 @@ Layout forward_layout(int dtype, int mode, int T, int E, int topk, int D, int I,
     L.off[8] = -1;
   }
   if (mode == MOE_OUT_ATOMIC_BF16) L.off[9] = -1;
-  else take(9, (mode == MOE_OUT_ATOMIC ? (int64_t)T : n) * D * 4);
+  else take(9, (mode == MOE_OUT_ATOMIC ? (int64_t)T : n) * D * (mode == MOE_OUT_REDUCE_BF16 ? 2 : 4));
   L.total = p;
   return L;
 }
@@ -311,7 +312,7 @@ int moe_gemm2_down(int dtype, const void* a, const void* a_scale, const void* w2
                                          D, I, block_m, mode, y, (hipStream_t)stream));
 }
 
-int moe_finalize(int mode, const float* y, int T, int topk, int D, uint16_t* out, void* stream) {
+int moe_finalize(int mode, const void* y, int T, int topk, int D, uint16_t* out, void* stream) {
   if (!ok_mode(mode)) return MOE_EINVAL;
   if (T < 0 || topk < 1 || D < 64 || D % 64) return T < 0 || topk < 1 ? MOE_EINVAL : MOE_EUNSUPPORTED;
   if ((int64_t)T * topk * D > INT_MAX) return MOE_ERANGE;
@@ -355,11 +356,12 @@ static int forward_impl(int dtype, int score, int renorm, int mode, const float*
   void* a = at(6);
   void* a_scale = at(7);
   void* g1ws = at(8);
-  float* y = static_cast<float*>(at(9));
+  void* y = at(9);
   // ATOMIC clears the fp32 accumulator, ATOMIC_BF16 the bf16 output (T*D/2 floats' worth)
-  float* zero = mode == MOE_OUT_ATOMIC ? y : mode == MOE_OUT_ATOMIC_BF16 ? reinterpret_cast<float*>(out) : nullptr;
+  float* zero = mode == MOE_OUT_ATOMIC ? static_cast<float*>(y)
+              : mode == MOE_OUT_ATOMIC_BF16 ? reinterpret_cast<float*>(out) : nullptr;
   const int64_t zero_n = mode == MOE_OUT_ATOMIC ? (int64_t)T * D : mode == MOE_OUT_ATOMIC_BF16 ? (int64_t)T * D / 2 : 0;
-  void* y2 = mode == MOE_OUT_ATOMIC_BF16 ? static_cast<void*>(out) : static_cast<void*>(y);
+  void* y2 = mode == MOE_OUT_ATOMIC_BF16 ? static_cast<void*>(out) : y;
   const int64_t cap = moe::sorted_capacity(T, E, topk, block_m);
   hipStream_t s = (hipStream_t)stream;
 

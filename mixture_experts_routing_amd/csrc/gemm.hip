@@ -41,9 +41,9 @@ __device__ __forceinline__ i32x4_t ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(p));
 }
 
-// Output modes of stage 2 (moe_mode): fp32 atomic accumulation, fp32 slot rows, or packed
-// bf16 atomic accumulation straight into the bf16 output.
-enum { OM_ATOMIC = 0, OM_REDUCE = 1, OM_ATOMIC_BF16 = 2 };
+// Output modes of stage 2 (moe_mode): fp32 atomic accumulation, fp32 slot rows, packed
+// bf16 atomic accumulation straight into the bf16 output, or bf16 slot rows.
+enum { OM_ATOMIC = 0, OM_REDUCE = 1, OM_ATOMIC_BF16 = 2, OM_REDUCE_BF16 = 3 };
 
 // out[0..1] += (lo, hi): both values rounded to bf16 (nearest even), then one packed bf16
 // atomic add (the sum is rounded to bf16 again); out must be 4-byte aligned.
@@ -604,6 +604,9 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
       for (int r = 0; r < 4; ++r) c[r] = acc[q][tt][r] * (FP8 ? sc * ws[q][r] : sc);
       if constexpr (OM == OM_REDUCE) {
         *reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)s * D + d0) = make_float4(c[0], c[1], c[2], c[3]);
+      } else if constexpr (OM == OM_REDUCE_BF16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)s * D + d0) =
+            make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
       } else if constexpr (OM == OM_ATOMIC) {
         float* dst = static_cast<float*>(y) + (size_t)(s / k) * D + d0;
 #pragma unroll
@@ -631,7 +634,7 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
 //    4 slots and 16 lanes cover 16 consecutive channels of one slot: each atomic
 //    instruction adds into 64 contiguous bytes per row; the fp32 slot rows of the reduce
 //    mode are regrouped through LDS and stored 256 contiguous bytes per row.
-enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2, PF_G2_ATOMIC_BF16 = 3 };
+enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2, PF_G2_ATOMIC_BF16 = 3, PF_G2_REDUCE_BF16 = 4 };
 constexpr int kPfRows = 64;                          // rows of one sorted block
 constexpr int kPfMaxBlocks = 4;                      // sorted blocks per tile
 constexpr int kPfMaxRows = kPfRows * kPfMaxBlocks;   // 256
@@ -675,6 +678,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
                                              const float* __restrict__ s_fac,
                                              uint8_t* __restrict__ ring) {
   constexpr bool G1 = MODE == PF_G1;
+  constexpr bool RED = MODE == PF_G2_REDUCE || MODE == PF_G2_REDUCE_BF16;  // slot rows through LDS
   constexpr bool FP8 = DT == DT_FP8, FP4 = DT == DT_FP4;
   constexpr int MH = 2 * NB;  // slot-row groups per wave
   // LDS ring: NBUF buffers of (slot rows | weight rows | mxfp4 scales) for one 128-byte chunk
@@ -892,7 +896,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     }
     // the reduce epilogue stages slot rows through the last chunk's buffer, once every wave
     // has read its fragments
-    if (MODE == PF_G2_REDUCE) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (RED) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     uint8_t* const stage = tb;
     const int row0 = G1 ? nt * 128 + wr * 32 : nt * 256 + wr * 64;
     if (row0 < N) {
@@ -967,15 +971,14 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
                 atomic_add_bf16x2(out + (size_t)(s_b / p.k) * D + dch, odd ? rb : cv[1], odd ? cv[3] : rb);
             }
           }
-        } else if constexpr (MODE == PF_G2_REDUCE) {
+        } else if constexpr (RED) {
           // slot rows through LDS (a ring buffer no wave reads any more): each wave
-          // writes its 16 rows x 64 channels of group m, then lane l of store v takes channels
-          // 4 (l % 16) .. + 3 of row 4 v + l / 16, so each store covers 256 contiguous bytes of
-          // four rows (two full lines each) instead of 64 bytes of four rows.  Rows are padded to
-          // 68 floats: the 16 lanes i16 of each of the four rows g land in different banks.
-          float* y = reinterpret_cast<float*>(p.out);
+          // writes its 16 rows x 64 channels of group m in fp32, then each store instruction
+          // covers whole 256-byte (fp32) or 128-byte (bf16) row pieces: fp32, lane l of store v
+          // takes channels 4 (l % 16) .. + 3 of row 4 v + l / 16; bf16, channels 8 (l % 8) .. + 7
+          // of row 8 v + l / 8.  Rows are padded to 68 floats: the 16 lanes i16 of each of the
+          // four rows g land in different banks.
           float* stg = reinterpret_cast<float*>(stage + wave * (16 * 68 * 4));
-          const int j4 = lane & 15, rho0 = lane >> 4;
 #pragma unroll
           for (int m = 0; m < MH; ++m) {
 #pragma unroll
@@ -985,13 +988,31 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
               for (int q = 0; q < 4; ++q) stg[(4 * g + r) * 68 + 16 * q + i16] = acc[q][m][r] * (FP8 ? sc * ws[q] : sc);
             }
             wave_lds_sync();
+            if constexpr (MODE == PF_G2_REDUCE) {
+              float* y = reinterpret_cast<float*>(p.out);
+              const int j4 = lane & 15, rho0 = lane >> 4;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int rho = 4 * v + rho0;
-              const int s = s_slot[(2 * m + th) * 16 + rho];
-              const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&stg[rho * 68 + 4 * j4]);
-              if ((unsigned)s < (unsigned)n_slots)  // padding rows issue nothing
-                __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(y + (size_t)s * D + row0 + 4 * j4));
+              for (int v = 0; v < 4; ++v) {
+                const int rho = 4 * v + rho0;
+                const int s = s_slot[(2 * m + th) * 16 + rho];
+                const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&stg[rho * 68 + 4 * j4]);
+                if ((unsigned)s < (unsigned)n_slots)  // padding rows issue nothing
+                  __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(y + (size_t)s * D + row0 + 4 * j4));
+              }
+            } else {
+              uint16_t* y = reinterpret_cast<uint16_t*>(p.out);
+              const int j8 = lane & 7, rho0 = lane >> 3;
+#pragma unroll
+              for (int v = 0; v < 2; ++v) {
+                const int rho = 8 * v + rho0;
+                const int s = s_slot[(2 * m + th) * 16 + rho];
+                const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(&stg[rho * 68 + 8 * j8]);
+                const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(&stg[rho * 68 + 8 * j8 + 4]);
+                const i32x4_t val = {(int)pack_bf16x2(lo[0], lo[1]), (int)pack_bf16x2(lo[2], lo[3]),
+                                     (int)pack_bf16x2(hi[0], hi[1]), (int)pack_bf16x2(hi[2], hi[3])};
+                if ((unsigned)s < (unsigned)n_slots)  // padding rows issue nothing
+                  __builtin_nontemporal_store(val, reinterpret_cast<i32x4_t*>(y + (size_t)s * D + row0 + 8 * j8));
+              }
             }
             wave_lds_sync();  // the staging rows are rewritten for the next group
           }
@@ -1015,7 +1036,7 @@ __device__ __forceinline__ void prefill_tile(const PfArgs& p, const int* __restr
     // only the reduce mode runs several channel tiles per workgroup (the host launches the
     // others with one): their kernels keep a single pass, whose chunk loop the compiler does
     // not see follow an epilogue with memory operations it counts as pending
-    if (MODE != PF_G2_REDUCE || nt + 1 == p.nt1) return;
+    if (!RED || nt + 1 == p.nt1) return;
     // the next chunk has landed, the epilogue's loads and stores are done and no wave reads
     // the staging.  A builtin wait, which the compiler sees: after an opaque one it would
     // assume the epilogue's memory operations still pending and wait for every load in flight
@@ -1106,10 +1127,10 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
 // is short and the stores are a large share of a tile: runs of up to 8 equal lengths for at
 // most 8 chunks of K (Kimi-K2.5 fp8 down projection, 4 chunks, 28 channel tiles: 1546 ->
 // 1285 us at T=16384 with runs of 7; runs of 4 1465 us, of 10 1534 us, of 14 1653 us), one
-// tile otherwise (GPT-OSS, 45 chunks: 538 us alone, 587 us in runs of 2).  The other modes
-// compute one channel tile per workgroup.
-static int prefill_ntr(int mode, int nts, int nch) {
-  if (mode != PF_G2_REDUCE || nch > 8) return 1;
+// tile otherwise (GPT-OSS, 45 chunks: 538 us alone, 587 us in runs of 2); the same for fp32
+// and bf16 slot rows.  The other modes compute one channel tile per workgroup.
+static int prefill_ntr(bool reduce, int nts, int nch) {
+  if (!reduce || nch > 8) return 1;
   for (int r = nts < 8 ? nts : 8; r > 1; --r)
     if (nts % r == 0) return r;
   return nts < 4 ? nts : 4;
@@ -1166,6 +1187,40 @@ __global__ void __launch_bounds__(256) finalize_reduce_kernel(const float* __res
     }
     const u32x2_t o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
     __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(out) + i);
+  }
+}
+
+// bf16 slot rows: 8 channels per thread (16-byte loads and stores), each value widened to
+// fp32 exactly and added in slot order, as in the fp32 version.
+__global__ void __launch_bounds__(256) finalize_reduce_bf16_kernel(const uint16_t* __restrict__ y,
+                                                                   int T, int k, int D,
+                                                                   uint16_t* __restrict__ out) {
+  const int d8 = D / 8;
+  const int64_t n8 = (int64_t)T * d8;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / d8;
+    const int c = (int)(i - t * d8);
+    const i32x4_t* row = reinterpret_cast<const i32x4_t*>(y + (size_t)t * k * D) + c;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      i32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) v[u] = __builtin_nontemporal_load(row + (size_t)(j0 + u) * (D / 8));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t w = (uint32_t)v[u][h];
+            s[2 * h] += __uint_as_float(w << 16);
+            s[2 * h + 1] += __uint_as_float(w & 0xFFFF0000u);
+          }
+        }
+    }
+    const i32x4_t o = {(int)pack_bf16x2(s[0], s[1]), (int)pack_bf16x2(s[2], s[3]),
+                       (int)pack_bf16x2(s[4], s[5]), (int)pack_bf16x2(s[6], s[7])};
+    __builtin_nontemporal_store(o, reinterpret_cast<i32x4_t*>(out) + i);
   }
 }
 
@@ -1240,14 +1295,17 @@ hipError_t launch_preshuffle(const void* w, int64_t rows, int rowb, void* out, h
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16_t* out,
+hipError_t launch_finalize(int mode, const void* y, int T, int k, int D, uint16_t* out,
                            hipStream_t st) {
   const int64_t n4 = (int64_t)T * D / 4;
   if (n4 == 0 || mode == OM_ATOMIC_BF16) return hipSuccess;  // bf16 atomics wrote out itself
-  if (mode == 0)
-    finalize_atomic_kernel<<<grid_1d(n4), 256, 0, st>>>(y, n4, out);
+  const float* yf = static_cast<const float*>(y);
+  if (mode == OM_ATOMIC)
+    finalize_atomic_kernel<<<grid_1d(n4), 256, 0, st>>>(yf, n4, out);
+  else if (mode == OM_REDUCE)
+    finalize_reduce_kernel<<<grid_1d(n4), 256, 0, st>>>(yf, T, k, D, out);
   else
-    finalize_reduce_kernel<<<grid_1d(n4), 256, 0, st>>>(y, T, k, D, out);
+    finalize_reduce_bf16_kernel<<<grid_1d(n4 / 2), 256, 0, st>>>(static_cast<const uint16_t*>(y), T, k, D, out);
   return hipGetLastError();
 }
 
@@ -1404,7 +1462,7 @@ hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, con
   if (T == 0) return hipSuccess;
   const int mbs = (int)(cap / B);
   if (use_prefill(2, dt, B, T, k, E, D, I)) {
-    const int ntr = prefill_ntr(mode == OM_REDUCE ? PF_G2_REDUCE : PF_G2_ATOMIC, (D + 255) / 256,
+    const int ntr = prefill_ntr(mode == OM_REDUCE || mode == OM_REDUCE_BF16, (D + 255) / 256,
                                 (row_bytes_of(dt, I) + 127) / 128);
     const dim3 grid(xcd_grid(mbs, ((D + 255) / 256 + ntr - 1) / ntr));
 #define MOE_PF2(DTV, MD)                                                                                \
@@ -1412,8 +1470,9 @@ hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, con
                                                     w2_scale, topk_w, sorted_ids, expert_ids, num_valid, \
                                                     T, E, k, D, I, mbs, ntr, y, nullptr, 0, pre)
 #define MOE_PF2_MODES(F8)                                   \
-  if (mode == OM_REDUCE) MOE_PF2(F8, PF_G2_REDUCE);         \
-  else if (mode == OM_ATOMIC) MOE_PF2(F8, PF_G2_ATOMIC);    \
+  if (mode == OM_REDUCE) MOE_PF2(F8, PF_G2_REDUCE);                   \
+  else if (mode == OM_REDUCE_BF16) MOE_PF2(F8, PF_G2_REDUCE_BF16);    \
+  else if (mode == OM_ATOMIC) MOE_PF2(F8, PF_G2_ATOMIC);              \
   else MOE_PF2(F8, PF_G2_ATOMIC_BF16);
     if (dt == DT_FP8) {
       MOE_PF2_MODES(DT_FP8)
@@ -1434,8 +1493,9 @@ hipError_t launch_gemm2(int dt, int pre, const void* a, const void* a_scale, con
 #define MOE_G2_OM(BMV, DTV, OMV) \
   gemm2_ks<BMV, DTV, OMV>(ks, mbs, a, a_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_valid, T, E, k, D, I, y, pre, st)
 #define MOE_G2_DT(BMV, DTV)                                  \
-  if (mode == OM_REDUCE) MOE_G2_OM(BMV, DTV, OM_REDUCE);      \
-  else if (mode == OM_ATOMIC) MOE_G2_OM(BMV, DTV, OM_ATOMIC); \
+  if (mode == OM_REDUCE) MOE_G2_OM(BMV, DTV, OM_REDUCE);                \
+  else if (mode == OM_REDUCE_BF16) MOE_G2_OM(BMV, DTV, OM_REDUCE_BF16); \
+  else if (mode == OM_ATOMIC) MOE_G2_OM(BMV, DTV, OM_ATOMIC);           \
   else MOE_G2_OM(BMV, DTV, OM_ATOMIC_BF16);
 #define MOE_G2(BMV)                             \
   if (dt == DT_FP8) {                           \

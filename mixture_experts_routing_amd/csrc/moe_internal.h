@@ -59,7 +59,7 @@ hipError_t launch_route_backward(const float* logits, const int32_t* topk_ids, c
                                  const float* grad_w, int T, int E, int k, int score, int renorm,
                                  float* grad_logits, hipStream_t st);
 
-hipError_t launch_finalize(int mode, const float* y, int T, int k, int D, uint16_t* out,
+hipError_t launch_finalize(int mode, const void* y, int T, int k, int D, uint16_t* out,
                            hipStream_t st);
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);

@@ -104,14 +104,34 @@ def combined_fp32(y: torch.Tensor, mode: str, k: int, rows) -> np.ndarray:
     return acc
 
 
+# Half a bf16 step relative to the value rounded: bf16 keeps 8 significant bits, so round to
+# nearest even moves a value by at most 2^-8 of its magnitude.
+BF16_HALF_STEP = 2.0 ** -8
+
+
+def contrib_magnitude(ref, rows, k: int, tol: float) -> np.ndarray:
+    """[len(rows), D]: sum over a token's k slots of |c_j| plus the room the slot-row checks
+    give the kernel's fp32 contribution (tol * rms of those contributions + the oracle's
+    contrib_allow): a bound on sum_j |c~_j| for the kernel's own contributions c~_j, the
+    magnitude a bf16 rounding of each of them is measured against."""
+    rows = np.asarray(rows, dtype=np.int64)
+    D = ref.contrib.shape[1]
+    c = ref.contrib.reshape(-1, k, D)[rows]
+    rms_c = float(np.sqrt(np.mean(c * c)))
+    room = tol * rms_c + (0.0 if ref.contrib_allow is None else ref.contrib_allow.reshape(-1, k, D)[rows])
+    return (np.abs(c) + room).sum(axis=1)
+
+
 def compare_layer(out: torch.Tensor, y: torch.Tensor, mode: str, k: int, ref, rows,
                   tol: float, cos_min: float | None):
-    """Layer output of the fp32 combine modes, in two parts: the bf16 output is the fp32
-    combined value rounded to nearest even, bit for bit; the fp32 value is within
+    """Layer output of the modes with a separate combine, in two parts: the bf16 output is the
+    fp32 combined value rounded to nearest even, bit for bit; the fp32 value is within
     tol * rms(out) of the oracle's exact sum (and cosine >= cos_min).  The bound applies before
     the output's own rounding, which alone moves an element by up to half a bf16 step (more
     than 2e-2 * rms for elements beyond 8 * rms).  ref is the oracle's LayerResult; its
-    out_allow (room for the intermediate's rounding decisions) is added element by element."""
+    out_allow (room for the intermediate's rounding decisions) is added element by element.
+    reduce_bf16: each slot row was rounded to bf16 once before the sum, which adds half a bf16
+    step of each contribution, 2^-8 * contrib_magnitude."""
     pre = combined_fp32(y, mode, k, rows)
     got_bits = host_bits(out)[np.asarray(rows, dtype=np.int64)]
     want_bits = oracle.bf16_encode_rne(pre.astype(np.float64))
@@ -119,30 +139,48 @@ def compare_layer(out: torch.Tensor, y: torch.Tensor, mode: str, k: int, ref, ro
     assert bad.size == 0, (f"output is not the rounded fp32 combine at {bad[:4].tolist()}: "
                            f"{got_bits[tuple(bad[0])]:#06x} vs {want_bits[tuple(bad[0])]:#06x}")
     allow = None if ref.out_allow is None else ref.out_allow[rows]
+    if mode == "reduce_bf16":
+        extra = BF16_HALF_STEP * contrib_magnitude(ref, rows, k, tol)
+        allow = extra if allow is None else allow + extra
     return _within(pre.astype(np.float64), ref.out[rows], tol, cos_min, allow)
 
 
-def compare_out_bf16_atomic(out_gpu: torch.Tensor, ref_out: np.ndarray, ref_contrib: np.ndarray, rows,
-                            k: int, tol: float, out_allow: np.ndarray | None = None):
+def compare_slot_rows(y: torch.Tensor, mode: str, ref, slots, tol: float, cos_min: float | None):
+    """Reduce-mode slot rows against the oracle's contributions, under the output's bounds
+    plus the oracle's contrib_allow; bf16 slot rows also move by up to half a bf16 step of
+    the kernel's fp32 contribution, at most 2^-8 * (|c| + the fp32 room)."""
+    slots = np.asarray(slots, dtype=np.int64)
+    want = ref.contrib[slots]
+    allow = None if ref.contrib_allow is None else ref.contrib_allow[slots]
+    if mode == "reduce_bf16":
+        rms = float(np.sqrt(np.mean(want * want)))
+        room = tol * rms + (0.0 if allow is None else allow)
+        extra = BF16_HALF_STEP * (np.abs(want) + room)
+        allow = extra if allow is None else allow + extra
+    return _within(take_rows(y, slots), want, tol, cos_min, allow)
+
+
+def compare_out_bf16_atomic(out_gpu: torch.Tensor, ref, rows, k: int, tol: float):
     """Packed bf16 atomic accumulation: each of a token's k contributions is rounded to bf16
     and each of the k atomic adds rounds the running sum to bf16, so on top of the fp32
-    modes' bound tol * rms(ref) an element may move by (k + 1) * 2^-9 * sum_j |c_j| (half a
-    bf16 step per rounding, of a value at most sum_j |c_j|).  Returns the largest fraction
-    of that allowance used."""
+    modes' bound tol * rms(ref) an element may move by (k + 1) half bf16 steps, each at most
+    2^-8 of a value no larger than M = sum_j |c~_j| (1 + 2^-8)^k (the kernel's fp32
+    contributions, bounded by contrib_magnitude; the factor covers the running sum's own
+    roundings).  ref is the oracle's LayerResult.  Returns the largest fraction of that
+    allowance used."""
     got = take_rows(out_gpu, rows)
-    ref = ref_out[rows]
+    ref_o = ref.out[rows]
     assert np.isfinite(got).all()
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    D = ref.shape[1]
-    s_abs = np.abs(ref_contrib.reshape(-1, k, D)[rows]).sum(axis=1)
-    allow = tol * rms + (k + 1) * 2.0 ** -9 * s_abs
-    if out_allow is not None:
-        allow = allow + out_allow[rows]
-    err = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref_o * ref_o)))
+    m_abs = contrib_magnitude(ref, rows, k, tol) * (1.0 + BF16_HALF_STEP) ** k
+    allow = tol * rms + (k + 1) * BF16_HALF_STEP * m_abs
+    if ref.out_allow is not None:
+        allow = allow + ref.out_allow[rows]
+    err = np.abs(got - ref_o)
     used = float((err / allow).max())
     i = np.unravel_index(np.argmax(err / allow), err.shape)
-    assert used <= 1.0, (f"err {err[i]:.4g} > allowance {allow[i]:.4g} at {i} (ref {ref[i]:.5g}, "
-                         f"sum|c| {s_abs[i]:.4g}, rms {rms:.4g})")
+    assert used <= 1.0, (f"err {err[i]:.4g} > allowance {allow[i]:.4g} at {i} (ref {ref_o[i]:.5g}, "
+                         f"sum|c| bound {m_abs[i]:.4g}, rms {rms:.4g})")
     return used
 
 

@@ -55,7 +55,7 @@ def test_sorted_capacity_matches_oracle(lib, T, E, k, B):
 def test_workspace_layout(lib):
     import mixture_experts_routing_amd as m
     for dtype in ("bf16", "fp8", "mxfp4"):
-        for mode in ("atomic", "reduce", "atomic_bf16"):
+        for mode in ("atomic", "reduce", "atomic_bf16", "reduce_bf16"):
             for (T, E, k, D, I, B) in [(4, 8, 2, 128, 128, 16), (8192, 2304, 36, 128, 128, 32),
                                        (16, 256, 8, 7168, 2048, 16)]:
                 total, offs = m.moe_forward_workspace_layout(dtype, mode, T, E, k, D, I, B)
@@ -66,7 +66,8 @@ def test_workspace_layout(lib):
                          "a": n * I * 2 if dtype == "bf16" else n * I if dtype == "fp8" else n * I // 2,
                          "a_scale": 4 * n if dtype == "fp8" else n * I // 32 if dtype == "mxfp4" else 0,
                          "gemm1_scratch": 2 * n * I if dtype in ("fp8", "mxfp4") else 0,
-                         "y": 0 if mode == "atomic_bf16" else 4 * D * (T if mode == "atomic" else n)}
+                         "y": (0 if mode == "atomic_bf16" else 4 * D * T if mode == "atomic" else
+                               4 * D * n if mode == "reduce" else 2 * D * n)}
                 spans = []
                 for f, o in offs.items():
                     if sizes[f] == 0:
@@ -93,7 +94,7 @@ def test_forward_workspace_bytes(lib):
     """moe_forward_workspace_bytes returns the layout's total, and 0 for invalid arguments."""
     import mixture_experts_routing_amd as m
     for dtype in ("bf16", "fp8", "mxfp4"):
-        for mode in ("atomic", "reduce", "atomic_bf16"):
+        for mode in ("atomic", "reduce", "atomic_bf16", "reduce_bf16"):
             for (T, E, k, D, I, B) in [(4, 8, 2, 128, 128, 16), (8192, 2304, 36, 128, 128, 32),
                                        (16, 256, 8, 7168, 2048, 16), (0, 8, 2, 128, 128, 16)]:
                 total, _ = m.moe_forward_workspace_layout(dtype, mode, T, E, k, D, I, B)
@@ -201,7 +202,7 @@ def gemm2_call(lib, dtype=0, mode=0, T=4, E=8, k=2, D=128, I=64, B=16, cap=None,
 
 
 def test_gemm2_validation(lib):
-    assert gemm2_call(lib, mode=3) == EINVAL
+    assert gemm2_call(lib, mode=4) == EINVAL
     assert gemm2_call(lib, mode=-1) == EINVAL
     assert gemm2_call(lib, dtype=-1) == EINVAL
     assert gemm2_call(lib, D=64 + 32) == EUNSUP
@@ -214,7 +215,9 @@ def test_gemm2_validation(lib):
 
 
 def test_finalize_and_forward_validation(lib):
-    assert lib.moe_finalize(3, GOOD, 4, 2, 128, GOOD, None) == EINVAL
+    assert lib.moe_finalize(4, GOOD, 4, 2, 128, GOOD, None) == EINVAL
+    assert lib.moe_finalize(3, GOOD, 4, 2, 100, GOOD, None) == EUNSUP
+    assert lib.moe_finalize(3, None, 4, 2, 128, GOOD, None) == EINVAL
     # packed bf16 atomics write out in stage 2: nothing to combine, no pointer is used
     assert lib.moe_finalize(2, None, 4, 2, 128, None, None) == OK
     assert lib.moe_finalize(2, None, 4, 2, 100, None, None) == EUNSUP

@@ -35,7 +35,9 @@ def default_secondaries():
                           ("kimi", 4096, "atomic_bf16"), ("kimi", 16384, "atomic_bf16"),
                           ("kimi_mxfp4", 64, None), ("kimi_mxfp4", 4096, None),
                           ("kimi_mxfp4", 16384, None), ("kimi", 4096, "reduce"),
-                          ("kimi", 16384, "reduce"), ("kimi_mxfp4", 16384, "reduce")):
+                          ("kimi", 16384, "reduce"), ("kimi_mxfp4", 16384, "reduce"),
+                          ("gptoss", 4096, "reduce_bf16"), ("kimi", 4096, "reduce_bf16"),
+                          ("kimi", 16384, "reduce_bf16"), ("kimi_mxfp4", 16384, "reduce_bf16")):
         out.append(fake_layer(name, T, mode))
     for name, T in (("deepseek", 16), ("deepseek", 1), ("deepseek", 2), ("deepseek", 4), ("deepseek", 8),
                     ("kimi", 64), ("kimi_mxfp4", 64), ("gptoss", 16)):

@@ -15,8 +15,8 @@ import torch
 import oracle
 import synth
 from _gpu_helpers import (ACC_REL, BF16_COS, BF16_TOL, FP8_TOL, PerExpert, check_a_bf16, check_a_fp8, check_a_mx,
-                          check_route, compare_layer, compare_out, compare_out_bf16_atomic, host_bits,
-                          oracle_route)
+                          check_route, compare_layer, compare_out, compare_out_bf16_atomic, compare_slot_rows,
+                          host_bits, oracle_route)
 
 pytestmark = pytest.mark.gpu
 
@@ -127,7 +127,7 @@ SMALL = ([(*c, "bf16") for c in SMALL_BF16] + [(*c, "fp8") for c in SMALL_FP8] +
          [(*c, "mxfp4") for c in SMALL_MX])
 
 
-@pytest.mark.parametrize("mode", ["atomic", "reduce"])
+@pytest.mark.parametrize("mode", ["atomic", "reduce", "reduce_bf16"])
 @pytest.mark.parametrize("T,E,k,D,I,B,dtype", SMALL)
 def test_layer_small_full_compare(T, E, k, D, I, B, dtype, mode):
     inp = synth.small_layer_inputs(T, E, k, D, I, dtype, seed=T + D, w_std=0.05)
@@ -140,8 +140,8 @@ def test_layer_small_full_compare(T, E, k, D, I, B, dtype, mode):
     rows = np.arange(T)
     tol, cos = (BF16_TOL, BF16_COS) if dtype == "bf16" else (FP8_TOL, None)
     compare_layer(out, views["y"], mode, k, ref, rows, tol, cos)
-    if mode == "reduce":  # the slot rows themselves
-        compare_out(views["y"], ref.contrib, np.arange(T * k), tol, cos, allow=ref.contrib_allow)
+    if mode != "atomic":  # the slot rows themselves
+        compare_slot_rows(views["y"], mode, ref, np.arange(T * k), tol, cos)
     check_intermediate(views, ref, dtype, np.arange(T * k))
 
 
@@ -155,12 +155,11 @@ def test_layer_small_atomic_bf16(T, E, k, D, I, B, dtype):
     ref = oracle_layer(inp, ref_route, dtype)
     out, views = run_forward(to_cuda(inp), k, B, dtype, "atomic_bf16")
     assert views["y"] is None
-    compare_out_bf16_atomic(out, ref.out, ref.contrib, np.arange(T), k, BF16_TOL if dtype == "bf16" else FP8_TOL,
-                            out_allow=ref.out_allow)
+    compare_out_bf16_atomic(out, ref, np.arange(T), k, BF16_TOL if dtype == "bf16" else FP8_TOL)
     check_intermediate(views, ref, dtype, np.arange(T * k))
 
 
-@pytest.mark.parametrize("mode", ["atomic", "reduce"])
+@pytest.mark.parametrize("mode", ["atomic", "reduce", "reduce_bf16"])
 @pytest.mark.parametrize("dtype,I", [("bf16", 64), ("fp8", 512)])
 def test_layer_long_expert_run(dtype, I, mode):
     """One expert holding 65 sorted blocks: prefill tiles of four blocks are counted from the
@@ -175,10 +174,12 @@ def test_layer_long_expert_run(dtype, I, mode):
     ref = oracle_layer(inp, ref_route, dtype)
     out, views = run_forward(to_cuda(inp), k, B, dtype, mode)
     y = views["y"]
-    want, allow = (ref.out, ref.out_allow) if mode == "atomic" else (ref.contrib, ref.contrib_allow)
     tol = BF16_TOL if dtype == "bf16" else FP8_TOL
-    compare_out(y, want, np.arange(y.shape[0]), tol, BF16_COS, allow=allow)
-    fin = y if mode == "atomic" else y.view(T, k, D).sum(1)
+    if mode == "atomic":
+        compare_out(y, ref.out, np.arange(T), tol, BF16_COS, allow=ref.out_allow)
+    else:
+        compare_slot_rows(y, mode, ref, np.arange(T * k), tol, BF16_COS)
+    fin = y if mode == "atomic" else y.view(T, k, D).float().sum(1)
     assert torch.equal(out, fin.to(torch.bfloat16))
 
 
@@ -295,8 +296,7 @@ def test_layer_full_size_sampled(name, T, tokens, weights_cache):
                 ref_route, T, wl.topk)
     tile = None
     if T >= 4096:
-        # every slot row of one whole prefill tile, in reduce mode (the slot rows themselves)
-        y_red = views["y"] if wl.mode == "reduce" else run_forward(inp, wl.topk, wl.block_m, wl.dtype, "reduce")[1]["y"]
+        # every slot row of one whole prefill tile, in both reduce modes (the slot rows themselves)
         sid, nb, nblocks = largest_tile_slots(views, wl.block_m)
         tile = sid[sid < T * wl.topk]
     ref = oracle_layer(inp, ref_route, wl.dtype, tokens=tokens, slots=tile)
@@ -307,13 +307,23 @@ def test_layer_full_size_sampled(name, T, tokens, weights_cache):
     slots = np.concatenate([np.arange(t * wl.topk, (t + 1) * wl.topk) for t in tokens])
     check_intermediate(views, ref, wl.dtype, slots)
     if tile is not None:
-        res = compare_out(y_red, ref.contrib, tile, tol, cos, allow=ref.contrib_allow)
-        report(name, T, f"slot rows of a {nb}-block tile ({len(tile)} rows; the expert has {nblocks} blocks)", res)
-        del y_red
+        for mode in ("reduce", "reduce_bf16"):
+            if mode == wl.mode:
+                out_r, y_r = out, views["y"]
+            else:
+                out_r, v_r = run_forward(inp, wl.topk, wl.block_m, wl.dtype, mode)
+                y_r = v_r["y"]
+                res = compare_layer(out_r, y_r, mode, wl.topk, ref, rows, tol, cos)
+                report(name, T, f"{len(rows)} tokens, {mode}", res)
+            res = compare_slot_rows(y_r, mode, ref, tile, tol, cos)
+            report(name, T, f"{mode} slot rows of a {nb}-block tile ({len(tile)} rows; the expert has {nblocks} blocks)",
+                   res)
+            del out_r, y_r
+            torch.cuda.empty_cache()
     if name in ("deepseek", "kimi") and T in (16, 16384):
         # the same inputs with packed bf16 atomics into out
         out2, _ = run_forward(inp, wl.topk, wl.block_m, wl.dtype, "atomic_bf16")
-        used = compare_out_bf16_atomic(out2, ref.out, ref.contrib, rows, wl.topk, tol, out_allow=ref.out_allow)
+        used = compare_out_bf16_atomic(out2, ref, rows, wl.topk, tol)
         sys.stderr.write(f"[parity] {name} T={T} packed bf16 atomics: {used:.3g} of the allowance used\n")
 
 

@@ -120,7 +120,8 @@ FWD = [
     (37, 16, 4, 384, 192, 16, "bf16", "atomic"), (640, 8, 4, 384, 512, 64, "bf16", "atomic"),
     (200, 40, 5, 256, 640, 64, "fp8", "atomic_bf16"), (640, 8, 4, 384, 1024, 64, "fp8", "reduce"),
     (61, 12, 3, 512, 512, 32, "fp8", "atomic"), (300, 8, 2, 512, 512, 64, "mxfp4", "atomic"),
-    (37, 16, 4, 512, 512, 16, "mxfp4", "reduce"),
+    (37, 16, 4, 512, 512, 16, "mxfp4", "reduce"), (640, 8, 4, 384, 1024, 64, "fp8", "reduce_bf16"),
+    (37, 16, 4, 384, 192, 16, "bf16", "reduce_bf16"),
 ]
 
 
@@ -138,7 +139,7 @@ def test_preshuffled_forward_against_oracle(T, E, k, D, I, B, dtype, mode, seed)
     ref = oracle_layer(cpu, oracle_route(cpu["logits"], k, B), dtype)
     tol = BF16_TOL if dtype == "bf16" else FP8_TOL
     if mode == "atomic_bf16":
-        compare_out_bf16_atomic(out, ref.out, ref.contrib, np.arange(T), k, tol, out_allow=ref.out_allow)
+        compare_out_bf16_atomic(out, ref, np.arange(T), k, tol)
     else:
         y = m.workspace_views(ws, offs, dtype, mode, T, E, k, D, I, B)["y"]
         compare_layer(out, y, mode, k, ref, np.arange(T), tol, BF16_COS if dtype == "bf16" else None)
