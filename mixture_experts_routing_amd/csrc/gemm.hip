@@ -632,8 +632,8 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
 //    consecutive channels of one slot (gate and up pair in the same lane);
 //  * stage 2 (down): the operands are swapped, so a lane holds one model_dim channel of
 //    4 slots and 16 lanes cover 16 consecutive channels of one slot: each atomic
-//    instruction adds into 64 contiguous bytes per row; the fp32 slot rows of the reduce
-//    mode are regrouped through LDS and stored 256 contiguous bytes per row.
+//    instruction adds into 64 contiguous bytes per row; the slot rows of the reduce modes
+//    are regrouped through LDS and stored 256 (fp32) or 128 (bf16) contiguous bytes per row.
 enum { PF_G1 = 0, PF_G2_ATOMIC = 1, PF_G2_REDUCE = 2, PF_G2_ATOMIC_BF16 = 3, PF_G2_REDUCE_BF16 = 4 };
 constexpr int kPfRows = 64;                          // rows of one sorted block
 constexpr int kPfMaxBlocks = 4;                      // sorted blocks per tile
@@ -1127,8 +1127,8 @@ __global__ void __launch_bounds__(512, 1) gemm_prefill_kernel(
 // is short and the stores are a large share of a tile: runs of up to 8 equal lengths for at
 // most 8 chunks of K (Kimi-K2.5 fp8 down projection, 4 chunks, 28 channel tiles: 1546 ->
 // 1285 us at T=16384 with runs of 7; runs of 4 1465 us, of 10 1534 us, of 14 1653 us), one
-// tile otherwise (GPT-OSS, 45 chunks: 538 us alone, 587 us in runs of 2); the same for fp32
-// and bf16 slot rows.  The other modes compute one channel tile per workgroup.
+// tile otherwise (GPT-OSS, 45 chunks: 538 us alone, 587 us in runs of 2); bf16 slot rows take
+// the same runs.  The other modes compute one channel tile per workgroup.
 static int prefill_ntr(bool reduce, int nts, int nch) {
   if (!reduce || nch > 8) return 1;
   for (int r = nts < 8 ? nts : 8; r > 1; --r)
