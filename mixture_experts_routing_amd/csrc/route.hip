@@ -20,7 +20,9 @@
 //    outputs) -> one-workgroup sort (two launches).
 //  * Otherwise: select -> per-chunk counts -> per-expert prefix over chunks with a
 //    padded scan per 64 experts -> per-chunk scatter, which also combines the group
-//    offsets and writes the block experts (four launches, 64-token chunks).
+//    offsets and writes the block experts (four launches, 64-token chunks); where each
+//    chunk's workgroup can read all E x nch counts (one byte each, at most 128 KB) the prefix
+//    and the padded scan run inside the scatter kernel instead (three launches).
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "route_select.h"
@@ -378,6 +380,145 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(
   if (chunk == 0 && tid == 0) *num_valid = nv;
 }
 
+// ----------------------------------------------------------------------------- fused prefix
+// Where every chunk may read all per-chunk counts (route_fused_scan), the prefix over chunks
+// and the padded scan run inside the scatter kernel: three launches instead of four.  Counts
+// are bytes (a chunk of 64 tokens picks an expert at most 64 times), expert-major with rows of
+// nchp = nch rounded up to 16 bytes: cnt8[e * nchp + chunk]; the row tails are never written
+// and never summed.
+__global__ void __launch_bounds__(1024) route_count8_kernel(const int32_t* __restrict__ topk_ids,
+                                                            int T, int E, int k, int nch,
+                                                            uint8_t* __restrict__ cnt8) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* h = reinterpret_cast<int32_t*>(smem);
+  const int tid = threadIdx.x, chunk = blockIdx.x;
+  const int nchp = (nch + 15) & ~15;
+  for (int e = tid; e < E; e += 1024) h[e] = 0;
+  __syncthreads();
+  const int t0 = chunk * kChunkTokens, t1 = min(T, t0 + kChunkTokens);
+  for (int s = t0 * k + tid; s < t1 * k; s += 1024) {
+    const int e = topk_ids[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) cnt8[(size_t)e * nchp + chunk] = (uint8_t)h[e];
+}
+
+// Bytes of a dword at chunk positions c0 .. c0 + 3 below `lim`: a byte mask.
+__device__ __forceinline__ uint32_t bytes_below(int lim, int c0) {
+  const int n = lim - c0;
+  return n <= 0 ? 0u : n >= 4 ? 0xFFFFFFFFu : (1u << (8 * n)) - 1u;
+}
+
+// Per chunk, as route_scatter_kernel, but each workgroup first sums every expert's row of
+// chunk counts (its total, and the part before this chunk: v_sad_u8 adds four bytes at once)
+// and scans the padded totals itself.  The ids of its tokens are loaded before the counts, so
+// both are in flight together.
+// Dynamic LDS: hist [16][E4] u8 | tot [E4] i32 | pre [E4] i32 | off [E4] i32 | wsum [20] i32
+__global__ void __launch_bounds__(1024) route_scan_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int E, int k, int B, int nch,
+    const uint8_t* __restrict__ cnt8, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_valid) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int E4 = (E + 3) & ~3;
+  const int nchp = (nch + 15) & ~15;
+  uint8_t* s_hist = smem;
+  int32_t* s_tot = reinterpret_cast<int32_t*>(smem + 16 * E4);
+  int32_t* s_pre = s_tot + E4;
+  int32_t* s_off = s_pre + E4;
+  int32_t* s_wsum = s_off + E4;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, chunk = blockIdx.x;
+  constexpr int TPW = kChunkTokens / 16;
+  const int t0 = chunk * kChunkTokens + w * TPW, t1 = min(T, t0 + TPW);
+  int ids[TPW];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q)
+    ids[q] = (t0 + q < t1 && lane < k) ? topk_ids[(size_t)(t0 + q) * k + lane] : -1;
+  for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
+  for (int e = tid; e < E; e += 1024) {
+    const uint4* row = reinterpret_cast<const uint4*>(cnt8 + (size_t)e * nchp);
+    uint32_t tot = 0, pre = 0;
+    for (int q = 0; q < nchp / 16; ++q) {
+      const uint4 v = row[q];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int c0 = 16 * q + 4 * h;
+        tot = __builtin_amdgcn_sad_u8(d[h] & bytes_below(nch, c0), 0u, tot);
+        pre = __builtin_amdgcn_sad_u8(d[h] & bytes_below(chunk, c0), 0u, pre);
+      }
+    }
+    s_tot[e] = (int)tot;
+    s_pre[e] = (int)pre;
+  }
+  __syncthreads();
+  // padded exclusive offsets of the experts, in expert order (each thread a contiguous range)
+  const int per = (E + 1023) / 1024;
+  const int e0 = tid * per;
+  int local = 0;
+  for (int q = 0; q < per; ++q)
+    if (e0 + q < E) local += (s_tot[e0 + q] + B - 1) / B * B;
+  const int incl = wave_incl_scan_i32(local);
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int x = lane < 16 ? s_wsum[lane] : 0;
+    const int xi = wave_incl_scan_i32(x);
+    if (lane < 16) s_wsum[lane] = xi - x;
+    if (lane == 15) s_wsum[16] = xi;
+  }
+  __syncthreads();
+  {
+    int run = s_wsum[w] + incl - local;
+    for (int q = 0; q < per; ++q) {
+      const int e = e0 + q;
+      if (e < E) {
+        s_off[e] = run;
+        run += (s_tot[e] + B - 1) / B * B;
+      }
+    }
+  }
+  uint8_t* my_hist = s_hist + w * E4;
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int t = t0 + q;
+    if (t >= t1) break;
+    for (int j = lane; j < k; j += 64) {
+      const int e = j < 64 ? ids[q] : topk_ids[(size_t)t * k + j];
+      if ((unsigned)e < (unsigned)E) my_hist[e] += 1;
+    }
+    wave_lds_sync();
+  }
+  __syncthreads();  // s_off; the histograms
+  for (int e = tid; e < E; e += 1024) {
+    int c = 0;
+    for (int ww = 0; ww < 16; ++ww) {
+      const int h = s_hist[ww * E4 + e];
+      s_hist[ww * E4 + e] = (uint8_t)c;
+      c += h;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int t = t0 + q;
+    if (t >= t1) break;
+    for (int j = lane; j < k; j += 64) {
+      const int e = j < 64 ? ids[q] : topk_ids[(size_t)t * k + j];
+      if ((unsigned)e >= (unsigned)E) continue;
+      const int r = my_hist[e];
+      my_hist[e] = (uint8_t)(r + 1);
+      sorted_ids[s_off[e] + s_pre[e] + r] = t * k + j;
+    }
+    wave_lds_sync();
+  }
+  for (int64_t e = chunk + (int64_t)nch * tid; e < E; e += (int64_t)nch * 1024) {
+    const int c = s_tot[e];
+    if (c > 0) write_block_experts((int)e, s_off[e], c, B, expert_ids);
+  }
+  if (chunk == 0 && tid == 0) *num_valid = s_wsum[16];
+}
+
 __global__ void write_zero_i32(int32_t* p) { *p = 0; }
 
 // ----------------------------------------------------------------------------- host side
@@ -397,10 +538,23 @@ bool route_is_twostage(int T, int E, int k) {
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// The fused prefix: every chunk's workgroup reads all E rows of count bytes, and its LDS holds
+// 28 bytes per expert.  Up to 128 KB per workgroup it beats the separate prefix launch (graph
+// replay: T = 8192, E = 512, k = 4: 23.1 -> 19.6 us; E = 1024: 27.2 -> 25.9 us; the Kimi-K2.5
+// share at T = 16384, 98.5 KB: 32.6 -> 29.6 us); beyond, it loses (E = 2304 at T = 8192, 295 KB:
+// 44.4 -> 46.3 us; the Kimi share at T = 33288, 203 KB: 55.8 -> 66.1 us).
+static bool route_fused_scan(int E, int nch) {
+  return E <= 4096 && (int64_t)E * ((nch + 15) / 16 * 16) <= 128 * 1024;
+}
+
+// The larger of the two layouts: int32 counts, totals, offsets and group sums (four launches)
+// or byte counts in rows of nch rounded up to 16 (fused prefix).
 int64_t route_workspace_bytes(int T, int E, int k) {
   if (T == 0 || route_is_oneshot(T, E, k) || route_is_twostage(T, E, k)) return 0;
   const int64_t nchunks = (T + kChunkTokens - 1) / kChunkTokens;
-  return align256(nchunks * E * 4) + align256((int64_t)E * 4) * 2 + align256(128 * 4);
+  const int64_t unfused = align256(nchunks * E * 4) + align256((int64_t)E * 4) * 2 + align256(128 * 4);
+  const int64_t fused = align256((int64_t)E * ((nchunks + 15) / 16 * 16));
+  return fused > unfused ? fused : unfused;
 }
 
 template <int NV, bool GROUPED>
@@ -450,6 +604,23 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
     }
     const int nch = (T + kChunkTokens - 1) / kChunkTokens;
     char* wsb = reinterpret_cast<char*>(ws);
+    if (route_fused_scan(E, nch)) {
+      uint8_t* cnt8 = reinterpret_cast<uint8_t*>(wsb);
+      route_select_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
+          logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
+          expert_ids);
+      route_count8_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt8);
+      const size_t lds = 28 * (size_t)E4 + 20 * 4;  // <= 112 KB for E <= 4096
+      if (lds > 64 * 1024) {
+        const hipError_t err = hipFuncSetAttribute((const void*)route_scan_scatter_kernel,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)lds);
+        if (err != hipSuccess) return err;
+      }
+      route_scan_scatter_kernel<<<nch, 1024, lds, st>>>(topk_ids, T, E, k, B, nch, cnt8,
+                                                        sorted_ids, expert_ids, num_valid);
+      return hipGetLastError();
+    }
     int32_t* cnt = reinterpret_cast<int32_t*>(wsb);
     int32_t* tot = reinterpret_cast<int32_t*>(wsb + align256((int64_t)nch * E * 4));
     int32_t* loff =

@@ -153,6 +153,10 @@ def test_route_validation(lib):
     assert route_call(lib, T=1000, E=256, k=8, ws=GOOD, ws_bytes=need - 1) == ENOSPC
     assert route_call(lib, T=1000, E=256, k=8, ws=None, ws_bytes=need) == EINVAL
     assert lib.moe_route_workspace_bytes(16, 256, 8, 16) == 0
+    # the larger of the two multi-workgroup layouts: int32 counts with totals and offsets, or byte
+    # counts in rows of 16 chunks (one chunk of 64 tokens, 3000 experts: 48000 bytes)
+    assert lib.moe_route_workspace_bytes(64, 3000, 8, 16) == 48128
+    assert lib.moe_route_workspace_bytes(8192, 512, 4, 32) == 128 * 512 * 4 + 2 * 2048 + 512
 
 
 def gemm1_call(lib, dtype=0, T=4, E=8, k=2, D=128, I=64, B=16, cap=None, ptrs=None, ws_bytes=1 << 30):
