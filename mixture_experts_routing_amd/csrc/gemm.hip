@@ -575,8 +575,31 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
     for (int tt = 0; tt < NT; ++tt) acc[q][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int kb0, kb1;
   k_range(rowb, kp, KS, kb0, kb1);
-  if (pre) mainloop<DT, NG, NT, U, true>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
-  else mainloop<DT, NG, NT, U, false>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  // A block whose real rows all sit in its first 16 (decode sizes with 64-row blocks, where an
+  // expert holds a few slots; the sort puts an expert's slots ahead of its padding) runs that
+  // row group alone, two chunks per batch of loads (short rows, no K split): mxfp4 rows of 256
+  // bytes in one memory round trip per wave instead of two, and no MFMAs on the padding row
+  // groups, whose accumulators stay zero and which the epilogue skips.  (Four chunks per batch
+  // would take the kernel past 256 registers, to one wave per SIMD.)
+  bool small = false;
+  if constexpr (NT > 1 && KS == 1) small = (rowb == 256 || rowb == 512) && __ballot(xrow[1] != nullptr) == 0;
+  if (small) {
+    if constexpr (NT > 1 && KS == 1) {
+      f32x4_t a1[NG][1];
+#pragma unroll
+      for (int q = 0; q < NG; ++q) a1[q][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* const x1[1] = {xrow[0]};
+      const uint8_t* const s1[1] = {xsc[0]};
+      if (pre) mainloop<DT, NG, 1, 2, true>(wrow, x1, wsc, s1, kb0, kb1, rowb, a1);
+      else mainloop<DT, NG, 1, 2, false>(wrow, x1, wsc, s1, kb0, kb1, rowb, a1);
+#pragma unroll
+      for (int q = 0; q < NG; ++q) acc[q][0] = a1[q][0];
+    }
+  } else if (pre) {
+    mainloop<DT, NG, NT, U, true>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  } else {
+    mainloop<DT, NG, NT, U, false>(wrow, xrow, wsc, xsc, kb0, kb1, rowb, acc);
+  }
   if (!reduce_k_split<KS, RG, NG, NT>(acc, rg, kp, red)) return;
 
   float ws[NG][4];

@@ -237,13 +237,13 @@ FULL = [
     ("deepseek", 16, [0, 5, 9, 15]),
     ("gptoss", 16, [0, 7, 15]),
     ("gptoss", 4096, spread(4096)),
-    ("kimi", 64, [0, 33, 63]),
+    ("kimi", 64, list(range(0, 64, 4)) + [63]),
     ("kimi", 4096, spread(4096)),
     ("kimi", 16384, spread(16384)),
     # the largest T the layer calls accept at this shape (T*k*D < 2^31): the prefill GEMMs at
     # their largest gathered-row offsets
     ("kimi", 33288, spread(33288)),
-    ("kimi_mxfp4", 64, [0, 33, 63]),
+    ("kimi_mxfp4", 64, list(range(0, 64, 4)) + [63]),
     ("kimi_mxfp4", 4096, spread(4096)),
     ("kimi_mxfp4", 16384, spread(16384)),
 ]
@@ -327,14 +327,19 @@ def test_layer_full_size_sampled(name, T, tokens, weights_cache):
         sys.stderr.write(f"[parity] {name} T={T} packed bf16 atomics: {used:.3g} of the allowance used\n")
 
 
+@pytest.mark.parametrize("skew", [False, True])
 @pytest.mark.parametrize("mode", ["reduce", "atomic"])
-def test_layer_short_rows_no_k_split(mode):
+def test_layer_short_rows_no_k_split(mode, skew):
     """Decode down projection with BLOCK_M 64, no K split (n_act * D/32 >= 256*16*12 waves) and
     rows of at most 1 KB (bf16 I = 256): the kernel variant with four 16-row weight groups per
-    wave.  Sampled tokens against the oracle."""
+    wave.  Its blocks with at most 16 real rows run the first row group alone; with skew, two
+    experts that every token prefers fill whole 64-row blocks, so both forms run in one launch.
+    Sampled tokens against the oracle."""
     T, E, k, D, I, B = 64, 256, 8, 7168, 256, 64
     wl = synth.Workload("short_rows", E, k, D, I, B, "bf16", mode, 1.0, 0.02)
     inp = synth.layer_inputs(wl, T, seed=11, device="cuda")
+    if skew:
+        inp["logits"][:, :2] += 6.0
     ref_route = oracle_route(inp["logits"], k, B)
     # the library sizes the K split from min(T*k, E) experts (before routing is known)
     assert min(T * k, E) * (D // 32) >= 256 * 16 * 12 and 2 * I <= 1024 and T * k < 32 * E
