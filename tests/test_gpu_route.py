@@ -105,12 +105,14 @@ def test_route_crafted_ties(kind, T, E, k, B):
                                      (16, 256, 64, 16), (17, 8160, 1, 64), (128, 2560, 8, 16),
                                      (129, 2560, 8, 16), (128, 2561, 4, 16), (100, 64, 64, 64),
                                      (64, 3000, 8, 16), (1, 3000, 2, 16), (8192, 4096, 8, 32),
-                                     (200, 300, 70, 64), (200, 4100, 70, 64)])
+                                     (200, 300, 70, 64), (200, 4100, 70, 64),
+                                     (8192, 1024, 8, 32), (8193, 1024, 8, 32)])
 def test_route_edges(T, E, k, B):
     """Path boundaries: one-shot, two-stage and multi-workgroup sorts; in the last, the prefix over
     chunks inside the scatter kernel (E <= 4096 and at most 128 KB of count bytes per chunk, e.g.
     3000 experts in one or two chunks) and in a launch of its own (E = 8160; E = 4096 at T = 8192),
-    each also with k > 64 (picks past the first 64 read from memory)."""
+    each also with k > 64 (picks past the first 64 read from memory); and either side of the
+    128 KB limit (E = 1024: 128 chunks of counts fused, 129 not)."""
     logits = synth.logits(T, E, seed=11)
     got = run_route(logits.cuda(), k, B)
     check_route(got, oracle_route(logits, k, B), T, k)
