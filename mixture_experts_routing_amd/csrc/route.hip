@@ -435,21 +435,51 @@ __global__ void __launch_bounds__(1024) route_scan_scatter_kernel(
   for (int q = 0; q < TPW; ++q)
     ids[q] = (t0 + q < t1 && lane < k) ? topk_ids[(size_t)(t0 + q) * k + lane] : -1;
   for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
-  for (int e = tid; e < E; e += 1024) {
-    const uint4* row = reinterpret_cast<const uint4*>(cnt8 + (size_t)e * nchp);
-    uint32_t tot = 0, pre = 0;
-    for (int q = 0; q < nchp / 16; ++q) {
-      const uint4 v = row[q];
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  {
+    // L lanes share an expert's row of R 16-byte pieces (L = R rounded up to a power of two,
+    // at most 64): a wave load covers whole consecutive rows, four passes of loads are in
+    // flight together, and a butterfly over the L lanes adds the pieces' sums.
+    const int R = nchp / 16;
+    int L = 1;
+    while (L < R && L < 64) L <<= 1;
+    const int lgL = __builtin_ctz(L);
+    const int sub = lane & (L - 1);
+    const int pass = 16 * (64 >> lgL);  // rows per workgroup and pass
+    const uint4* cnt16 = reinterpret_cast<const uint4*>(cnt8);
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    for (int base = w * (64 >> lgL); base < E; base += 4 * pass) {  // wave-uniform
+      uint4 v[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int c0 = 16 * q + 4 * h;
-        tot = __builtin_amdgcn_sad_u8(d[h] & bytes_below(nch, c0), 0u, tot);
-        pre = __builtin_amdgcn_sad_u8(d[h] & bytes_below(chunk, c0), 0u, pre);
+      for (int u = 0; u < 4; ++u) {
+        const int e = base + u * pass + (lane >> lgL);
+        v[u] = (e < E && sub < R) ? cnt16[(size_t)e * R + sub] : zero4;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = base + u * pass + (lane >> lgL);
+        uint32_t tot = 0, pre = 0;
+        for (int q = sub; q < R; q += 64) {  // several pieces per lane only when R > 64
+          const uint4 x = q == sub ? v[u] : e < E ? cnt16[(size_t)e * R + q] : zero4;
+          const uint32_t d[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const int c0 = 16 * q + 4 * h;
+            tot = __builtin_amdgcn_sad_u8(d[h] & bytes_below(nch, c0), 0u, tot);
+            pre = __builtin_amdgcn_sad_u8(d[h] & bytes_below(chunk, c0), 0u, pre);
+          }
+        }
+        if (L > 1) tot += xor_lane<1>(tot), pre += xor_lane<1>(pre);
+        if (L > 2) tot += xor_lane<2>(tot), pre += xor_lane<2>(pre);
+        if (L > 4) tot += xor_lane<4>(tot), pre += xor_lane<4>(pre);
+        if (L > 8) tot += xor_lane<8>(tot), pre += xor_lane<8>(pre);
+        if (L > 16) tot += xor_lane<16>(tot), pre += xor_lane<16>(pre);
+        if (L > 32) tot += xor_lane<32>(tot), pre += xor_lane<32>(pre);
+        if (sub == 0 && e < E) {
+          s_tot[e] = (int)tot;
+          s_pre[e] = (int)pre;
+        }
       }
     }
-    s_tot[e] = (int)tot;
-    s_pre[e] = (int)pre;
   }
   __syncthreads();
   // padded exclusive offsets of the experts, in expert order (each thread a contiguous range)
@@ -540,9 +570,12 @@ static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // The fused prefix: every chunk's workgroup reads all E rows of count bytes, and its LDS holds
 // 28 bytes per expert.  Up to 128 KB per workgroup it beats the separate prefix launch (graph
-// replay: T = 8192, E = 512, k = 4: 23.1 -> 19.6 us; E = 1024: 27.2 -> 25.9 us; the Kimi-K2.5
-// share at T = 16384, 98.5 KB: 32.6 -> 29.6 us); beyond, it loses (E = 2304 at T = 8192, 295 KB:
-// 44.4 -> 46.3 us; the Kimi share at T = 33288, 203 KB: 55.8 -> 66.1 us).
+// replay: T = 8192, E = 512, k = 4: 23.1 -> 18.9 us; E = 1024: 27.2 -> 25.9 us; the Kimi-K2.5
+// share at T = 16384, 98.5 KB: 32.6 -> 27.7 us).  Beyond, neither wins throughout: fused is
+// faster for E = 2304, k = 36 at T = 4096 and 8192 (147 and 295 KB: 34.0 -> 31.5, 44.6 -> 43.0
+// us) and E = 1024 at T = 16384 (256 KB: 37.6 -> 35.1 us), slower for E = 4096 at T = 4096 (256
+// KB: 35.6 -> 36.6), E = 3000 at T = 8192 (384 KB: 42.7 -> 45.1), E = 2304 at T = 12000 (442
+// KB: 52.1 -> 56.8) and the Kimi share at T = 33288 (203 KB: 55.6 -> 84.2 us).
 static bool route_fused_scan(int E, int nch) {
   return E <= 4096 && (int64_t)E * ((nch + 15) / 16 * 16) <= 128 * 1024;
 }
