@@ -532,7 +532,6 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   __shared__ f32x4_t red[KS > 1 ? (KS - 1) * RG * NG * NT * 64 : 1];
   int mb, nt;
   if (!block_tile(mbs, (D + 16 * NG * RG - 1) / (16 * NG * RG), mb, nt)) return;
-  if (mb * BM >= *num_valid) return;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int rg = wave / KS, kp = wave % KS;
   const int d_w = nt * 16 * NG * RG + rg * 16 * NG;
@@ -540,9 +539,19 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   // otherwise, with NG == 2), so leaving here never skips a barrier; D % 64 == 0 keeps a
   // wave's 16*NG rows inside D once d_w < D
   if (KS == 1 && d_w >= D) return;
-  const int e = expert_ids[mb];
-  if ((unsigned)e >= (unsigned)E) return;  // defensive: ids come from the routing step
+  // The valid count, the block's expert and its slot ids are independent loads (mb < mbs keeps
+  // them in bounds): issued together, before the branch that uses them, so that a wave waits
+  // one memory latency for all three before its weight stream starts.
   const int i16 = lane & 15, g = lane >> 4;
+  int slot[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) slot[tt] = sorted_ids[mb * BM + tt * 16 + i16];
+  const int nv = *num_valid;
+  const int e = expert_ids[mb];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) asm volatile("" ::"v"(slot[tt]));  // keeps the loads above the branch
+  // blocks past the valid count, and (defensive: ids come from the routing step) bad ids
+  if (mb * BM >= nv || (unsigned)e >= (unsigned)E) return;
   const int n_slots = T * k;
   const int rowb = DT == DT_BF16 ? I * 2 : DT == DT_FP8 ? I : I / 2;
   const int rows_s = I / 32;  // FP4: E8M0 scales per row
@@ -559,14 +568,21 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   }
   const uint8_t* xrow[NT];
   const uint8_t* xsc[NT];
-  int slot[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
-    const int s = sorted_ids[mb * BM + tt * 16 + i16];
-    slot[tt] = s;
+    const int s = slot[tt];
     const bool real = (unsigned)s < (unsigned)n_slots;
     xrow[tt] = real ? a + (size_t)s * rowb : nullptr;
     xsc[tt] = FP4 && real ? static_cast<const uint8_t*>(a_scale_v) + (size_t)s * rows_s : nullptr;
+  }
+  // the epilogue's factors (routed weight, fp8: times the slot's row scale), loaded while the
+  // weights stream
+  float fac[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int s = slot[tt];
+    fac[tt] = 0.f;
+    if ((unsigned)s < (unsigned)n_slots) fac[tt] = FP8 ? topk_w[s] * a_scale[s] : topk_w[s];
   }
   f32x4_t acc[NG][NT];
 #pragma unroll
@@ -617,8 +633,7 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   for (int tt = 0; tt < NT; ++tt) {
     const int s = slot[tt];
     if ((unsigned)s >= (unsigned)n_slots) continue;  // padding rows issue no store and no atomic
-    float sc = topk_w[s];
-    if constexpr (FP8) sc *= a_scale[s];
+    const float sc = fac[tt];
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       const int d0 = d_w + 16 * q + 4 * g;
