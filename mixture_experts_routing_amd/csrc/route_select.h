@@ -243,6 +243,31 @@ __device__ void select_token_exact(const float* __restrict__ row, int E, int k, 
   }
 }
 
+// The largest key of the wave and the k-th largest of its 64/L lane-group maxima (groups of L
+// consecutive lanes), for a group width fixed at compile time: a butterfly takes each group's
+// maximum, and a descending bitonic network over the groups (each maximum repeated over its
+// group's lanes, so only distances of at least L take part) sorts them.
+template <int L>
+__device__ __forceinline__ void group_threshold(uint32_t lk, int k, uint32_t& top, uint32_t& tk) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int mm = 1; mm < L; mm <<= 1) {
+    const uint32_t o = xor_lane_u32(lk, mm);
+    lk = o > lk ? o : lk;
+  }
+#pragma unroll
+  for (int size = 2 * L; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride >= L; stride >>= 1) {
+      const uint32_t p = xor_lane_u32(lk, stride);
+      const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      lk = keep_max ? (lk > p ? lk : p) : (lk < p ? lk : p);
+    }
+  }
+  top = readlane_u32(lk, 0);
+  tk = readlane_u32(lk, (k - 1) * L);
+}
+
 // Loads a token's row: lane l gets experts l, l+64, ...; empty slots hold NaN, which no
 // comparison selects.
 template <int NV>
@@ -291,19 +316,18 @@ __device__ void select_from_row(float (&x)[NV], const float* __restrict__ row, i
 #pragma unroll
     for (int i = 1; i < NV; ++i) lm = fmaxf(lm, x[i]);
     // threshold: k-th largest of the G lane-group maxima (as order-preserving keys, 0 = empty)
-    uint32_t lk = lm == lm ? logit_key(lm) : 0u;
+    const uint32_t lk = lm == lm ? logit_key(lm) : 0u;
     int G = 2;
     while (G < 2 * k && G < 64) G <<= 1;
-    const int L = 64 / G;
-#pragma unroll
-    for (int mm = 1; mm < 64; mm <<= 1)
-      if (mm < L) {
-        const uint32_t o = shfl_xor_u32(lk, mm);
-        lk = o > lk ? o : lk;
-      }
-    const uint32_t srt = bitonic64_desc_grouped(lk, L);
-    const uint32_t top = readlane_u32(srt, 0);  // the largest eligible key
-    const uint32_t tk = readlane_u32(srt, (k - 1) * L);
+    uint32_t top, tk;  // the largest eligible key, the threshold key
+    switch (64 / G) {  // wave-uniform: one straight-line network per group width
+      case 32: group_threshold<32>(lk, k, top, tk); break;
+      case 16: group_threshold<16>(lk, k, top, tk); break;
+      case 8: group_threshold<8>(lk, k, top, tk); break;
+      case 4: group_threshold<4>(lk, k, top, tk); break;
+      case 2: group_threshold<2>(lk, k, top, tk); break;
+      default: group_threshold<1>(lk, k, top, tk); break;
+    }
     const float tau = tk == 0u ? -__builtin_inff() : key_logit(tk);
     // compaction of the logits >= tau: a ballot per register gives each lane its slot
     int c = 0;  // wave-uniform
