@@ -165,13 +165,12 @@ __global__ void __launch_bounds__(1024) route_oneshot_kernel(
 // One token per wave; each workgroup also writes one share of the sentinel / -1 fill of
 // sorted_ids and expert_ids.  Dynamic LDS (GROUPED): keys [4][E4] u32.
 template <int NV, bool GROUPED>
-__global__ void __launch_bounds__(256) route_select_kernel(const float* __restrict__ logits,
-                                                           int T, int E, int k, int score,
-                                                           int renorm, GroupSel gs, int B,
-                                                           int cap, float* __restrict__ topk_w,
-                                                           int32_t* __restrict__ topk_ids,
-                                                           int32_t* __restrict__ sorted_ids,
-                                                           int32_t* __restrict__ expert_ids) {
+__device__ __forceinline__ void select_block(const float* __restrict__ logits, int T, int E, int k,
+                                             int score, int renorm, GroupSel gs, int B, int cap,
+                                             float* __restrict__ topk_w,
+                                             int32_t* __restrict__ topk_ids,
+                                             int32_t* __restrict__ sorted_ids,
+                                             int32_t* __restrict__ expert_ids) {
   __shared__ uint64_t s_cand[4][kMaxCand];
   extern __shared__ __align__(16) unsigned char s_dyn[];
   const int w = threadIdx.x >> 6;
@@ -182,6 +181,33 @@ __global__ void __launch_bounds__(256) route_select_kernel(const float* __restri
   select_token<NV, GROUPED, true>(logits + (size_t)t * E, E, k, score, renorm, gs, s_cand[w],
                                   topk_w + (size_t)t * k, topk_ids + (size_t)t * k,
                                   [](int, int) {});
+}
+
+template <int NV, bool GROUPED>
+__global__ void __launch_bounds__(256) route_select_kernel(const float* __restrict__ logits,
+                                                           int T, int E, int k, int score,
+                                                           int renorm, GroupSel gs, int B,
+                                                           int cap, float* __restrict__ topk_w,
+                                                           int32_t* __restrict__ topk_ids,
+                                                           int32_t* __restrict__ sorted_ids,
+                                                           int32_t* __restrict__ expert_ids) {
+  select_block<NV, GROUPED>(logits, T, E, k, score, renorm, gs, B, cap, topk_w, topk_ids,
+                            sorted_ids, expert_ids);
+}
+
+// The plain selection for 65 <= E <= 1536 (2 <= NV <= kSelOccMaxNV) fits 64 registers: 8 waves
+// per SIMD, one token each, so a T = 8192 call is resident at once (at 72 registers, 7 waves
+// per SIMD, an eighth of its tokens waited for a second round).  Larger rows, NV = 1 and the
+// group-limited selection would spill there and keep the kernel above.
+constexpr int kSelOccMaxNV = 24;
+template <int NV>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
+route_select_occ_kernel(const float* __restrict__ logits, int T, int E, int k, int score,
+                        int renorm, GroupSel gs, int B, int cap, float* __restrict__ topk_w,
+                        int32_t* __restrict__ topk_ids, int32_t* __restrict__ sorted_ids,
+                        int32_t* __restrict__ expert_ids) {
+  select_block<NV, false>(logits, T, E, k, score, renorm, gs, B, cap, topk_w, topk_ids,
+                          sorted_ids, expert_ids);
 }
 
 // Single-workgroup sort after the select kernel (T <= kSort1MaxT, E <= kSort1MaxE): 16
@@ -626,10 +652,18 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
       if (err != hipSuccess) return err;
     }
+    auto launch_select = [&]() {
+      if constexpr (!GROUPED && NV >= 2 && NV <= kSelOccMaxNV)
+        route_select_occ_kernel<NV><<<(T + 3) / 4, 256, 0, st>>>(
+            logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
+            expert_ids);
+      else
+        route_select_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
+            logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
+            expert_ids);
+    };
     if (route_is_twostage(T, E, k)) {
-      route_select_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
-          logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
-          expert_ids);
+      launch_select();
       const size_t lds = 24 * (size_t)E4 + 20 * 4;  // <= 61.5 KB for E <= 2560
       route_sort1_kernel<<<1, 1024, lds, st>>>(topk_ids, T, E, k, B, sorted_ids, expert_ids,
                                                num_valid);
@@ -639,9 +673,7 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
     char* wsb = reinterpret_cast<char*>(ws);
     if (route_fused_scan(E, nch)) {
       uint8_t* cnt8 = reinterpret_cast<uint8_t*>(wsb);
-      route_select_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
-          logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
-          expert_ids);
+      launch_select();
       route_count8_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt8);
       const size_t lds = 28 * (size_t)E4 + 20 * 4;  // <= 112 KB for E <= 4096
       if (lds > 64 * 1024) {
@@ -660,9 +692,7 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
         reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tot) + align256((int64_t)E * 4));
     int32_t* gsum =
         reinterpret_cast<int32_t*>(reinterpret_cast<char*>(loff) + align256((int64_t)E * 4));
-    route_select_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
-        logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
-        expert_ids);
+    launch_select();
     route_count_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt);
     route_colscan_kernel<<<(E + 63) / 64, 1024, 0, st>>>(cnt, nch, E, B, tot, loff, gsum);
     const size_t lds = 16 * (size_t)E4;
