@@ -67,10 +67,9 @@ __device__ __forceinline__ void row_scores(float (&x)[NV], float (&y)[NV], int E
 
 // Dynamic LDS: map bytes [4][E4].
 template <int NV>
-__global__ void __launch_bounds__(256) aux_scores_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k, int score,
-                                                         float* __restrict__ scores,
-                                                         uint8_t* __restrict__ rmap) {
+__device__ __forceinline__ void aux_scores_block(const float* __restrict__ logits, int T, int E,
+                                                 int k, int score, float* __restrict__ scores,
+                                                 uint8_t* __restrict__ rmap) {
   __shared__ uint64_t s_cand[4][kMaxCand];
   extern __shared__ __align__(16) unsigned char s_map[];
   const int w = threadIdx.x >> 6;
@@ -162,10 +161,30 @@ __global__ void __launch_bounds__(256) aux_scores_backward_kernel(
 }
 
 template <int NV>
+__global__ void __launch_bounds__(256) aux_scores_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int score,
+                                                         float* __restrict__ scores,
+                                                         uint8_t* __restrict__ rmap) {
+  aux_scores_block<NV>(logits, T, E, k, score, scores, rmap);
+}
+// As for the router's select kernel: for 65 <= E <= 1024 the forward fits 64 registers, 8
+// waves per SIMD (a T = 8192 call resident at once; 37 registers at E = 512, 65 without the
+// bound); elsewhere it would spill.
+template <int NV>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
+aux_scores_occ_kernel(const float* __restrict__ logits, int T, int E, int k, int score,
+                      float* __restrict__ scores, uint8_t* __restrict__ rmap) {
+  aux_scores_block<NV>(logits, T, E, k, score, scores, rmap);
+}
+
+template <int NV>
 static hipError_t launch_aux_nv(const float* logits, int T, int E, int k, int score,
                                 float* scores, uint8_t* rmap, hipStream_t st) {
   const size_t lds = 4 * (size_t)((E + 3) & ~3);
-  aux_scores_kernel<NV><<<(T + 3) / 4, 256, lds, st>>>(logits, T, E, k, score, scores, rmap);
+  if constexpr (NV >= 2 && NV <= 16)
+    aux_scores_occ_kernel<NV><<<(T + 3) / 4, 256, lds, st>>>(logits, T, E, k, score, scores, rmap);
+  else
+    aux_scores_kernel<NV><<<(T + 3) / 4, 256, lds, st>>>(logits, T, E, k, score, scores, rmap);
   return hipGetLastError();
 }
 
