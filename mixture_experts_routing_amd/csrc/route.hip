@@ -22,7 +22,8 @@
 //    padded scan per 64 experts -> per-chunk scatter, which also combines the group
 //    offsets and writes the block experts (four launches, 64-token chunks); where each
 //    chunk's workgroup can read all E x nch counts (one byte each, at most 128 KB) the prefix
-//    and the padded scan run inside the scatter kernel instead (three launches).
+//    and the padded scan run inside the scatter kernel instead (three launches), and with at
+//    most 32768 ids in all each chunk's workgroup counts them all itself (two launches).
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "route_select.h"
@@ -441,6 +442,10 @@ __device__ __forceinline__ uint32_t bytes_below(int lim, int c0) {
 // and scans the padded totals itself.  The ids of its tokens are loaded before the counts, so
 // both are in flight together.
 // Dynamic LDS: hist [16][E4] u8 | tot [E4] i32 | pre [E4] i32 | off [E4] i32 | wsum [20] i32
+// COUNT_ALL (few ids in all, T < 65536): there are no chunk counts; each workgroup counts all
+// T*k ids itself, into one LDS word per expert (its total in the low half, the part before this
+// chunk in the high half), which saves the count launch.
+template <bool COUNT_ALL>
 __global__ void __launch_bounds__(1024) route_scan_scatter_kernel(
     const int32_t* __restrict__ topk_ids, int T, int E, int k, int B, int nch,
     const uint8_t* __restrict__ cnt8, int32_t* __restrict__ sorted_ids,
@@ -461,7 +466,27 @@ __global__ void __launch_bounds__(1024) route_scan_scatter_kernel(
   for (int q = 0; q < TPW; ++q)
     ids[q] = (t0 + q < t1 && lane < k) ? topk_ids[(size_t)(t0 + q) * k + lane] : -1;
   for (int i = tid; i < 16 * E4 / 4; i += 1024) reinterpret_cast<uint32_t*>(s_hist)[i] = 0u;
-  {
+  if constexpr (COUNT_ALL) {
+    uint32_t* h = reinterpret_cast<uint32_t*>(s_tot);
+    for (int e = tid; e < E4; e += 1024) h[e] = 0u;
+    __syncthreads();
+    // slot s = t*k + j lies before this chunk iff s < lim; eight loads per thread in flight
+    const int n = T * k, lim = chunk * kChunkTokens * k;
+    for (int s0 = tid; s0 < n; s0 += 8 * 1024) {
+      int e8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) e8[u] = s0 + u * 1024 < n ? topk_ids[s0 + u * 1024] : -1;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if ((unsigned)e8[u] < (unsigned)E) atomicAdd(&h[e8[u]], s0 + u * 1024 < lim ? 0x10001u : 1u);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 1024) {
+      const uint32_t v = h[e];
+      s_pre[e] = (int)(v >> 16);
+      s_tot[e] = (int)(v & 0xFFFFu);
+    }
+  } else {
     // L lanes share an expert's row of R 16-byte pieces (L = R rounded up to a power of two,
     // at most 64): a wave load covers whole consecutive rows, four passes of loads are in
     // flight together, and a butterfly over the L lanes adds the pieces' sums.
@@ -606,6 +631,16 @@ static bool route_fused_scan(int E, int nch) {
   return E <= 4096 && (int64_t)E * ((nch + 15) / 16 * 16) <= 128 * 1024;
 }
 
+// Few ids in all: every chunk's workgroup counts all T*k of them (route_scan_scatter_kernel
+// <true>), two launches in all; the packed counts need T < 65536.  Graph replay against the
+// three-launch fused prefix: T*k = 32768 at E = 512, k = 4, T = 8192: 17.7 -> 16.4 us;
+// E = 128, k = 4, T = 4096: 14.1 -> 11.8 us; E = 1024, k = 4, T = 8192: 22.3 -> 19.2 us.  Past
+// that it loses: 54000 ids (E = 385, k = 9) 17.9 -> 18.0 us, 65536 (E = 512, k = 8) 18.9 -> 20.7.
+constexpr int64_t kCountAllMaxIds = 32768;
+static bool route_count_all(int T, int E, int k) {
+  return E <= 4096 && T < 65536 && (int64_t)T * k <= kCountAllMaxIds;
+}
+
 // The larger of the two layouts: int32 counts, totals, offsets and group sums (four launches)
 // or byte counts in rows of nch rounded up to 16 (fused prefix).
 int64_t route_workspace_bytes(int T, int E, int k) {
@@ -671,19 +706,26 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
     }
     const int nch = (T + kChunkTokens - 1) / kChunkTokens;
     char* wsb = reinterpret_cast<char*>(ws);
-    if (route_fused_scan(E, nch)) {
+    const bool count_all = route_count_all(T, E, k);
+    if (count_all || route_fused_scan(E, nch)) {
       uint8_t* cnt8 = reinterpret_cast<uint8_t*>(wsb);
       launch_select();
-      route_count8_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt8);
+      if (!count_all)
+        route_count8_kernel<<<nch, 1024, (size_t)E4 * 4, st>>>(topk_ids, T, E, k, nch, cnt8);
       const size_t lds = 28 * (size_t)E4 + 20 * 4;  // <= 112 KB for E <= 4096
+      const void* fn = count_all ? (const void*)route_scan_scatter_kernel<true>
+                                 : (const void*)route_scan_scatter_kernel<false>;
       if (lds > 64 * 1024) {
-        const hipError_t err = hipFuncSetAttribute((const void*)route_scan_scatter_kernel,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   (int)lds);
+        const hipError_t err =
+            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
       }
-      route_scan_scatter_kernel<<<nch, 1024, lds, st>>>(topk_ids, T, E, k, B, nch, cnt8,
-                                                        sorted_ids, expert_ids, num_valid);
+      if (count_all)
+        route_scan_scatter_kernel<true><<<nch, 1024, lds, st>>>(topk_ids, T, E, k, B, nch, cnt8,
+                                                                sorted_ids, expert_ids, num_valid);
+      else
+        route_scan_scatter_kernel<false><<<nch, 1024, lds, st>>>(topk_ids, T, E, k, B, nch, cnt8,
+                                                                 sorted_ids, expert_ids, num_valid);
       return hipGetLastError();
     }
     int32_t* cnt = reinterpret_cast<int32_t*>(wsb);

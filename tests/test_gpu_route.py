@@ -106,8 +106,8 @@ def test_route_crafted_ties(kind, T, E, k, B):
                                      (129, 2560, 8, 16), (128, 2561, 4, 16), (100, 64, 64, 64),
                                      (64, 3000, 8, 16), (1, 3000, 2, 16), (8192, 4096, 8, 32),
                                      (200, 300, 70, 64), (200, 4100, 70, 64),
-                                     (8192, 1024, 8, 32), (8193, 1024, 8, 32), (2500, 512, 4, 32),
-                                     (70000, 64, 2, 16)])
+                                     (8192, 1024, 8, 32), (8193, 1024, 8, 32), (2500, 512, 16, 32),
+                                     (70000, 64, 2, 16), (8193, 512, 4, 32), (4096, 385, 8, 64)])
 def test_route_edges(T, E, k, B):
     """Path boundaries: one-shot, two-stage and multi-workgroup sorts; in the last, the prefix over
     chunks inside the scatter kernel (E <= 4096 and at most 128 KB of count bytes per chunk, e.g.
@@ -115,7 +115,11 @@ def test_route_edges(T, E, k, B):
     each also with k > 64 (picks past the first 64 read from memory); and either side of the
     128 KB limit (E = 1024: 128 chunks of counts fused, 129 not).  In the fused prefix a row of
     counts is 16-byte pieces shared by a power-of-two group of lanes: 40 chunks are three pieces
-    per row on four lanes, 1094 chunks (T = 70000) 69 pieces on 64 lanes, some lanes taking two."""
+    per row on four lanes, 1094 chunks (T = 70000) 69 pieces on 64 lanes, some lanes taking two.
+    Up to 32768 ids in all (T*k) every chunk counts all of them itself (no count launch): 385
+    experts at T*k = 32768 and the 512/4 workload at 32768 (CASES) take that path, T = 8193 with
+    k = 4 (32772 ids) the fused prefix; so do the cases above with T > 128 and few ids (T = 200,
+    k = 70 picks past the first 64)."""
     logits = synth.logits(T, E, seed=11)
     got = run_route(logits.cuda(), k, B)
     check_route(got, oracle_route(logits, k, B), T, k)
