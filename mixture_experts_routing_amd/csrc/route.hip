@@ -196,19 +196,22 @@ __global__ void __launch_bounds__(256) route_select_kernel(const float* __restri
                             sorted_ids, expert_ids);
 }
 
-// The plain selection for 65 <= E <= 1536 (2 <= NV <= kSelOccMaxNV) fits 64 registers: 8 waves
-// per SIMD, one token each, so a T = 8192 call is resident at once (at 72 registers, 7 waves
-// per SIMD, an eighth of its tokens waited for a second round).  Larger rows, NV = 1 and the
-// group-limited selection would spill there and keep the kernel above.
-constexpr int kSelOccMaxNV = 24;
-template <int NV>
+// The plain selection for 65 <= E <= 1536 (2 <= NV <= 24) and the group-limited one for
+// E <= 256 (NV <= 4) fit 64 registers: 8 waves per SIMD, one token each, so a T = 8192 call is
+// resident at once (at 72 registers, 7 waves per SIMD, an eighth of its tokens waited for a
+// second round).  Larger rows and NV = 1 (plain) would spill there and keep the kernel above.
+template <int NV, bool GROUPED>
+constexpr bool select_occ() {
+  return GROUPED ? NV <= 4 : NV >= 2 && NV <= 24;
+}
+template <int NV, bool GROUPED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
 route_select_occ_kernel(const float* __restrict__ logits, int T, int E, int k, int score,
                         int renorm, GroupSel gs, int B, int cap, float* __restrict__ topk_w,
                         int32_t* __restrict__ topk_ids, int32_t* __restrict__ sorted_ids,
                         int32_t* __restrict__ expert_ids) {
-  select_block<NV, false>(logits, T, E, k, score, renorm, gs, B, cap, topk_w, topk_ids,
-                          sorted_ids, expert_ids);
+  select_block<NV, GROUPED>(logits, T, E, k, score, renorm, gs, B, cap, topk_w, topk_ids,
+                            sorted_ids, expert_ids);
 }
 
 // Single-workgroup sort after the select kernel (T <= kSort1MaxT, E <= kSort1MaxE): 16
@@ -688,8 +691,8 @@ static hipError_t launch_route_nv(const float* logits, int T, int E, int k, int 
       if (err != hipSuccess) return err;
     }
     auto launch_select = [&]() {
-      if constexpr (!GROUPED && NV >= 2 && NV <= kSelOccMaxNV)
-        route_select_occ_kernel<NV><<<(T + 3) / 4, 256, 0, st>>>(
+      if constexpr (select_occ<NV, GROUPED>())
+        route_select_occ_kernel<NV, GROUPED><<<(T + 3) / 4, 256, sel_lds, st>>>(
             logits, T, E, k, score, renorm, gs, B, (int)cap, topk_w, topk_ids, sorted_ids,
             expert_ids);
       else
