@@ -107,7 +107,8 @@ def test_route_crafted_ties(kind, T, E, k, B):
                                      (64, 3000, 8, 16), (1, 3000, 2, 16), (8192, 4096, 8, 32),
                                      (200, 300, 70, 64), (200, 4100, 70, 64),
                                      (8192, 1024, 8, 32), (8193, 1024, 8, 32), (2500, 512, 16, 32),
-                                     (70000, 64, 2, 16), (8193, 512, 4, 32), (4096, 385, 8, 64)])
+                                     (70000, 64, 2, 16), (8193, 512, 4, 32), (4096, 385, 8, 64),
+                                     (32768, 128, 1, 16), (16384, 64, 2, 32)])
 def test_route_edges(T, E, k, B):
     """Path boundaries: one-shot, two-stage and multi-workgroup sorts; in the last, the prefix over
     chunks inside the scatter kernel (E <= 4096 and at most 128 KB of count bytes per chunk, e.g.
@@ -119,7 +120,8 @@ def test_route_edges(T, E, k, B):
     Up to 32768 ids in all (T*k) every chunk counts all of them itself (no count launch): 385
     experts at T*k = 32768 and the 512/4 workload at 32768 (CASES) take that path, T = 8193 with
     k = 4 (32772 ids) the fused prefix; so do the cases above with T > 128 and few ids (T = 200,
-    k = 70 picks past the first 64)."""
+    k = 70 picks past the first 64), and, at the limit with many chunks, T = 32768 with k = 1 (512
+    chunks) and T = 16384 with E = 64."""
     logits = synth.logits(T, E, seed=11)
     got = run_route(logits.cuda(), k, B)
     check_route(got, oracle_route(logits, k, B), T, k)
@@ -142,11 +144,14 @@ def test_route_deterministic_and_bounded(T, E, k, B):
     assert torch.all(a["expert_ids"][cap // B:] == -12345)
 
 
-def test_route_skewed_load():
-    # a few hot experts: long per-expert lists spanning many blocks and chunks
-    T, E, k, B = 5000, 64, 6, 32
+@pytest.mark.parametrize("T,E,k,B,hot,boost", [(5000, 64, 6, 32, 4, 3.0), (32768, 64, 1, 64, 1, 30.0)])
+def test_route_skewed_load(T, E, k, B, hot, boost):
+    """A few hot experts: long per-expert lists spanning many blocks and chunks.  In the second
+    case every token picks expert 0, so with the ids counted in every chunk's workgroup (at most
+    32768 ids) that expert's count and the part before the last chunk reach 32768 and 32704 in
+    their 16-bit halves."""
     logits = synth.logits(T, E, seed=5)
-    logits[:, :4] += 3.0
+    logits[:, :hot] += boost
     got = run_route(logits.cuda(), k, B)
     check_route(got, oracle_route(logits, k, B), T, k)
 
