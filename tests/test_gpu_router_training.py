@@ -160,6 +160,7 @@ AUX = [
     (4, 8, 2, "normal"), (33, 100, 5, "normal"), (64, 4096, 8, "normal"),
     (8192, 512, 22, "normal"), (8192, 2304, 36, "normal"),
     (16, 512, 80, "normal"), (40, 256, 8, "ties3"), (20, 130, 3, "equal"), (300, 512, 8, "wide"),
+    (17, 700, 6, "normal"), (50, 1000, 10, "normal"),
 ]
 
 
